@@ -1,0 +1,294 @@
+"""CPU oracle for the 3-bit FP8-codebook decode linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  It shares no code with the GPU path
+(no kernels, headers, tables or helpers) and imports nothing from it; it is a
+plain, slow, obviously-correct restatement of what the layer computes, in
+float64 with numpy.
+
+What the layer computes (Hibana: Fast Agentic Inference on Unified-Memory
+Devices -- "Model surgery", subsection "Three-bit weights"): every group of 32
+consecutive weights of a row is stored as 3-bit indices into an 8-entry FP8
+codebook, plus one 8-bit scale per group, 3 + 8/32 = 3.25 bits per weight.
+A decode step multiplies the dequantised matrix by a handful of token
+activations:
+
+    w[n][k] = E4M3FN(codebook[n][code[n][k]]) * 2^(scale[n][k // 32] - 127)
+    y[m][n] = sum_k x[m][k] * w[n][k]
+
+Readings taken where the page is silent (each also listed in the design notes):
+  * one 8-entry codebook per output row (its 8 bytes are outside the 3.25
+    bits/weight count, which only has codes and scales);
+  * "FP8" is OCP E4M3FN (bias 7, max 448, NaN = 0x7F/0xFF, has -0);
+  * the "8-bit scale" is an OCP-MX E8M0 power of two, value 2^(s-127);
+  * the scale multiplies the codebook value;
+  * activations are bf16, outputs fp32 (oracle: fp64);
+  * the bit order of the 96 code bits of a group is this project's own
+    "byte-lane" layout (see pack_group).
+MoE verify rounds (same page, "Adaptive speculation" -- "Expert sharing"):
+verifying drafted tokens reads every expert any of them picked; the oracle
+routes each token to its top-k experts by router logit (ties to the lower
+expert index) and reports the union.
+
+Parity status per function (what pins each one lives in tests/test_oracle.py):
+  e4m3fn_decode   pinned: all 256 bytes vs torch.float8_e4m3fn, spec values
+  e8m0_decode     pinned: spec values of the OCP MX E8M0 type
+  bf16_decode     pinned: torch.bfloat16 for random and special bit patterns
+  layout          pinned: payload = n*k*13/32 (3.25 bits/weight closed form)
+  pack_group      pinned: hand-derived worked example, brute-force round trip
+  pack/unpack     pinned: round trip, worked example, padding is zero
+  linear          pinned: torch fp64 matmul of torch-decoded weights, closed
+                  forms (one-hot codebook, constant codes, single group),
+                  exact Fraction brute force on tiny K
+  topk_route      pinned: brute-force ranking, torch.topk on distinct logits
+  grouped_linear  pinned: equals per-(token, slot) dense linear calls
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 32                 # weights per group (one scale each)
+CODEBOOK_SIZE = 8          # 3-bit indices
+CHUNK_GROUPS = 4           # groups per 48-byte chunk (3 x 16-byte loads)
+CODE_BYTES_PER_GROUP = 12  # 96 code bits
+E8M0_BIAS = 127
+
+
+# ----------------------------------------------------------------- numbers
+
+def e4m3fn_decode(byte: int) -> float:
+    """One OCP E4M3FN byte -> its value (float64).
+
+    Sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0.  Exponent 0
+    is subnormal (m/8 * 2^-6); exponent 15 with mantissa 7 is NaN (no
+    infinities); everything else is (1 + m/8) * 2^(e-7).
+    """
+    byte = int(byte) & 0xFF
+    sign = -1.0 if byte & 0x80 else 1.0
+    e = (byte >> 3) & 0xF
+    m = byte & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+E4M3FN_TABLE = np.array([e4m3fn_decode(b) for b in range(256)], dtype=np.float64)
+
+
+def e8m0_decode(s) -> np.ndarray:
+    """E8M0 scale byte(s) -> 2^(s-127) in float64; 255 is NaN."""
+    s = np.asarray(s, dtype=np.int64)
+    out = np.ldexp(np.ones(s.shape, dtype=np.float64), (s - E8M0_BIAS).astype(np.int32))
+    return np.where(s == 255, np.nan, out)
+
+
+def bf16_decode(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64.  bf16 is the top half of an
+    IEEE binary32, so widening is exact: place the bits in the high half."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------------ layout
+
+def layout(n: int, k: int) -> dict:
+    """Sizes of the packed planes for an n x k matrix.
+
+    Codes: per row ceil(k/128) chunks of 4 groups x 12 bytes (48 bytes, three
+    16-byte loads); groups past k/32 in the last chunk are zero padding.
+    Scales: one byte per group, row pitch 4*ceil(k/128) rounded up to 16.
+    Codebook: 8 bytes per row.  Payload counts only real codes and scales:
+    k/32 * 13 bytes per row = n*k*13/32 bytes, i.e. 3.25 bits per weight.
+    """
+    if n < 0 or k <= 0 or k % GROUP:
+        raise ValueError("k must be a positive multiple of 32")
+    groups = k // GROUP
+    chunks = -(-k // (GROUP * CHUNK_GROUPS))
+    code_row = chunks * CHUNK_GROUPS * CODE_BYTES_PER_GROUP
+    scale_row = -(-(chunks * CHUNK_GROUPS) // 16) * 16
+    return dict(n=n, k=k, groups=groups, chunks=chunks,
+                code_row_bytes=code_row, scale_row_bytes=scale_row,
+                code_plane_bytes=n * code_row, scale_plane_bytes=n * scale_row,
+                codebook_bytes=n * CODEBOOK_SIZE,
+                payload_bytes=n * groups * (CODE_BYTES_PER_GROUP + 1))
+
+
+# --------------------------------------------------------------- bit layout
+
+def pack_group(c) -> tuple:
+    """32 codes (0..7, K order) -> three little-endian uint32 words.
+
+    Byte b (0..3) of word j (0..2) holds
+        bits 0..2: code 8j+b
+        bits 3..5: code 8j+4+b
+        bits 6..7: bits 2j..2j+1 of the six-bit value c[24+b] | c[28+b] << 3
+    so masking a word with 0x07 per byte yields four codes in K order, and the
+    last eight codes are spread two bits at a time over the top of all bytes.
+    """
+    c = [int(v) & 7 for v in c]
+    assert len(c) == GROUP
+    words = []
+    for j in range(3):
+        w = 0
+        for b in range(4):
+            spill = c[24 + b] | (c[28 + b] << 3)
+            byte = c[8 * j + b] | (c[8 * j + 4 + b] << 3) | (((spill >> (2 * j)) & 3) << 6)
+            w |= byte << (8 * b)
+        words.append(w)
+    return tuple(words)
+
+
+def unpack_group(words) -> list:
+    """Inverse of pack_group: three uint32 words -> 32 codes in K order."""
+    c = [0] * GROUP
+    spill = [0, 0, 0, 0]
+    for j in range(3):
+        for b in range(4):
+            byte = (int(words[j]) >> (8 * b)) & 0xFF
+            c[8 * j + b] = byte & 7
+            c[8 * j + 4 + b] = (byte >> 3) & 7
+            spill[b] |= ((byte >> 6) & 3) << (2 * j)
+    for b in range(4):
+        c[24 + b] = spill[b] & 7
+        c[28 + b] = (spill[b] >> 3) & 7
+    return c
+
+
+def _pack_bytes(c):
+    """Vectorised byte-lane packing: c uint8 [..., 32] -> bytes uint8 [..., 12]
+    (byte 4j+b of the group = byte b of word j), same rule as pack_group."""
+    c = c.astype(np.uint8) & 7
+    out = np.empty(c.shape[:-1] + (12,), dtype=np.uint8)
+    for b in range(4):
+        spill = c[..., 24 + b] | (c[..., 28 + b] << 3)
+        for j in range(3):
+            out[..., 4 * j + b] = (c[..., 8 * j + b] | (c[..., 8 * j + 4 + b] << 3)
+                                   | (((spill >> (2 * j)) & 3) << 6))
+    return out
+
+
+def _unpack_bytes(by):
+    """Vectorised inverse: bytes uint8 [..., 12] -> codes uint8 [..., 32]."""
+    c = np.empty(by.shape[:-1] + (32,), dtype=np.uint8)
+    for b in range(4):
+        spill = np.zeros(by.shape[:-1], dtype=np.uint8)
+        for j in range(3):
+            byte = by[..., 4 * j + b]
+            c[..., 8 * j + b] = byte & 7
+            c[..., 8 * j + 4 + b] = (byte >> 3) & 7
+            spill |= ((byte >> 6) & 3) << (2 * j)
+        c[..., 24 + b] = spill & 7
+        c[..., 28 + b] = (spill >> 3) & 7
+    return c
+
+
+def pack(codes: np.ndarray, scales: np.ndarray):
+    """codes uint8 [n][k] (only bits 0..2 used), scales uint8 [n][k/32] ->
+    (code_plane uint8 [n][code_row_bytes], scale_plane uint8 [n][scale_row_bytes]),
+    padding bytes zero."""
+    n, k = codes.shape
+    L = layout(n, k)
+    G = L["groups"]
+    cp = np.zeros((n, L["code_row_bytes"]), dtype=np.uint8)
+    cp[:, :G * 12] = _pack_bytes(codes.reshape(n, G, 32)).reshape(n, G * 12)
+    sp = np.zeros((n, L["scale_row_bytes"]), dtype=np.uint8)
+    sp[:, :G] = scales
+    return cp, sp
+
+
+def unpack(code_plane: np.ndarray, scale_plane: np.ndarray, n: int, k: int):
+    """(code_plane, scale_plane) -> (codes uint8 [n][k], scales uint8 [n][k/32])."""
+    G = k // GROUP
+    by = np.ascontiguousarray(code_plane[:n, :G * 12]).reshape(n, G, 12)
+    return _unpack_bytes(by).reshape(n, k), np.ascontiguousarray(scale_plane[:n, :G])
+
+
+# ---------------------------------------------------------------- the layer
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, codebook: np.ndarray) -> np.ndarray:
+    """w[n][k] = E4M3FN(codebook[n][codes[n][k] & 7]) * 2^(scales[n][k/32] - 127), float64."""
+    n, k = codes.shape
+    rows = np.arange(n)[:, None]
+    cbv = E4M3FN_TABLE[codebook.astype(np.int64)]               # [n][8]
+    w = cbv[rows, (codes & 7).astype(np.int64)]                  # [n][k]
+    return w * np.repeat(e8m0_decode(scales), GROUP, axis=1)
+
+
+def linear(code_plane, scale_plane, codebook, n, k, x_bits, rows=None, block=2048):
+    """y[m][r] = sum_k x[m][k] w[r][k] and bound[m][r] = sum_k |x[m][k] w[r][k]|
+    in float64, for r in `rows` (default: all n rows).  Weights are read back
+    from the packed planes with this module's own unpacking, so a wrong
+    packing shows up here.  Rows are processed in blocks of `block` to bound
+    memory; the per-block products are plain fp64 matrix products."""
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    x = bf16_decode(x_bits)                                      # [m][k]
+    xa = np.abs(x)
+    y = np.empty((x.shape[0], rows.size), dtype=np.float64)
+    bound = np.empty_like(y)
+    for s in range(0, rows.size, block):
+        r = rows[s:s + block]
+        codes, scales = unpack(code_plane[r], scale_plane[r], r.size, k)
+        w = dequantize(codes, scales, codebook[r])
+        y[:, s:s + r.size] = x @ w.T
+        bound[:, s:s + r.size] = xa @ np.abs(w).T
+    return y, bound
+
+
+def within_tolerance(y_gpu, y_ref, bound, rel=1e-3):
+    """Acceptance rule: |y - y_ref| <= rel * sum_k |x_k w_k|, and an exact 0
+    where that sum is 0.  Returns (ok, worst err/bound ratio)."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    err = np.abs(y_gpu - y_ref)
+    zero = bound == 0
+    ok = bool(np.all(err[~zero] <= rel * bound[~zero]) and np.all(y_gpu[zero] == 0))
+    ratio = float(np.max(err[~zero] / bound[~zero])) if (~zero).any() else 0.0
+    return ok, ratio
+
+
+# --------------------------------------------------------------------- MoE
+
+def topk_route(logits: np.ndarray, topk: int) -> np.ndarray:
+    """Top-k expert ids per token by router logit, highest first; equal logits
+    go to the lower expert index.  Softmax is monotone, so ranking the logits
+    ranks the routing probabilities."""
+    t, E = logits.shape
+    ids = np.empty((t, topk), dtype=np.int32)
+    for i in range(t):
+        order = sorted(range(E), key=lambda e: (-float(logits[i, e]), e))
+        ids[i] = order[:topk]
+    return ids
+
+
+def expert_union(ids: np.ndarray) -> np.ndarray:
+    """Sorted distinct experts that at least one token picked."""
+    return np.unique(ids.reshape(-1)).astype(np.int32)
+
+
+def grouped_linear(planes, ids, x_bits, x_by_slot: bool, rows=None):
+    """Expert-grouped products for one verify round.
+
+    planes: list over experts of (code_plane, scale_plane, codebook, n, k).
+    ids:    int [t][topk] routed experts.
+    x_bits: bf16 [t][k] when x_by_slot is False (each token's activation goes to
+            all of its experts), or bf16 [t][topk][k] when True (one activation
+            per (token, slot), as for a down projection).
+    Returns y[t][topk][n] and the matching bounds; each expert in the union is
+    dequantised once and applied only to the (token, slot) pairs routed to it.
+    """
+    t, topk = ids.shape
+    n = planes[0][3]
+    nr = n if rows is None else len(rows)
+    y = np.zeros((t, topk, nr))
+    bound = np.zeros_like(y)
+    for e in expert_union(ids):
+        pairs = [(i, j) for i in range(t) for j in range(topk) if ids[i, j] == e]
+        cp, sp, cb, ne, ke = planes[e]
+        xs = np.stack([x_bits[i, j] if x_by_slot else x_bits[i] for i, j in pairs])
+        ye, be = linear(cp, sp, cb, ne, ke, xs, rows=rows)
+        for p, (i, j) in enumerate(pairs):
+            y[i, j] = ye[p]
+            bound[i, j] = be[p]
+    return y, bound
