@@ -1,0 +1,207 @@
+// C ABI of the q3 library: host-side validation, then one launch on the
+// caller's stream.  Nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/q3.h"
+#include "q3_internal.h"
+
+namespace {
+
+constexpr int64_t kGroup = 32;
+
+int64_t chunks_of(int64_t k) { return (k + 127) / 128; }
+int64_t code_row_min(int64_t k) { return 48 * chunks_of(k); }
+int64_t scale_row_min(int64_t k) { return (4 * chunks_of(k) + 15) / 16 * 16; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+q3_status check_shape(int64_t n, int64_t k) {
+  if (n < 0) return Q3_ERR_INVALID_ARG;
+  if (k <= 0 || k % kGroup != 0 || k > (int64_t(1) << 30)) return Q3_ERR_UNSUPPORTED_SHAPE;
+  if (n > (int64_t(1) << 31)) return Q3_ERR_UNSUPPORTED_SHAPE;
+  return Q3_OK;
+}
+
+// Packed planes of one matrix: pointers present, pitches large enough, aligned.
+q3_status check_planes(int64_t n, int64_t k, const void* code, int64_t code_pitch, const void* scale,
+                       int64_t scale_pitch, const void* cb) {
+  q3_status st = check_shape(n, k);
+  if (st != Q3_OK) return st;
+  if (n > 0 && (!code || !scale || !cb)) return Q3_ERR_INVALID_ARG;
+  if (code_pitch < code_row_min(k) || scale_pitch < scale_row_min(k)) return Q3_ERR_INVALID_ARG;
+  if (code_pitch % 16 || scale_pitch % 4) return Q3_ERR_MISALIGNED;
+  if (!aligned(code, 16) || !aligned(scale, 4) || !aligned(cb, 8)) return Q3_ERR_MISALIGNED;
+  return Q3_OK;
+}
+
+q3_status check_matrix(const q3_matrix* w) {
+  if (!w) return Q3_ERR_INVALID_ARG;
+  return check_planes(w->n, w->k, w->code_plane, w->code_row_bytes, w->scale_plane, w->scale_row_bytes,
+                      w->codebook);
+}
+
+q3_status check_tokens(int64_t k, int64_t n, const uint16_t* x, int64_t m, int64_t ldx, const float* y,
+                       int64_t ldy, int64_t m_max) {
+  if (m < 1 || m > m_max) return Q3_ERR_UNSUPPORTED_SHAPE;
+  if (!x || (!y && n > 0)) return Q3_ERR_INVALID_ARG;
+  if (ldx < k || ldy < n) return Q3_ERR_INVALID_ARG;
+  if (ldx % 8 || !aligned(x, 16) || !aligned(y, 4)) return Q3_ERR_MISALIGNED;
+  return Q3_OK;
+}
+
+// gfx950 check, once per device (the only global state of the library).
+std::atomic<int> g_device_ok[64];
+
+q3_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return Q3_ERR_HIP;
+  if (dev < 0 || dev >= 64) return Q3_ERR_UNSUPPORTED_DEVICE;
+  int state = g_device_ok[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return Q3_ERR_HIP;
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_device_ok[dev].store(state, std::memory_order_release);
+  }
+  return state == 1 ? Q3_OK : Q3_ERR_UNSUPPORTED_DEVICE;
+}
+
+q3_status from_hip(hipError_t e) { return e == hipSuccess ? Q3_OK : Q3_ERR_HIP; }
+
+q3::PlaneView view_of(const q3_matrix* w) {
+  q3::PlaneView v;
+  v.code = static_cast<const uint8_t*>(w->code_plane);
+  v.code_pitch = w->code_row_bytes;
+  v.scale = static_cast<const uint8_t*>(w->scale_plane);
+  v.scale_pitch = w->scale_row_bytes;
+  v.cb = static_cast<const uint8_t*>(w->codebook);
+  v.n = w->n;
+  v.groups = static_cast<int32_t>(w->k / kGroup);
+  return v;
+}
+
+}  // namespace
+
+extern "C" {
+
+Q3_API const char* q3_status_string(q3_status s) {
+  switch (s) {
+    case Q3_OK: return "ok";
+    case Q3_ERR_INVALID_ARG: return "invalid argument";
+    case Q3_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case Q3_ERR_MISALIGNED: return "misaligned pointer or pitch";
+    case Q3_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
+    case Q3_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+Q3_API q3_status q3_layout(int64_t n, int64_t k, q3_layout_info* out) {
+  if (!out) return Q3_ERR_INVALID_ARG;
+  q3_status st = check_shape(n, k);
+  if (st != Q3_OK) return st;
+  out->n = n;
+  out->k = k;
+  out->groups = k / kGroup;
+  out->chunks = chunks_of(k);
+  out->code_row_bytes = code_row_min(k);
+  out->scale_row_bytes = scale_row_min(k);
+  out->code_plane_bytes = n * out->code_row_bytes;
+  out->scale_plane_bytes = n * out->scale_row_bytes;
+  out->codebook_bytes = 8 * n;
+  out->payload_bytes = n * (k / kGroup) * 13;
+  return Q3_OK;
+}
+
+Q3_API q3_status q3_pack(const uint8_t* codes, int64_t ldc, const uint8_t* scale_bytes, int64_t lds, int64_t n,
+                         int64_t k, void* code_plane, int64_t code_row_bytes, void* scale_plane,
+                         int64_t scale_row_bytes, void* stream) {
+  q3_status st = check_shape(n, k);
+  if (st != Q3_OK) return st;
+  if (n > 0 && (!codes || !scale_bytes || !code_plane || !scale_plane)) return Q3_ERR_INVALID_ARG;
+  if (ldc < k || lds < k / kGroup) return Q3_ERR_INVALID_ARG;
+  if (code_row_bytes < code_row_min(k) || scale_row_bytes < scale_row_min(k)) return Q3_ERR_INVALID_ARG;
+  if (code_row_bytes % 16 || scale_row_bytes % 4 || !aligned(code_plane, 16) || !aligned(scale_plane, 4))
+    return Q3_ERR_MISALIGNED;
+  if ((st = check_device()) != Q3_OK) return st;
+  return from_hip(q3::launch_pack(codes, ldc, scale_bytes, lds, n, k, static_cast<uint8_t*>(code_plane),
+                                  code_row_bytes, static_cast<uint8_t*>(scale_plane), scale_row_bytes,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+Q3_API q3_status q3_unpack(const q3_matrix* w, uint8_t* codes_out, uint8_t* scale_out, void* stream) {
+  q3_status st = check_matrix(w);
+  if (st != Q3_OK) return st;
+  if (w->n > 0 && (!codes_out || !scale_out)) return Q3_ERR_INVALID_ARG;
+  if (!aligned(codes_out, 4)) return Q3_ERR_MISALIGNED;
+  if ((st = check_device()) != Q3_OK) return st;
+  return from_hip(q3::launch_unpack(view_of(w), codes_out, scale_out, static_cast<hipStream_t>(stream)));
+}
+
+Q3_API q3_status q3_gemv(const q3_matrix* w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
+                         void* stream) {
+  q3_status st = check_matrix(w);
+  if (st != Q3_OK) return st;
+  if ((st = check_tokens(w->k, w->n, x, m, ldx, y, ldy, 8)) != Q3_OK) return st;
+  if ((st = check_device()) != Q3_OK) return st;
+  return from_hip(q3::launch_gemv(view_of(w), x, m, ldx, y, ldy, static_cast<hipStream_t>(stream)));
+}
+
+Q3_API q3_status q3_gemm_small_m(const q3_matrix* w, const uint16_t* x, int64_t m, int64_t ldx, float* y,
+                                 int64_t ldy, void* stream) {
+  q3_status st = check_matrix(w);
+  if (st != Q3_OK) return st;
+  if ((st = check_tokens(w->k, w->n, x, m, ldx, y, ldy, 64)) != Q3_OK) return st;
+  if ((st = check_device()) != Q3_OK) return st;
+  return from_hip(q3::launch_gemm_small_m(view_of(w), x, m, ldx, y, ldy, static_cast<hipStream_t>(stream)));
+}
+
+Q3_API q3_status q3_moe_topk(const float* logits, int32_t t, int32_t num_experts, int32_t topk,
+                             int32_t* topk_ids, void* stream) {
+  if (!logits || !topk_ids) return Q3_ERR_INVALID_ARG;
+  if (t < 1 || num_experts < 1 || num_experts > 1024 || topk < 1 || topk > num_experts)
+    return Q3_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4)) return Q3_ERR_MISALIGNED;
+  q3_status st = check_device();
+  if (st != Q3_OK) return st;
+  return from_hip(q3::launch_moe_topk(logits, t, num_experts, topk, topk_ids, static_cast<hipStream_t>(stream)));
+}
+
+Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t* x, int64_t ldx,
+                                        int32_t x_by_slot, const int32_t* topk_ids, int32_t t, int32_t topk,
+                                        float* y, int64_t ldy, void* stream) {
+  if (!w) return Q3_ERR_INVALID_ARG;
+  if (w->num_experts < 1 || w->num_experts > 65535) return Q3_ERR_UNSUPPORTED_SHAPE;
+  q3_status st = check_planes(w->n, w->k, w->code_plane, w->code_row_bytes, w->scale_plane, w->scale_row_bytes,
+                              w->codebook);
+  if (st != Q3_OK) return st;
+  if (w->code_expert_stride < 0 || w->scale_expert_stride < 0 || w->codebook_expert_stride < 0)
+    return Q3_ERR_INVALID_ARG;
+  if (w->code_expert_stride % 16 || w->scale_expert_stride % 4 || w->codebook_expert_stride % 8)
+    return Q3_ERR_MISALIGNED;
+  if (x_by_slot != 0 && x_by_slot != 1) return Q3_ERR_INVALID_ARG;
+  if (!x || !topk_ids || !y) return Q3_ERR_INVALID_ARG;
+  if (t < 1 || topk < 1 || int64_t(t) * topk > 64) return Q3_ERR_UNSUPPORTED_SHAPE;
+  if (ldx < w->k || ldy < w->n) return Q3_ERR_INVALID_ARG;
+  if (ldx % 8 || !aligned(x, 16) || !aligned(y, 4) || !aligned(topk_ids, 4)) return Q3_ERR_MISALIGNED;
+  if ((st = check_device()) != Q3_OK) return st;
+  q3::ExpertView v;
+  v.base.code = static_cast<const uint8_t*>(w->code_plane);
+  v.base.code_pitch = w->code_row_bytes;
+  v.base.scale = static_cast<const uint8_t*>(w->scale_plane);
+  v.base.scale_pitch = w->scale_row_bytes;
+  v.base.cb = static_cast<const uint8_t*>(w->codebook);
+  v.base.n = w->n;
+  v.base.groups = static_cast<int32_t>(w->k / kGroup);
+  v.code_stride = w->code_expert_stride;
+  v.scale_stride = w->scale_expert_stride;
+  v.cb_stride = w->codebook_expert_stride;
+  v.num_experts = static_cast<int32_t>(w->num_experts);
+  return from_hip(q3::launch_grouped(v, x, ldx, x_by_slot, topk_ids, t, topk, y, ldy,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Device-side building blocks shared by the q3 kernels (gfx950 only).
+//
+// Format (Hibana: Fast Agentic Inference on Unified-Memory Devices, "Model
+// surgery" / "Three-bit weights"): a group of 32 weights is 32 three-bit
+// indices into the row's 8-entry E4M3FN codebook plus one E8M0 scale.  The 96
+// code bits of a group sit in three 32-bit words in a byte-lane order chosen so
+// that a per-byte mask yields four indices in K order, ready to be used as
+// v_perm_b32 byte selectors into the 8-byte codebook:
+//   byte b of word j: bits 0..2 = c[8j+b], bits 3..5 = c[8j+4+b],
+//                     bits 6..7 = bits 2j..2j+1 of (c[24+b] | c[28+b] << 3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q3 {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGroup = 32;
+
+// Three code words of a group -> eight selector words; selector i holds the
+// indices of weights 4i..4i+3 (one per byte, values 0..7).  17 VALU ops.
+__device__ __forceinline__ void unpack_selectors(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t (&s)[8]) {
+  const uint32_t m3 = 0x07070707u;
+  s[0] = d0 & m3;
+  s[1] = (d0 >> 3) & m3;
+  s[2] = d1 & m3;
+  s[3] = (d1 >> 3) & m3;
+  s[4] = d2 & m3;
+  s[5] = (d2 >> 3) & m3;
+  // Bits 6..7 of every byte of the three words carry the last eight indices,
+  // two bits per word; gather them into bits 0..5 of each byte.
+  const uint32_t sp = ((d0 >> 6) & 0x03030303u) | ((d1 >> 4) & 0x0C0C0C0Cu) | ((d2 >> 2) & 0x30303030u);
+  s[6] = sp & m3;
+  s[7] = (sp >> 3) & m3;
+}
+
+// Codebook lookup of four indices at once: v_perm_b32 picks byte sel[b] of the
+// 8-byte table {cb_hi:cb_lo} (entries 0..3 in cb_lo, 4..7 in cb_hi).
+__device__ __forceinline__ uint32_t lookup4(uint32_t cb_lo, uint32_t cb_hi, uint32_t sel) {
+  return __builtin_amdgcn_perm(cb_hi, cb_lo, sel);
+}
+
+// The E8M0 scale byte as an fp32 power of two 2^(s-127) (exact for 1..254).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return __builtin_bit_cast(float, s << 23);
+}
+
+// Two E4M3FN bytes (low or high half of q) -> two bf16 values times the scale.
+// Exact: an E4M3FN value has 4 significant bits and the power-of-two scale
+// keeps it inside bf16's range for scale bytes 16..240.
+__device__ __forceinline__ bf16x2 fp8x2_to_bf16x2(uint32_t q, float scale, bool high) {
+  return high ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, scale, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, scale, false);
+}
+
+// Dequantise one group to 16 bf16 pairs in K order (pair p = weights 2p, 2p+1).
+__device__ __forceinline__ void dequant_group_bf16(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t sbyte,
+                                                   uint32_t cb_lo, uint32_t cb_hi, bf16x2 (&w)[16]) {
+  uint32_t sel[8];
+  unpack_selectors(d0, d1, d2, sel);
+  const float sc = e8m0_to_f32(sbyte);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t q = lookup4(cb_lo, cb_hi, sel[i]);
+    w[2 * i] = fp8x2_to_bf16x2(q, sc, false);
+    w[2 * i + 1] = fp8x2_to_bf16x2(q, sc, true);
+  }
+}
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+
+}  // namespace q3

@@ -1,0 +1,166 @@
+/*
+ * q3.h -- C ABI of the 3-bit FP8-codebook decode linear layer for MI355X (gfx950).
+ *
+ * The method (Hibana: Fast Agentic Inference on Unified-Memory Devices, section
+ * "Model surgery", subsection "Three-bit weights"): every group of 32 consecutive
+ * weights of a row is stored as 3-bit indices into an 8-entry FP8 codebook plus
+ * one 8-bit scale per group, 3 + 8/32 = 3.25 bits per weight.  A decode or
+ * speculative-verify step multiplies the dequantised matrix by a few token
+ * activations:
+ *
+ *     w[n][k] = E4M3FN(codebook[n][code[n][k]]) * 2^(scale[n][k/32] - 127)
+ *     y[m][n] = sum_k x[m][k] * w[n][k]          (x bf16, y fp32)
+ *
+ * Readings of the page used here: one codebook per output row (8 bytes, outside
+ * the 3.25 bits/weight count); FP8 = OCP E4M3FN; scale = OCP-MX E8M0.
+ *
+ * ---- Packed format (all planes are row-major, one row per output n) ----------
+ *   groups G = k/32, chunks C = ceil(k/128) (a chunk is 4 groups)
+ *   code plane : uint32 words, row pitch code_row_bytes >= 48*C (multiple of 16).
+ *                Group g of row n is the 3 words at byte offset n*pitch + 12*g.
+ *                Byte b (0..3) of word j (0..2) of a group with codes c[0..31]:
+ *                  bits 0..2 = c[8j+b], bits 3..5 = c[8j+4+b],
+ *                  bits 6..7 = bits 2j..2j+1 of (c[24+b] | c[28+b] << 3).
+ *                Groups past G in the last chunk are zero.
+ *   scale plane: uint8, row pitch scale_row_bytes >= round_up(4*C, 16); byte g
+ *                of row n is the E8M0 scale of group g; padding is zero.
+ *   codebook   : uint8 [n][8], E4M3FN bytes, entry j is what code j selects.
+ *   x          : bf16 bit patterns, [m][ldx] (ldx >= k elements).
+ *   y          : fp32, [m][ldy] (ldy >= n elements).
+ *
+ * ---- Conventions ----------------------------------------------------------------
+ *   * Every pointer argument except the descriptor structs is a DEVICE pointer.
+ *     Descriptor structs are host memory, read during the call only.
+ *   * The caller owns all buffers; compute calls never allocate or free.
+ *   * Every call is asynchronous on `stream` (a hipStream_t; NULL = the legacy
+ *     default stream) and returns after launching.  Calls on different streams
+ *     may run concurrently; the library keeps no mutable global state besides a
+ *     once-per-device capability check.
+ *   * Arguments are validated on the host before any HIP call; a rejected call
+ *     launches nothing.  Launch failures are reported as Q3_ERR_HIP.
+ *   * Numerics: products are formed exactly and accumulated in fp32, so every
+ *     output satisfies |y - y_exact| <= 1e-3 * sum_k |x_k w_k| for k <= 8192.
+ *     Preconditions (not checked on the device): scale bytes in [16, 240],
+ *     codebook bytes not NaN (0x7F/0xFF), x finite.  Code bits above bit 2 of
+ *     q3_pack's input are ignored.
+ */
+#ifndef Q3_H
+#define Q3_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q3_API __attribute__((visibility("default")))
+
+typedef enum q3_status {
+  Q3_OK = 0,
+  Q3_ERR_INVALID_ARG = 1,        /* null pointer, negative size, bad mode          */
+  Q3_ERR_UNSUPPORTED_SHAPE = 2,  /* k not a multiple of 32, m out of range, ...    */
+  Q3_ERR_MISALIGNED = 3,         /* pointer or pitch not aligned as required       */
+  Q3_ERR_UNSUPPORTED_DEVICE = 4, /* current device is not gfx950                   */
+  Q3_ERR_HIP = 5                 /* a HIP runtime call or kernel launch failed     */
+} q3_status;
+
+/* Sizes of the packed planes for an n x k matrix (host-only, no HIP call). */
+typedef struct q3_layout_info {
+  int64_t n, k;
+  int64_t groups;            /* k/32                                          */
+  int64_t chunks;            /* ceil(k/128)                                   */
+  int64_t code_row_bytes;    /* 48*chunks                                     */
+  int64_t scale_row_bytes;   /* round_up(4*chunks, 16)                        */
+  int64_t code_plane_bytes;  /* n*code_row_bytes                              */
+  int64_t scale_plane_bytes; /* n*scale_row_bytes                             */
+  int64_t codebook_bytes;    /* 8*n                                           */
+  int64_t payload_bytes;     /* n*k*13/32: codes + scales, 3.25 bits/weight   */
+} q3_layout_info;
+
+/* A packed matrix.  Pointers are device pointers; the code plane and its pitch
+ * must be 16-byte aligned, the scale plane and its pitch 4-byte aligned, the
+ * codebook 8-byte aligned. */
+typedef struct q3_matrix {
+  int64_t n, k;
+  const void* code_plane;
+  int64_t code_row_bytes;
+  const void* scale_plane;
+  int64_t scale_row_bytes;
+  const void* codebook;
+} q3_matrix;
+
+/* A stack of E experts with one shape; expert e's planes start at
+ * base + e*stride (bytes).  Strides keep the alignments of q3_matrix. */
+typedef struct q3_expert_stack {
+  int64_t num_experts, n, k;
+  const void* code_plane;
+  int64_t code_row_bytes, code_expert_stride;
+  const void* scale_plane;
+  int64_t scale_row_bytes, scale_expert_stride;
+  const void* codebook;
+  int64_t codebook_expert_stride;
+} q3_expert_stack;
+
+/* Human-readable name of a status code (static string). */
+Q3_API const char* q3_status_string(q3_status s);
+
+/* Packed-plane sizes for an n x k matrix (the 3.25 bits/weight format of
+ * "Three-bit weights").  Q3_ERR_UNSUPPORTED_SHAPE unless k > 0, k % 32 == 0,
+ * n >= 0.  Host only. */
+Q3_API q3_status q3_layout(int64_t n, int64_t k, q3_layout_info* out);
+
+/* Pack unpacked codes and scales into the planes ("Three-bit weights": a
+ * 3-bit index per weight, one 8-bit scale per group of 32).
+ *   codes       [n][ldc] uint8, entries 0..7 (higher bits ignored), ldc >= k
+ *   scale_bytes [n][lds] uint8 E8M0, lds >= k/32
+ *   code_plane / scale_plane: outputs with the pitches given (>= q3_layout's,
+ *   aligned as in q3_matrix); padding is written as zero.
+ * Bit-exact; one launch. */
+Q3_API q3_status q3_pack(const uint8_t* codes, int64_t ldc, const uint8_t* scale_bytes, int64_t lds,
+                         int64_t n, int64_t k, void* code_plane, int64_t code_row_bytes,
+                         void* scale_plane, int64_t scale_row_bytes, void* stream);
+
+/* Inverse of q3_pack: codes_out [n][k] (values 0..7), scale_out [n][k/32]. */
+Q3_API q3_status q3_unpack(const q3_matrix* w, uint8_t* codes_out, uint8_t* scale_out, void* stream);
+
+/* y[m][n] = x[m][:] . w[n][:] for 1 <= m <= 8 tokens (decode and short
+ * speculative-verify rounds), on the vector ALUs: the packed codes are streamed
+ * once, looked up in the row's codebook with byte permutes, widened exactly to
+ * bf16 with the group scale folded in, and dotted with x in fp32.  x is bf16
+ * [m][ldx], y fp32 [m][ldy]; ldx, ldy in elements. */
+Q3_API q3_status q3_gemv(const q3_matrix* w, const uint16_t* x, int64_t m, int64_t ldx,
+                         float* y, int64_t ldy, void* stream);
+
+/* Same product for 1 <= m <= 64 on the matrix cores: each 16-row tile of
+ * codes is dequantised exactly to bf16 in registers and multiplied by the
+ * activations with bf16 MFMA, fp32 accumulation.  m > 64 is rejected
+ * (Q3_ERR_UNSUPPORTED_SHAPE); call again per 64-token slice. */
+Q3_API q3_status q3_gemm_small_m(const q3_matrix* w, const uint16_t* x, int64_t m, int64_t ldx,
+                                 float* y, int64_t ldy, void* stream);
+
+/* Router of an MoE verify round (Hibana page, "Adaptive speculation",
+ * "Expert sharing": verifying drafted tokens reads every expert any of them
+ * picked).  logits fp32 [t][num_experts] (row pitch num_experts) ->
+ * topk_ids int32 [t][topk], highest logit first, ties to the lower expert
+ * index.  1 <= topk <= num_experts <= 1024, t >= 1. */
+Q3_API q3_status q3_moe_topk(const float* logits, int32_t t, int32_t num_experts, int32_t topk,
+                             int32_t* topk_ids, void* stream);
+
+/* Expert-grouped product of one verify round.  Only experts that appear in
+ * topk_ids are read from memory, each once, and each is applied only to the
+ * (token, slot) pairs routed to it:
+ *     y[i][j][:] = W[topk_ids[i][j]] . xin(i, j)
+ * where xin(i, j) = x[i][:] when x_by_slot == 0 (gate/up projection) or
+ * x[i*topk + j][:] when x_by_slot == 1 (down projection, one activation per
+ * pair).  x bf16 with row pitch ldx elements; y fp32 [t*topk][ldy].
+ * topk_ids is a device int32 [t][topk] array (e.g. from q3_moe_topk); ids
+ * outside [0, num_experts) are skipped.  t*topk <= 64. */
+Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t* x, int64_t ldx,
+                                        int32_t x_by_slot, const int32_t* topk_ids, int32_t t,
+                                        int32_t topk, float* y, int64_t ldy, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q3_H */

@@ -1,0 +1,92 @@
+"""The C ABI library without a GPU: it loads, exports every entry point that
+include/q3.h declares, its layout query agrees with the oracle's independent
+layout, and argument validation rejects bad calls before touching HIP."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "q3.h")
+
+
+@pytest.fixture(scope="module")
+def q3lib():
+    from bit_fp8_codebook_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from bit_fp8_codebook_amd import build
+        build.build(verbose=False)
+    return _lib.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"Q3_API\s+[\w\s\*]+?\b(q3_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_symbols() == sorted(["q3_status_string", "q3_layout", "q3_pack", "q3_unpack", "q3_gemv",
+                                         "q3_gemm_small_m", "q3_moe_topk", "q3_grouped_expert_gemv"])
+
+
+def test_library_exports_every_declared_symbol(q3lib):
+    from bit_fp8_codebook_amd import _lib
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT\s+(q3_\w+)", out))
+    for s in declared_symbols():
+        assert s in exported, s
+        assert hasattr(q3lib, s)
+    assert set(_lib.SIGNATURES) == set(declared_symbols())
+
+
+@pytest.mark.parametrize("n,k", [(1024, 1024), (4096, 4096), (1536, 2048), (2048, 768), (28672, 8192),
+                                 (151936, 4096), (5, 32), (3, 96), (7, 160), (1, 8224)])
+def test_layout_matches_oracle(q3lib, n, k):
+    from bit_fp8_codebook_amd import q3_layout
+    got = q3_layout(n, k)
+    ref = oracle.layout(n, k)
+    for key in ref:
+        assert got[key] == ref[key], key
+
+
+def test_status_strings(q3lib):
+    for s in range(6):
+        assert q3lib.q3_status_string(s)
+
+
+def test_validation_rejects_before_any_hip_call(q3lib):
+    from bit_fp8_codebook_amd import _lib
+    info = _lib.Q3LayoutInfo()
+    assert q3lib.q3_layout(4, 33, ctypes.byref(info)) == 2
+    assert q3lib.q3_layout(4, 0, ctypes.byref(info)) == 2
+    assert q3lib.q3_layout(-1, 32, ctypes.byref(info)) == 1
+    assert q3lib.q3_layout(4, 32, None) == 1
+    fake = 0x1000   # never dereferenced: every call below fails validation first
+    w = _lib.Q3Matrix(16, 64, fake, 48, fake, 16, fake)
+    assert q3lib.q3_gemv(None, fake, 1, 64, fake, 16, None) == 1
+    assert q3lib.q3_gemv(ctypes.byref(w), fake, 0, 64, fake, 16, None) == 2       # m = 0
+    assert q3lib.q3_gemv(ctypes.byref(w), fake, 9, 64, fake, 16, None) == 2       # m > 8
+    assert q3lib.q3_gemm_small_m(ctypes.byref(w), fake, 65, 64, fake, 16, None) == 2
+    assert q3lib.q3_gemv(ctypes.byref(w), None, 1, 64, fake, 16, None) == 1       # null x
+    assert q3lib.q3_gemv(ctypes.byref(w), fake + 2, 1, 64, fake, 16, None) == 3   # x misaligned
+    assert q3lib.q3_gemv(ctypes.byref(w), fake, 1, 60, fake, 16, None) == 1       # ldx < k
+    assert q3lib.q3_gemv(ctypes.byref(w), fake, 1, 64, fake, 8, None) == 1        # ldy < n
+    bad = _lib.Q3Matrix(16, 48, fake, 48, fake, 16, fake)                          # k % 32 != 0
+    assert q3lib.q3_gemv(ctypes.byref(bad), fake, 1, 64, fake, 16, None) == 2
+    pitch = _lib.Q3Matrix(16, 256, fake, 48, fake, 16, fake)                       # code pitch too small
+    assert q3lib.q3_gemv(ctypes.byref(pitch), fake, 1, 256, fake, 16, None) == 1
+    mis = _lib.Q3Matrix(16, 64, fake + 4, 48, fake, 16, fake)                      # code plane not 16-aligned
+    assert q3lib.q3_gemv(ctypes.byref(mis), fake, 1, 64, fake, 16, None) == 3
+    assert q3lib.q3_pack(fake, 63, fake, 2, 16, 64, fake, 48, fake, 16, None) == 1    # ldc < k
+    assert q3lib.q3_pack(fake, 64, fake, 2, 16, 64, fake + 8, 48, fake, 16, None) == 3
+    assert q3lib.q3_moe_topk(fake, 8, 64, 65, fake, None) == 2
+    assert q3lib.q3_moe_topk(fake, 8, 2048, 8, fake, None) == 2
+    st = _lib.Q3ExpertStack(4, 16, 64, fake, 48, 48 * 16, fake, 16, 256, fake, 128)
+    assert q3lib.q3_grouped_expert_gemv(ctypes.byref(st), fake, 64, 2, fake, 8, 8, fake, 16, None) == 1
+    assert q3lib.q3_grouped_expert_gemv(ctypes.byref(st), fake, 64, 0, fake, 9, 8, fake, 16, None) == 2
+    st.code_expert_stride = 40
+    assert q3lib.q3_grouped_expert_gemv(ctypes.byref(st), fake, 64, 0, fake, 8, 8, fake, 16, None) == 3

@@ -1,0 +1,170 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.  Packing and unpacking must be bit-exact; products must
+satisfy |y - y_ref| <= 1e-3 * sum_k |x_k w_k| for every output."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_close, dev, oracle_linear, pack_layer
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q3():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_fp8_codebook_amd as q3
+    q3.lib()
+    return q3
+
+
+PACK_SHAPES = [(1024, 1024), (37, 96), (5, 32), (64, 160), (2048, 768), (100, 4096), (3, 8224)]
+
+
+@pytest.mark.parametrize("n,k", PACK_SHAPES)
+def test_pack_bit_exact(q3, n, k):
+    layer = synth.make_layer(n, k, seed=n + k)
+    rng = np.random.default_rng(k)
+    codes = layer.codes | (rng.integers(0, 32, size=layer.codes.shape, dtype=np.uint8) << 3)  # high bits ignored
+    w = q3.q3_pack(dev(codes), dev(layer.scales), dev(layer.codebook))
+    cp, sp = oracle.pack(codes, layer.scales)
+    assert np.array_equal(w.code_plane.cpu().numpy(), cp)
+    assert np.array_equal(w.scale_plane.cpu().numpy(), sp)
+    c2, s2 = q3.q3_unpack(w)
+    assert np.array_equal(c2.cpu().numpy(), codes & 7)
+    assert np.array_equal(s2.cpu().numpy(), layer.scales)
+
+
+def test_pack_worked_example(q3):
+    codes = np.array([[k % 8 for k in range(32)]], dtype=np.uint8)
+    w = q3.q3_pack(dev(codes), dev(np.array([[127]], dtype=np.uint8)), dev(np.zeros((1, 8), np.uint8)))
+    words = w.code_plane.cpu().numpy()[0, :12].view(np.uint32)
+    assert [hex(v) for v in words] == ["0xfbb26920", "0xbb32a920", "0xfbf2a9a0"]
+
+
+GEMV_CASES = [(1024, 1024, 1), (4096, 4096, 1), (4096, 4096, 4), (4096, 4096, 8), (37, 96, 3), (1, 32, 1),
+              (130, 800, 2), (1000, 768, 5), (257, 8224, 6), (2048, 2048, 7), (300, 1536, 8), (64, 8192, 1)]
+
+
+@pytest.mark.parametrize("n,k,m", GEMV_CASES)
+def test_gemv_parity(q3, n, k, m):
+    layer, x = synth.make_linear(n, k, m, seed=n * 7 + k + m)
+    w = pack_layer(q3, layer)
+    y = q3.q3_gemv(w, dev(x)).cpu().numpy()
+    y_ref, bound = oracle_linear(layer, x)
+    assert_close(y, y_ref, bound, f"gemv n={n} k={k} m={m}")
+
+
+MFMA_CASES = [(1024, 1024, 1), (4096, 4096, 1), (4096, 4096, 4), (4096, 4096, 8), (4096, 4096, 16),
+              (100, 96, 3), (17, 32, 16), (333, 1024, 17), (200, 768, 33), (513, 2048, 64), (64, 8224, 5),
+              (2000, 8192, 16), (48, 4096, 48)]
+
+
+@pytest.mark.parametrize("n,k,m", MFMA_CASES)
+def test_gemm_small_m_parity(q3, n, k, m):
+    layer, x = synth.make_linear(n, k, m, seed=n * 11 + k + m)
+    w = pack_layer(q3, layer)
+    y = q3.q3_gemm_small_m(w, dev(x)).cpu().numpy()
+    y_ref, bound = oracle_linear(layer, x)
+    assert_close(y, y_ref, bound, f"gemm n={n} k={k} m={m}")
+
+
+@pytest.mark.parametrize("fn", ["q3_gemv", "q3_gemm_small_m"])
+def test_strided_x_and_y(q3, fn):
+    layer, x = synth.make_linear(70, 512, 4, seed=3)
+    w = pack_layer(q3, layer)
+    xbig = torch.zeros((4, 512 + 64), dtype=torch.int16, device="cuda")
+    xbig[:, :512] = dev(x)
+    ybig = torch.full((4, 70 + 5), 7.0, dtype=torch.float32, device="cuda")
+    getattr(q3, fn)(w, xbig[:, :512], ybig[:, :70])
+    yb = ybig.cpu().numpy()
+    assert np.all(yb[:, 70:] == 7.0)
+    y_ref, bound = oracle_linear(layer, x)
+    assert_close(yb[:, :70], y_ref, bound, fn)
+
+
+@pytest.mark.parametrize("fn,m", [("q3_gemv", 1), ("q3_gemv", 8), ("q3_gemm_small_m", 16), ("q3_gemm_small_m", 64)])
+def test_deterministic(q3, fn, m):
+    layer, x = synth.make_linear(1024, 4096, m, seed=5)
+    w = pack_layer(q3, layer)
+    xd = dev(x)
+    a = getattr(q3, fn)(w, xd).cpu().numpy()
+    b = getattr(q3, fn)(w, xd).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_edge_values(q3):
+    """Codebooks with -0, repeated and extreme entries; scales at the ends of the
+    supported range; a row whose codebook is all zero (bound 0 -> exact 0)."""
+    layer, x = synth.make_linear(64, 256, 3, seed=8)
+    layer.codebook[0, :] = 0x00
+    layer.codebook[1, :] = 0x80
+    layer.codebook[2, :] = 0x7E            # 448
+    layer.codebook[3, :] = 0xFE            # -448
+    layer.codebook[4, :] = 0x01            # 2^-9
+    layer.codebook[5, ::2] = 0x38
+    layer.scales[6, :] = 16
+    layer.scales[7, :] = 240
+    layer.scales[8, :] = np.array([16, 240, 127, 100, 150, 16, 240, 127], dtype=np.uint8)
+    w = pack_layer(q3, layer)
+    y_ref, bound = oracle_linear(layer, x)
+    for fn in ("q3_gemv", "q3_gemm_small_m"):
+        y = getattr(q3, fn)(w, dev(x)).cpu().numpy()
+        assert_close(y, y_ref, bound, fn)
+        assert np.all(y[:, :2] == 0)
+
+
+def test_empty_matrix(q3):
+    layer, x = synth.make_linear(0, 64, 1, seed=1)
+    w = q3.empty_packed(0, 64, "cuda")
+    y = torch.empty((1, 0), dtype=torch.float32, device="cuda")
+    q3.q3_gemv(w, dev(x), y)
+    q3.q3_gemm_small_m(w, dev(x), y)
+
+
+def test_device_side_rejections(q3):
+    layer, x = synth.make_linear(16, 64, 9, seed=2)
+    w = pack_layer(q3, layer)
+    with pytest.raises(q3.Q3Error, match="UNSUPPORTED_SHAPE"):
+        q3.q3_gemv(w, dev(x))
+    xd = torch.zeros((1, 72), dtype=torch.int16, device="cuda")
+    with pytest.raises(q3.Q3Error, match="MISALIGNED"):
+        q3.q3_gemv(w, xd[:, 1:65])
+
+
+# --------------------------------------------------------------- full sizes
+
+def test_config3_full_size_sampled_rows(q3):
+    """K=8192, N=28672, M=16 (batched verify), oracle on sampled rows."""
+    layer, x = synth.make_linear(28672, 8192, 16, seed=0)
+    w = pack_layer(q3, layer)
+    y = q3.q3_gemm_small_m(w, dev(x)).cpu().numpy()
+    rows = np.sort(np.random.default_rng(0).choice(28672, 192, replace=False))
+    rows = np.concatenate([rows, [0, 15, 16, 28671]])
+    y_ref, bound = oracle_linear(layer, x, rows=rows)
+    assert_close(y[:, rows], y_ref, bound, "config 3")
+
+
+def test_config4_full_size_sampled_rows(q3):
+    """K=4096, N=151936, M=64 (vocabulary projection, fp32 logits), sampled rows."""
+    layer, x = synth.make_linear(151936, 4096, 64, seed=0)
+    w = pack_layer(q3, layer)
+    del layer.codes
+    y = q3.q3_gemm_small_m(w, dev(x)).cpu().numpy()
+    layer2, _ = synth.make_linear(151936, 4096, 64, seed=0)
+    rows = np.sort(np.random.default_rng(1).choice(151936, 160, replace=False))
+    rows = np.concatenate([rows, [0, 151935]])
+    y_ref, bound = oracle_linear(layer2, x, rows=rows)
+    assert_close(y[:, rows], y_ref, bound, "config 4")
+
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_config1_full_gemv_and_mfma(q3, m):
+    layer, x = synth.make_linear(4096, 4096, m, seed=0)
+    w = pack_layer(q3, layer)
+    y_ref, bound = oracle_linear(layer, x)
+    assert_close(q3.q3_gemv(w, dev(x)).cpu().numpy(), y_ref, bound, "gemv config 1")
+    assert_close(q3.q3_gemm_small_m(w, dev(x)).cpu().numpy(), y_ref, bound, "mfma config 1")
