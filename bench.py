@@ -1,0 +1,387 @@
+#!/usr/bin/env python3
+"""Benchmark of the 3-bit FP8-codebook decode linear layer on one MI355X.
+
+Headline (the JSON line's `value`): packed-weight GB/s of the M=1 decode GEMV
+on the 4096 x 4096 layer shape (K = N = 4096, M = 1), streamed over a stack of
+distinct packed copies of that layer so every launch reads cold weights from
+HBM (the stack is larger than twice the 256 MB last-level cache).  One *step*
+is one pass over the stack: one launch per layer, back to back on one stream,
+replayed from a HIP graph.  value = payload bytes per step / step time, where
+payload = N*K*13/32 bytes per layer (3-bit codes + one 8-bit scale per 32
+weights, 3.25 bits/weight).
+
+The same line carries:
+  roofline      the dominant kernel's algorithmic bytes per launch over its
+                average launch duration (HIP events on the launch stream),
+                against the 8 TB/s HBM peak; traffic from rocprofv3 counters
+                when the committed counter file matches the current sources.
+  cpu_baseline  the CPU oracle (numpy fp64) on a bounded sample of the same
+                layer, on this host's cores.
+  points        per-kernel throughput at M = 1/4/8 (4096 x 4096), M = 16
+                (K=8192, N=28672), M = 64 (K=4096, N=151936) and the
+                expert-grouped MoE verify round, each on cold rotating copies.
+
+Inputs are synthetic and seeded (codes uniform 0..7, per-row codebooks of
+N(0,1) draws rounded to E4M3, power-of-two group scales 2^-10..2^-4, bf16
+N(0,1) activations); no dataset or trained weight is involved.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+LLC_BYTES = 256 << 20
+METRIC = "packed-weight HBM GB/s and % of MI355X peak at M=1/8/64; oracle-exact"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_fp8_codebook_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def to_dev(a):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda")
+
+
+def copies_for(nbytes: int, minimum: int = 2) -> int:
+    """Distinct copies so that one cycle through them is >= 2x the LLC."""
+    return max(minimum, -(-2 * LLC_BYTES // max(nbytes, 1)))
+
+
+class Timer:
+    """HIP events recorded on the stream the kernels are launched on."""
+
+    def __init__(self, stream):
+        import torch
+        self.stream = stream
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.a.record(self.stream)
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record(self.stream)
+        self.b.synchronize()
+        self.ms = self.a.elapsed_time(self.b)
+
+
+def capture(fn, stream):
+    """Capture fn() (a sequence of library launches on `stream`) into a graph."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fn()                       # warm: loads code objects, sets attributes
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, stream, reps: int, warmup: int) -> float:
+    import torch
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        with Timer(stream) as t:
+            for _ in range(reps):
+                g.replay()
+    return t.ms / reps
+
+
+def algorithmic_bytes(n, k, m):
+    """Payload (codes + scales) + codebook + bf16 activations + fp32 outputs."""
+    return n * k * 13 // 32 + 8 * n + 2 * m * k + 4 * m * n
+
+
+# ------------------------------------------------------------------ points
+
+def linear_point(q3, synth, n, k, m, kernel, reps=20, warmup=3, name=""):
+    import torch
+    layer, x = synth.make_linear(n, k, m, seed=0)
+    w0 = q3.q3_pack(to_dev(layer.codes), to_dev(layer.scales), to_dev(layer.codebook))
+    del layer
+    ncopy = copies_for(w0.payload_bytes)
+    ws = [w0] + [w0.clone() for _ in range(ncopy - 1)]
+    xd = to_dev(x)
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    fn = q3.q3_gemv if kernel == "gemv" else q3.q3_gemm_small_m
+    stream = torch.cuda.Stream()
+    g = capture(lambda: [fn(w, xd, y) for w in ws], stream)
+    ms = time_graph(g, stream, reps, warmup)
+    us = ms * 1e3 / len(ws)
+    payload = n * k * 13 // 32
+    flops = 2.0 * m * n * k
+    pt = dict(name=name, n=n, k=k, m=m, kernel=kernel, copies=len(ws), us_per_launch=round(us, 2),
+              payload_GBps=round(payload / us / 1e3, 1),
+              pct_of_8TBps=round(100 * payload / us / 1e3 / HBM_PEAK_GBPS, 1),
+              algorithmic_GBps=round(algorithmic_bytes(n, k, m) / us / 1e3, 1),
+              tokens_per_s=round(m / (us * 1e-6), 1),
+              mfma_pct_of_bf16_peak=round(100 * flops / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 2)
+              if kernel == "mfma" else None)
+    del ws, w0, g
+    torch.cuda.empty_cache()
+    return pt
+
+
+def moe_point(q3, synth, reps=20, warmup=3):
+    """Config 2: 64 experts (gate/up 2048->1536, down 768->2048), 8 drafted
+    tokens, top-8 routing; one round = router + grouped gate/up + grouped down."""
+    import numpy as np
+    import torch
+    moe = synth.make_moe(seed=0)
+    E = len(moe.experts_gu)
+
+    def stack(layers):
+        L = layers[0]
+        st = q3.empty_stack(E, L.n, L.k, "cuda")
+        for e, layer in enumerate(layers):
+            q3.q3_pack(to_dev(layer.codes), to_dev(layer.scales), to_dev(layer.codebook), out=st.expert(e))
+        return st
+
+    st_gu0, st_dn0 = stack(moe.experts_gu), stack(moe.experts_dn)
+    per_expert = st_gu0.payload_bytes_per_expert + st_dn0.payload_bytes_per_expert
+    ncopy = copies_for(E * per_expert)
+    stacks = [(st_gu0, st_dn0)]
+    for _ in range(ncopy - 1):
+        a, b = st_gu0, st_dn0
+        stacks.append((q3.ExpertStack(E, a.n, a.k, a.code_plane.clone(), a.scale_plane.clone(), a.codebook.clone()),
+                       q3.ExpertStack(E, b.n, b.k, b.code_plane.clone(), b.scale_plane.clone(), b.codebook.clone())))
+    logits = to_dev(moe.logits)
+    x = to_dev(moe.x)
+    x_dn = to_dev(np.ascontiguousarray(moe.x_dn).reshape(-1, moe.x_dn.shape[-1]))
+    t, topk = moe.logits.shape[0], 8
+    ids = torch.empty((t, topk), dtype=torch.int32, device="cuda")
+    y_gu = torch.empty((t * topk, st_gu0.n), dtype=torch.float32, device="cuda")
+    y_dn = torch.empty((t * topk, st_dn0.n), dtype=torch.float32, device="cuda")
+
+    def round_all():
+        for gu, dn in stacks:
+            q3.q3_moe_topk(logits, topk, ids)
+            q3.q3_grouped_expert_gemv(gu, x, ids, False, y_gu)
+            q3.q3_grouped_expert_gemv(dn, x_dn, ids, True, y_dn)
+
+    stream = torch.cuda.Stream()
+    g = capture(round_all, stream)
+    ms = time_graph(g, stream, reps, warmup)
+    us = ms * 1e3 / len(stacks)
+    union = int(np.unique(ids.cpu().numpy()).size)
+    payload = union * per_expert
+    pt = dict(name="moe_verify_round", experts=E, tokens=t, topk=topk, experts_read=union,
+              copies=len(stacks), us_per_round=round(us, 2), union_payload_bytes=payload,
+              payload_GBps=round(payload / us / 1e3, 1),
+              pct_of_8TBps=round(100 * payload / us / 1e3 / HBM_PEAK_GBPS, 1),
+              tokens_per_s=round(t / (us * 1e-6), 1), kernel="mfma grouped + top-k router")
+    del stacks, g
+    torch.cuda.empty_cache()
+    return pt
+
+
+# -------------------------------------------------------------- cpu baseline
+
+def cpu_baseline(synth, budget_s=12.0):
+    """The CPU oracle on the 4096 x 4096, M = 1 layer: unpack from the packed
+    planes, fp64 dequantisation and products, as the tests use it."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    cores = len(os.sched_getaffinity(0))
+    layer, x = synth.make_linear(4096, 4096, 1, seed=0)
+    cp, sp = oracle.pack(layer.codes, layer.scales)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.linear(cp, sp, layer.codebook, 4096, 4096, x)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    per = el / reps
+    payload = 4096 * 4096 * 13 // 32
+    return dict(value=round(payload / per / 1e9, 4), unit="GB/s", cores=int(min(threads, cores)),
+                kind="oracle", seconds_per_layer=round(per, 3), host_cores=cores,
+                sample=f"{reps} oracle passes over one 4096x4096 layer at M=1 "
+                       "(unpack from packed planes, fp64 dequant and product)")
+
+
+def read_traffic(kernel_name):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("kernels", {}).get(kernel_name)
+
+
+# --------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=0, help="layer copies per step (default: >= 2x LLC)")
+    ap.add_argument("--kernel", choices=["auto", "gemv", "mfma"], default="auto")
+    ap.add_argument("--no-points", action="store_true", help="skip the per-config points")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 256 MiB device copy first (scale reference for counter runs)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py measures one GPU only: the decode linear layer is benchmarked on a single "
+                  "MI355X (multi-GPU sharding is a design note, not a measured path); run with --gpus 1.",
+                  file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import bit_fp8_codebook_amd as q3
+    import synth
+    q3.lib()
+    torch.cuda.init()
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    n = k = 4096
+    m = 1
+    layer, x = synth.make_linear(n, k, m, seed=0)
+    w0 = q3.q3_pack(to_dev(layer.codes), to_dev(layer.scales), to_dev(layer.codebook))
+    xd = to_dev(x)
+
+    # Parity of the measured layer against the oracle (the metric is oracle-exact).
+    import oracle
+    cp, sp = oracle.pack(layer.codes, layer.scales)
+    y_ref, bound = oracle.linear(cp, sp, layer.codebook, n, k, x)
+    parity = {}
+    for name, fn in (("gemv", q3.q3_gemv), ("mfma", q3.q3_gemm_small_m)):
+        ok, ratio = oracle.within_tolerance(fn(w0, xd).cpu().numpy(), y_ref, bound)
+        parity[name] = dict(ok=ok, max_err_over_bound=ratio)
+        if not ok:
+            log(f"parity FAILED for {name}: {ratio:.3e}")
+            sys.exit(1)
+
+    layers = args.layers or copies_for(w0.payload_bytes, minimum=64)
+    ws = [w0] + [w0.clone() for _ in range(layers - 1)]
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    kernels = {"gemv": q3.q3_gemv, "mfma": q3.q3_gemm_small_m}
+
+    # Pick the faster M=1 kernel on this stack (both are reported in points).
+    probe = {}
+    for name, fn in kernels.items():
+        g = capture(lambda fn=fn: [fn(w, xd, y) for w in ws], stream)
+        probe[name] = time_graph(g, stream, 5, 2)
+        del g
+    chosen = min(probe, key=probe.get) if args.kernel == "auto" else args.kernel
+    fn = kernels[chosen]
+    g = capture(lambda: [fn(w, xd, y) for w in ws], stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            g.replay()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    with torch.cuda.stream(stream):
+        with Timer(stream) as t:
+            for _ in range(args.steps):
+                g.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = t.ms / args.steps
+    payload = w0.payload_bytes
+    value = layers * payload / (ms_step * 1e-3) / 1e9
+    launch_us = ms_step * 1e3 / layers
+    alg = algorithmic_bytes(n, k, m)
+    achieved = alg / (launch_us * 1e-6) / 1e9
+    kname = {"gemv": "gemv_kernel<1, true>", "mfma": "mfma_kernel<1, false, true>"}[chosen]
+    traffic = read_traffic(kname)
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic,
+                    kernel=kname, algorithmic_bytes_per_launch=alg, avg_launch_us=round(launch_us, 3))
+
+    points = []
+    if not args.no_points:
+        for kn in ("gemv", "mfma"):
+            for mm in (1, 4, 8):
+                points.append(linear_point(q3, synth, 4096, 4096, mm, kn, name=f"4096x4096 M={mm}"))
+                log(points[-1])
+        points.append(linear_point(q3, synth, 28672, 8192, 16, "mfma", name="K=8192 N=28672 M=16"))
+        log(points[-1])
+        points.append(linear_point(q3, synth, 151936, 4096, 64, "mfma", reps=5, name="K=4096 N=151936 M=64"))
+        log(points[-1])
+        points.append(moe_point(q3, synth))
+        log(points[-1])
+        points.append(linear_point(q3, synth, 1024, 1024, 1, chosen, name="1024x1024 M=1"))
+        log(points[-1])
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(synth)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded codes, E4M3 codebooks, E8M0 scales, bf16 N(0,1) activations)",
+        "config": {"workload": f"decode GEMV, K=4096 N=4096 M=1, {layers} cold layer copies per step",
+                   "K": k, "N": n, "M": m, "layers_per_step": layers, "kernel": chosen,
+                   "pct_of_8TBps": round(100 * value / HBM_PEAK_GBPS, 2),
+                   "tokens_per_s_per_layer": round(m / (launch_us * 1e-6), 1),
+                   "wall_s_timed_region": round(wall, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "kernel_choice_ms_per_step": {k_: round(v_, 4) for k_, v_ in probe.items()},
+        "points": points,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

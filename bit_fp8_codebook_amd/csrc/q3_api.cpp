@@ -11,6 +11,7 @@
 namespace {
 
 constexpr int64_t kGroup = 32;
+constexpr int64_t kMaxPlaneBytes = (int64_t(1) << 31) - (int64_t(1) << 24);   // per plane, and for x
 
 int64_t chunks_of(int64_t k) { return (k + 127) / 128; }
 int64_t code_row_min(int64_t k) { return 48 * chunks_of(k); }
@@ -34,6 +35,8 @@ q3_status check_planes(int64_t n, int64_t k, const void* code, int64_t code_pitc
   if (code_pitch < code_row_min(k) || scale_pitch < scale_row_min(k)) return Q3_ERR_INVALID_ARG;
   if (code_pitch % 16 || scale_pitch % 4) return Q3_ERR_MISALIGNED;
   if (!aligned(code, 16) || !aligned(scale, 4) || !aligned(cb, 8)) return Q3_ERR_MISALIGNED;
+  // The kernels address each plane through a 32-bit buffer resource.
+  if (n * code_pitch > kMaxPlaneBytes || n * scale_pitch > kMaxPlaneBytes) return Q3_ERR_UNSUPPORTED_SHAPE;
   return Q3_OK;
 }
 
@@ -49,6 +52,7 @@ q3_status check_tokens(int64_t k, int64_t n, const uint16_t* x, int64_t m, int64
   if (!x || (!y && n > 0)) return Q3_ERR_INVALID_ARG;
   if (ldx < k || ldy < n) return Q3_ERR_INVALID_ARG;
   if (ldx % 8 || !aligned(x, 16) || !aligned(y, 4)) return Q3_ERR_MISALIGNED;
+  if ((m - 1) * ldx * 2 + k * 2 > kMaxPlaneBytes) return Q3_ERR_UNSUPPORTED_SHAPE;
   return Q3_OK;
 }
 

@@ -73,4 +73,44 @@ __device__ __forceinline__ void dequant_group_bf16(uint32_t d0, uint32_t d1, uin
 
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
 
+// Where word j of group g sits inside a row.  Groups (padded to gp, a multiple
+// of 4) are stored in superchunks of 16; inside a superchunk of p groups the
+// three words are word-major: word j of its group t is at 4*(p*j + t).  A
+// 16-byte load then carries one word of 4 consecutive groups, and the four
+// such loads of a superchunk word are one contiguous 64-byte run.
+__device__ __forceinline__ uint32_t superchunk_groups(uint32_t s, uint32_t gp) {
+  const uint32_t rest = gp - 16u * s;
+  return rest < 16u ? rest : 16u;
+}
+__device__ __forceinline__ uint32_t word_offset(uint32_t g, uint32_t j, uint32_t gp) {
+  const uint32_t s = g >> 4, t = g & 15u;
+  return 192u * s + 4u * (superchunk_groups(s, gp) * j + t);
+}
+
+// Raw buffer resources: loads whose byte offset lies past num_records return
+// zero, which the kernels use instead of branches around out-of-range rows,
+// groups and tokens.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// An offset past every buffer: planes are kept below 2 GiB, so kOob plus any
+// in-kernel step advance stays out of range without wrapping.
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4 bload128(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 bload64(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload8(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
 }  // namespace q3

@@ -30,10 +30,10 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* __restri
       }
     }
   }
-  uint32_t* out = reinterpret_cast<uint32_t*>(plane + r * pitch) + 3 * g;
-  out[0] = w[0];
-  out[1] = w[1];
-  out[2] = w[2];
+  uint8_t* row = plane + r * pitch;
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    *reinterpret_cast<uint32_t*>(row + word_offset((uint32_t)g, (uint32_t)j, (uint32_t)padded_groups)) = w[j];
 }
 
 __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restrict__ scales, int64_t lds,
@@ -51,9 +51,13 @@ __global__ __launch_bounds__(256) void unpack_kernel(PlaneView w, uint8_t* __res
   const int64_t G = w.groups;
   if (idx >= w.n * G) return;
   const int64_t r = idx / G, g = idx % G;
-  const uint32_t* p = reinterpret_cast<const uint32_t*>(w.code + r * w.code_pitch) + 3 * g;
+  const uint8_t* row = w.code + r * w.code_pitch;
+  const uint32_t gp = ((uint32_t)G + 3u) & ~3u;
+  uint32_t d[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) d[j] = *reinterpret_cast<const uint32_t*>(row + word_offset((uint32_t)g, j, gp));
   uint32_t sel[8];
-  unpack_selectors(p[0], p[1], p[2], sel);
+  unpack_selectors(d[0], d[1], d[2], sel);
   uint32_t* out = reinterpret_cast<uint32_t*>(codes + r * G * kGroup + g * kGroup);
 #pragma unroll
   for (int i = 0; i < 8; ++i) out[i] = sel[i];   // selector bytes are the codes in K order

@@ -17,11 +17,14 @@
  * ---- Packed format (all planes are row-major, one row per output n) ----------
  *   groups G = k/32, chunks C = ceil(k/128) (a chunk is 4 groups)
  *   code plane : uint32 words, row pitch code_row_bytes >= 48*C (multiple of 16).
- *                Group g of row n is the 3 words at byte offset n*pitch + 12*g.
- *                Byte b (0..3) of word j (0..2) of a group with codes c[0..31]:
+ *                A group's 96 code bits are 3 words.  Byte b (0..3) of word j
+ *                (0..2) of a group with codes c[0..31]:
  *                  bits 0..2 = c[8j+b], bits 3..5 = c[8j+4+b],
  *                  bits 6..7 = bits 2j..2j+1 of (c[24+b] | c[28+b] << 3).
- *                Groups past G in the last chunk are zero.
+ *                Placement: the row's Gp = 4*C groups form superchunks of 16
+ *                groups (192 bytes; the last holds p = 4, 8, 12 or 16), and in
+ *                a superchunk of p groups word j of its group t sits at byte
+ *                192*s + 4*(p*j + t).  Groups past G are zero padding.
  *   scale plane: uint8, row pitch scale_row_bytes >= round_up(4*C, 16); byte g
  *                of row n is the E8M0 scale of group g; padding is zero.
  *   codebook   : uint8 [n][8], E4M3FN bytes, entry j is what code j selects.
@@ -38,6 +41,10 @@
  *     once-per-device capability check.
  *   * Arguments are validated on the host before any HIP call; a rejected call
  *     launches nothing.  Launch failures are reported as Q3_ERR_HIP.
+ *   * Size limits: each plane (n * pitch bytes) and the activation block
+ *     ((m-1)*ldx*2 + k*2 bytes) must stay below 2 GiB - 16 MiB
+ *     (Q3_ERR_UNSUPPORTED_SHAPE otherwise); x needs ldx % 8 == 0 and 16-byte
+ *     alignment, y 4-byte alignment (Q3_ERR_MISALIGNED).
  *   * Numerics: products are formed exactly and accumulated in fp32, so every
  *     output satisfies |y - y_exact| <= 1e-3 * sum_k |x_k w_k| for k <= 8192.
  *     Preconditions (not checked on the device): scale bytes in [16, 240],

@@ -24,7 +24,8 @@ Readings taken where the page is silent (each also listed in the design notes):
   * the scale multiplies the codebook value;
   * activations are bf16, outputs fp32 (oracle: fp64);
   * the bit order of the 96 code bits of a group is this project's own
-    "byte-lane" layout (see pack_group).
+    "byte-lane" layout (see pack_group), and so is the placement of a
+    group's three words inside its row (see word_offsets).
 MoE verify rounds (same page, "Adaptive speculation" -- "Expert sharing"):
 verifying drafted tokens reads every expert any of them picked; the oracle
 routes each token to its top-k experts by router logit (ties to the lower
@@ -36,7 +37,8 @@ Parity status per function (what pins each one lives in tests/test_oracle.py):
   bf16_decode     pinned: torch.bfloat16 for random and special bit patterns
   layout          pinned: payload = n*k*13/32 (3.25 bits/weight closed form)
   pack_group      pinned: hand-derived worked example, brute-force round trip
-  pack/unpack     pinned: round trip, worked example, padding is zero
+  word_offsets    pinned: hand-derived offsets, every code byte covered once
+  pack/unpack     pinned: round trip, worked examples, padding is zero
   linear          pinned: torch fp64 matmul of torch-decoded weights, closed
                   forms (one-hot codebook, constant codes, single group),
                   exact Fraction brute force on tiny K
@@ -97,8 +99,9 @@ def bf16_decode(bits) -> np.ndarray:
 def layout(n: int, k: int) -> dict:
     """Sizes of the packed planes for an n x k matrix.
 
-    Codes: per row ceil(k/128) chunks of 4 groups x 12 bytes (48 bytes, three
-    16-byte loads); groups past k/32 in the last chunk are zero padding.
+    Codes: per row ceil(k/128) chunks of 4 groups x 12 bytes; groups past
+    k/32 in the last chunk are zero padding.  Where each word of a group sits
+    inside the row is given by word_offsets.
     Scales: one byte per group, row pitch 4*ceil(k/128) rounded up to 16.
     Codebook: 8 bytes per row.  Payload counts only real codes and scales:
     k/32 * 13 bytes per row = n*k*13/32 bytes, i.e. 3.25 bits per weight.
@@ -185,6 +188,34 @@ def _unpack_bytes(by):
     return c
 
 
+def word_offsets(k: int) -> np.ndarray:
+    """Byte offset inside a row of word j (0..2) of group g, as int [Gp][3]
+    over the padded groups Gp = 4*ceil(k/128).
+
+    Groups are stored in superchunks of 16 consecutive groups (192 bytes); the
+    last superchunk of a row holds p = 4, 8, 12 or 16 groups.  Inside a
+    superchunk of p groups the words are stored word-major: word j of its
+    group t (0 <= t < p) is at byte 4*(p*j + t) from the superchunk start.
+    So the first words of all groups of a superchunk are contiguous, then all
+    second words, then all third words.
+    """
+    gp = layout(1, k)["chunks"] * CHUNK_GROUPS
+    off = np.empty((gp, 3), dtype=np.int64)
+    for g in range(gp):
+        s, t = divmod(g, 16)
+        p = min(16, gp - 16 * s)
+        for j in range(3):
+            off[g, j] = 192 * s + 4 * (p * j + t)
+    return off
+
+
+def _byte_index(k: int) -> np.ndarray:
+    """Row byte position of byte 4j+b of every real group's 12 packed bytes, [G][12]."""
+    G = k // GROUP
+    off = word_offsets(k)[:G]
+    return (off[:, :, None] + np.arange(4)[None, None, :]).reshape(G, 12)
+
+
 def pack(codes: np.ndarray, scales: np.ndarray):
     """codes uint8 [n][k] (only bits 0..2 used), scales uint8 [n][k/32] ->
     (code_plane uint8 [n][code_row_bytes], scale_plane uint8 [n][scale_row_bytes]),
@@ -193,7 +224,7 @@ def pack(codes: np.ndarray, scales: np.ndarray):
     L = layout(n, k)
     G = L["groups"]
     cp = np.zeros((n, L["code_row_bytes"]), dtype=np.uint8)
-    cp[:, :G * 12] = _pack_bytes(codes.reshape(n, G, 32)).reshape(n, G * 12)
+    cp[:, _byte_index(k).reshape(-1)] = _pack_bytes(codes.reshape(n, G, 32)).reshape(n, G * 12)
     sp = np.zeros((n, L["scale_row_bytes"]), dtype=np.uint8)
     sp[:, :G] = scales
     return cp, sp
@@ -202,7 +233,7 @@ def pack(codes: np.ndarray, scales: np.ndarray):
 def unpack(code_plane: np.ndarray, scale_plane: np.ndarray, n: int, k: int):
     """(code_plane, scale_plane) -> (codes uint8 [n][k], scales uint8 [n][k/32])."""
     G = k // GROUP
-    by = np.ascontiguousarray(code_plane[:n, :G * 12]).reshape(n, G, 12)
+    by = np.ascontiguousarray(code_plane[:n][:, _byte_index(k).reshape(-1)]).reshape(n, G, 12)
     return _unpack_bytes(by).reshape(n, k), np.ascontiguousarray(scale_plane[:n, :G])
 
 

@@ -41,7 +41,8 @@ def test_pack_bit_exact(q3, n, k):
 def test_pack_worked_example(q3):
     codes = np.array([[k % 8 for k in range(32)]], dtype=np.uint8)
     w = q3.q3_pack(dev(codes), dev(np.array([[127]], dtype=np.uint8)), dev(np.zeros((1, 8), np.uint8)))
-    words = w.code_plane.cpu().numpy()[0, :12].view(np.uint32)
+    row = w.code_plane.cpu().numpy()[0]
+    words = [int(row[16 * j:16 * j + 4].view(np.uint32)[0]) for j in range(3)]   # k = 32: words at 0, 16, 32
     assert [hex(v) for v in words] == ["0xfbb26920", "0xbb32a920", "0xfbf2a9a0"]
 
 

@@ -86,7 +86,27 @@ def test_worked_example():
     assert oracle.pack_group(codes) == words
     assert oracle.unpack_group(words) == codes
     cp, _ = oracle.pack(np.array(codes, dtype=np.uint8)[None, :], np.array([[127]], dtype=np.uint8))
-    assert cp[0, :12].tobytes() == b"".join(w.to_bytes(4, "little") for w in words)
+    # k = 32: one group in a 4-group superchunk, so its words sit at bytes 0, 16 and 32.
+    for j, w in enumerate(words):
+        assert cp[0, 16 * j:16 * j + 4].tobytes() == w.to_bytes(4, "little")
+    assert not np.delete(cp[0], [b for j in range(3) for b in range(16 * j, 16 * j + 4)]).any()
+
+
+def test_word_placement_worked_examples():
+    for row in read_golden("word_placement.txt"):
+        k, g, j, byte = (int(v) for v in row.split())
+        assert oracle.word_offsets(k)[g, j] == byte, (k, g, j)
+
+
+@pytest.mark.parametrize("k", [32, 96, 128, 160, 640, 768, 1024, 4096, 8224])
+def test_word_placement_covers_each_code_byte_once(k):
+    off = oracle.word_offsets(k)
+    L = oracle.layout(1, k)
+    cover = np.zeros(L["code_row_bytes"], dtype=np.int64)
+    for b in range(4):
+        np.add.at(cover, (off + b).reshape(-1), 1)
+    assert np.all(cover == 1)
+    assert off.min() == 0 and off.max() + 4 == L["code_row_bytes"]
 
 
 def test_each_code_position_owns_three_distinct_bits():
@@ -129,7 +149,9 @@ def test_plane_roundtrip_padding_and_masking(n, k):
     L = oracle.layout(n, k)
     assert cp.shape == (n, L["code_row_bytes"]) and sp.shape == (n, L["scale_row_bytes"])
     G = k // 32
-    assert not cp[:, G * 12:].any() and not sp[:, G:].any()
+    off = oracle.word_offsets(k)
+    pad = [int(o) + b for o in off[G:].reshape(-1) for b in range(4)]   # words of padding groups
+    assert not cp[:, pad].any() and not sp[:, G:].any()
     c2, s2 = oracle.unpack(cp, sp, n, k)
     assert np.array_equal(c2, codes & 7) and np.array_equal(s2, scales)
 
