@@ -147,8 +147,10 @@ __device__ __forceinline__ void stage_chunks(rsrc_t r, int count, uint8_t* lds, 
   }
 }
 
+// One-column-tile instances are held to 128 registers per lane, i.e. 4 waves
+// per SIMD: a decode launch needs every wave resident at once.
 template <int MT, bool kGrouped, bool kFullK>
-__global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
+__global__ __launch_bounds__(kThreads, MT == 1 ? 4 : 1) void mfma_kernel(MfmaArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ Tokens tk;
   __shared__ int pairs[64];
@@ -211,6 +213,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
   // reads at once fall into different banks.
   WStep A, B;
   load_step(t, s0, A);
+  load_step(t, s0 + 1, B);
   const uint32_t sstride = (((uint32_t)gp + 15u) & ~15u) + 16u;
   const int block_rows = 16 * rb;
   {
@@ -252,7 +255,10 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
     }
     __syncthreads();
     const int cnt = __builtin_amdgcn_readfirstlane(tk.count);
-    if (slice > 0) load_step(t, s0, A);
+    if (slice > 0) {
+      load_step(t, s0, A);
+      load_step(t, s0 + 1, B);
+    }
 
     f32x4 acc[MT];
 #pragma unroll
@@ -292,16 +298,18 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
         const uint32_t sc = *reinterpret_cast<const uint32_t*>(lds + sc_lane + 16u * s);
         compute_step<MT>(ws, sc, full ? cb.x : cbl_last, full ? cb.y : cbh_last, xb, xlds, acc);
       };
-      // The scheduling barriers keep each prefetch ahead of the computation it
-      // overlaps; without them the compiler sinks the loads below the MFMAs.
+      // Two steps are in flight when the loop starts; each computed step's
+      // registers are refilled with the step two ahead.  The scheduling
+      // barriers keep each refill where it is issued; without them the
+      // compiler sinks the loads below the MFMAs.
       for (int s = s0; s < s1; s += 2) {
-        load_step(t, s + 1, B);
-        __builtin_amdgcn_sched_barrier(0);
         run(A, s);
-        if (s + 1 >= s1) break;
         load_step(t, s + 2, A);
         __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 >= s1) break;
         run(B, s + 1);
+        load_step(t, s + 3, B);
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
       // Stream the activations one 512-k step at a time through two buffers of
@@ -344,16 +352,16 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
       fetch(s0 + 1, xr);
       __syncthreads();
       for (int s = s0; s < s1; s += 2) {
-        load_step(t, s + 1, B);
-        __builtin_amdgcn_sched_barrier(0);
         run(A, s);
+        load_step(t, s + 2, A);
+        __builtin_amdgcn_sched_barrier(0);
         put((s + 1 - s0) & 1, xr);   // buffer last read at step s-1
         fetch(s + 2, xr);
         __syncthreads();
         if (s + 1 >= s1) break;
-        load_step(t, s + 2, A);
-        __builtin_amdgcn_sched_barrier(0);
         run(B, s + 1);
+        load_step(t, s + 3, B);
+        __builtin_amdgcn_sched_barrier(0);
         put((s + 2 - s0) & 1, xr);
         fetch(s + 3, xr);
         __syncthreads();
@@ -393,14 +401,28 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
   }
 }
 
-// K split over the block's waves (full-K mode): split until there are enough
-// blocks to occupy the chip, never more ways than there are 512-k steps.
-int choose_split(int64_t n, int groups) {
+// K split over the block's waves (full-K mode): the largest split whose blocks
+// are all resident at once (`capacity` blocks on the chip), so no second round
+// of waves starts after the first drains; never more ways than there are
+// 512-k steps.
+int choose_split(int64_t n, int groups, int64_t capacity) {
   const int64_t tiles = (n + 15) / 16;
   const int steps = (((groups + 3) & ~3) + 15) / 16;
   int sk = 1;
-  while (sk < 4 && (tiles + (4 / sk) - 1) / (4 / sk) < 1024 && sk * 2 <= steps) sk *= 2;
+  while (sk < 4 && (tiles * sk * 2 + 3) / 4 <= capacity && sk * 2 <= steps) sk *= 2;
   return sk;
+}
+
+// Blocks of a kernel instance that fit on the device at once.
+template <int MT, bool kGrouped, bool kFullK>
+int64_t resident_blocks(size_t shm) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mfma_kernel<MT, kGrouped, kFullK>, kThreads, shm) !=
+          hipSuccess)
+    return 1024;
+  return (int64_t)cus * (per_cu > 0 ? per_cu : 1);
 }
 
 size_t scale_stage_bytes(int groups, int rb) {
@@ -436,12 +458,13 @@ hipError_t launch_cfg(MfmaArgs a, int tokens_in_slice, unsigned grid_y, hipStrea
   const int64_t tiles = (a.n + 15) / 16;
   const size_t fk = full_k_bytes(tokens_in_slice, a.G);
   if (fk + scale_stage_bytes(a.G, 4) <= (size_t)kFullKBudget) {
-    a.sk = kGrouped ? 1 : choose_split(a.n, a.G);
-    const int rb = 4 / a.sk;
+    // LDS with the largest split's needs (the scale staging shrinks as rb does).
     size_t shm = fk;
     const size_t red = (size_t)4 * MT * 64 * 16;
-    if (a.sk > 1 && shm < red) shm = red;
-    shm += scale_stage_bytes(a.G, rb);
+    if (shm < red) shm = red;
+    shm += scale_stage_bytes(a.G, 4);
+    a.sk = kGrouped ? 1 : choose_split(a.n, a.G, resident_blocks<MT, kGrouped, true>(shm));
+    const int rb = 4 / a.sk;
     const dim3 grid((unsigned)((tiles + rb - 1) / rb), grid_y);
     hipError_t e = allow_lds<MT, kGrouped, true>(shm);
     if (e != hipSuccess) return e;
