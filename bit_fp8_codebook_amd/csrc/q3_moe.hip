@@ -1,8 +1,8 @@
 // Router of an MoE verify round over 3.25-bit experts.
 //
 // Hibana: Fast Agentic Inference on Unified-Memory Devices, "Adaptive
-// speculation" / "Expert sharing": verifying a round of drafted tokens reads
-// every expert any of them picked.  This kernel picks each token's top-k
+// speculation" / "Expert sharing": a verify round must read each expert chosen
+// by at least one of its drafted tokens.  This kernel picks each token's top-k
 // experts on the device; the expert-grouped product (q3_mfma.hip) then reads
 // each picked expert once, without the list of picked experts ever coming back
 // to the host.

@@ -26,10 +26,11 @@ Readings taken where the page is silent (each also listed in the design notes):
   * the bit order of the 96 code bits of a group is this project's own
     "byte-lane" layout (see pack_group), and so is the placement of a
     group's three words inside its row (see word_offsets).
-MoE verify rounds (same page, "Adaptive speculation" -- "Expert sharing"):
-verifying drafted tokens reads every expert any of them picked; the oracle
-routes each token to its top-k experts by router logit (ties to the lower
-expert index) and reports the union.
+MoE verify rounds (same page, "Adaptive speculation" -- "Expert sharing"): a
+round that checks several drafted tokens at once must read the weights of
+each expert chosen by at least one of those tokens; the oracle routes each
+token to its top-k experts by router logit (ties to the lower expert index)
+and reports that union.
 
 Parity status per function (what pins each one lives in tests/test_oracle.py):
   e4m3fn_decode   pinned: all 256 bytes vs torch.float8_e4m3fn, spec values
