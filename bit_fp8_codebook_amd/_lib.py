@@ -22,19 +22,19 @@ c_vp = ctypes.c_void_p
 
 
 class Q3LayoutInfo(ctypes.Structure):
-    _fields_ = [(f, c_i64) for f in ("n", "k", "groups", "chunks", "code_row_bytes", "scale_row_bytes",
-                                     "code_plane_bytes", "scale_plane_bytes", "codebook_bytes", "payload_bytes")]
+    _fields_ = [(f, c_i64) for f in ("n", "k", "groups", "padded_groups", "tiles", "code_tile_bytes",
+                                     "scale_tile_bytes", "code_plane_bytes", "scale_plane_bytes", "codebook_bytes",
+                                     "payload_bytes")]
 
 
 class Q3Matrix(ctypes.Structure):
-    _fields_ = [("n", c_i64), ("k", c_i64), ("code_plane", c_vp), ("code_row_bytes", c_i64),
-                ("scale_plane", c_vp), ("scale_row_bytes", c_i64), ("codebook", c_vp)]
+    _fields_ = [("n", c_i64), ("k", c_i64), ("code_plane", c_vp), ("scale_plane", c_vp), ("codebook", c_vp)]
 
 
 class Q3ExpertStack(ctypes.Structure):
     _fields_ = [("num_experts", c_i64), ("n", c_i64), ("k", c_i64),
-                ("code_plane", c_vp), ("code_row_bytes", c_i64), ("code_expert_stride", c_i64),
-                ("scale_plane", c_vp), ("scale_row_bytes", c_i64), ("scale_expert_stride", c_i64),
+                ("code_plane", c_vp), ("code_expert_stride", c_i64),
+                ("scale_plane", c_vp), ("scale_expert_stride", c_i64),
                 ("codebook", c_vp), ("codebook_expert_stride", c_i64)]
 
 
@@ -42,7 +42,7 @@ class Q3ExpertStack(ctypes.Structure):
 SIGNATURES = {
     "q3_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "q3_layout": (ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(Q3LayoutInfo)]),
-    "q3_pack": (ctypes.c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
+    "q3_pack": (ctypes.c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp]),
     "q3_unpack": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), c_vp, c_vp, c_vp]),
     "q3_gemv": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), c_vp, c_i64, c_i64, c_vp, c_i64, c_vp]),
     "q3_gemm_small_m": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), c_vp, c_i64, c_i64, c_vp, c_i64, c_vp]),
@@ -108,13 +108,13 @@ class PackedMatrix:
     """Device-resident packed weights of an n x k layer (planes as uint8 tensors)."""
     n: int
     k: int
-    code_plane: torch.Tensor    # uint8 [n][code_row_bytes]
-    scale_plane: torch.Tensor   # uint8 [n][scale_row_bytes]
+    code_plane: torch.Tensor    # uint8 [code_plane_bytes], tile-major
+    scale_plane: torch.Tensor   # uint8 [scale_plane_bytes], tile-major
     codebook: torch.Tensor      # uint8 [n][8] E4M3FN
 
     def desc(self) -> Q3Matrix:
-        return Q3Matrix(self.n, self.k, self.code_plane.data_ptr(), self.code_plane.stride(0),
-                        self.scale_plane.data_ptr(), self.scale_plane.stride(0), self.codebook.data_ptr())
+        return Q3Matrix(self.n, self.k, self.code_plane.data_ptr(), self.scale_plane.data_ptr(),
+                        self.codebook.data_ptr())
 
     @property
     def payload_bytes(self) -> int:
@@ -127,8 +127,8 @@ class PackedMatrix:
 
 def empty_packed(n: int, k: int, device) -> PackedMatrix:
     L = q3_layout(n, k)
-    return PackedMatrix(n, k, torch.empty((n, L["code_row_bytes"]), dtype=torch.uint8, device=device),
-                        torch.empty((n, L["scale_row_bytes"]), dtype=torch.uint8, device=device),
+    return PackedMatrix(n, k, torch.empty(L["code_plane_bytes"], dtype=torch.uint8, device=device),
+                        torch.empty(L["scale_plane_bytes"], dtype=torch.uint8, device=device),
                         torch.empty((n, 8), dtype=torch.uint8, device=device))
 
 
@@ -141,8 +141,7 @@ def q3_pack(codes: torch.Tensor, scales: torch.Tensor, codebook: torch.Tensor, o
     w = out if out is not None else empty_packed(n, k, codes.device)
     w.codebook.copy_(codebook)
     _check("q3_pack", lib().q3_pack(codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0), n, k,
-                                    w.code_plane.data_ptr(), w.code_plane.stride(0), w.scale_plane.data_ptr(),
-                                    w.scale_plane.stride(0), _stream(codes)))
+                                    w.code_plane.data_ptr(), w.scale_plane.data_ptr(), _stream(codes)))
     return w
 
 
@@ -211,14 +210,14 @@ class ExpertStack:
     num_experts: int
     n: int
     k: int
-    code_plane: torch.Tensor    # uint8 [E][n][code_row_bytes]
-    scale_plane: torch.Tensor   # uint8 [E][n][scale_row_bytes]
+    code_plane: torch.Tensor    # uint8 [E][code_plane_bytes]
+    scale_plane: torch.Tensor   # uint8 [E][scale_plane_bytes]
     codebook: torch.Tensor      # uint8 [E][n][8]
 
     def desc(self) -> Q3ExpertStack:
         return Q3ExpertStack(self.num_experts, self.n, self.k,
-                             self.code_plane.data_ptr(), self.code_plane.stride(1), self.code_plane.stride(0),
-                             self.scale_plane.data_ptr(), self.scale_plane.stride(1), self.scale_plane.stride(0),
+                             self.code_plane.data_ptr(), self.code_plane.stride(0),
+                             self.scale_plane.data_ptr(), self.scale_plane.stride(0),
                              self.codebook.data_ptr(), self.codebook.stride(0))
 
     def expert(self, e: int) -> PackedMatrix:
@@ -232,8 +231,8 @@ class ExpertStack:
 def empty_stack(num_experts: int, n: int, k: int, device) -> ExpertStack:
     L = q3_layout(n, k)
     return ExpertStack(num_experts, n, k,
-                       torch.empty((num_experts, n, L["code_row_bytes"]), dtype=torch.uint8, device=device),
-                       torch.empty((num_experts, n, L["scale_row_bytes"]), dtype=torch.uint8, device=device),
+                       torch.empty((num_experts, L["code_plane_bytes"]), dtype=torch.uint8, device=device),
+                       torch.empty((num_experts, L["scale_plane_bytes"]), dtype=torch.uint8, device=device),
                        torch.empty((num_experts, n, 8), dtype=torch.uint8, device=device))
 
 

@@ -13,9 +13,10 @@ namespace {
 constexpr int64_t kGroup = 32;
 constexpr int64_t kMaxPlaneBytes = (int64_t(1) << 31) - (int64_t(1) << 24);   // per plane, and for x
 
-int64_t chunks_of(int64_t k) { return (k + 127) / 128; }
-int64_t code_row_min(int64_t k) { return 48 * chunks_of(k); }
-int64_t scale_row_min(int64_t k) { return (4 * chunks_of(k) + 15) / 16 * 16; }
+int64_t padded_groups(int64_t k) { return (k / kGroup + 3) / 4 * 4; }
+int64_t tiles_of(int64_t n) { return (n + 15) / 16; }
+int64_t code_plane_bytes(int64_t n, int64_t k) { return tiles_of(n) * 192 * padded_groups(k); }
+int64_t scale_plane_bytes(int64_t n, int64_t k) { return tiles_of(n) * 16 * padded_groups(k); }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -26,24 +27,20 @@ q3_status check_shape(int64_t n, int64_t k) {
   return Q3_OK;
 }
 
-// Packed planes of one matrix: pointers present, pitches large enough, aligned.
-q3_status check_planes(int64_t n, int64_t k, const void* code, int64_t code_pitch, const void* scale,
-                       int64_t scale_pitch, const void* cb) {
+// Packed planes of one matrix: pointers present, aligned, addressable.
+q3_status check_planes(int64_t n, int64_t k, const void* code, const void* scale, const void* cb) {
   q3_status st = check_shape(n, k);
   if (st != Q3_OK) return st;
   if (n > 0 && (!code || !scale || !cb)) return Q3_ERR_INVALID_ARG;
-  if (code_pitch < code_row_min(k) || scale_pitch < scale_row_min(k)) return Q3_ERR_INVALID_ARG;
-  if (code_pitch % 16 || scale_pitch % 4) return Q3_ERR_MISALIGNED;
   if (!aligned(code, 16) || !aligned(scale, 4) || !aligned(cb, 8)) return Q3_ERR_MISALIGNED;
   // The kernels address each plane through a 32-bit buffer resource.
-  if (n * code_pitch > kMaxPlaneBytes || n * scale_pitch > kMaxPlaneBytes) return Q3_ERR_UNSUPPORTED_SHAPE;
+  if (code_plane_bytes(n, k) > kMaxPlaneBytes || n * 8 > kMaxPlaneBytes) return Q3_ERR_UNSUPPORTED_SHAPE;
   return Q3_OK;
 }
 
 q3_status check_matrix(const q3_matrix* w) {
   if (!w) return Q3_ERR_INVALID_ARG;
-  return check_planes(w->n, w->k, w->code_plane, w->code_row_bytes, w->scale_plane, w->scale_row_bytes,
-                      w->codebook);
+  return check_planes(w->n, w->k, w->code_plane, w->scale_plane, w->codebook);
 }
 
 q3_status check_tokens(int64_t k, int64_t n, const uint16_t* x, int64_t m, int64_t ldx, const float* y,
@@ -78,9 +75,7 @@ q3_status from_hip(hipError_t e) { return e == hipSuccess ? Q3_OK : Q3_ERR_HIP; 
 q3::PlaneView view_of(const q3_matrix* w) {
   q3::PlaneView v;
   v.code = static_cast<const uint8_t*>(w->code_plane);
-  v.code_pitch = w->code_row_bytes;
   v.scale = static_cast<const uint8_t*>(w->scale_plane);
-  v.scale_pitch = w->scale_row_bytes;
   v.cb = static_cast<const uint8_t*>(w->codebook);
   v.n = w->n;
   v.groups = static_cast<int32_t>(w->k / kGroup);
@@ -96,7 +91,7 @@ Q3_API const char* q3_status_string(q3_status s) {
     case Q3_OK: return "ok";
     case Q3_ERR_INVALID_ARG: return "invalid argument";
     case Q3_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
-    case Q3_ERR_MISALIGNED: return "misaligned pointer or pitch";
+    case Q3_ERR_MISALIGNED: return "misaligned pointer or stride";
     case Q3_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
     case Q3_ERR_HIP: return "HIP runtime error";
   }
@@ -110,30 +105,28 @@ Q3_API q3_status q3_layout(int64_t n, int64_t k, q3_layout_info* out) {
   out->n = n;
   out->k = k;
   out->groups = k / kGroup;
-  out->chunks = chunks_of(k);
-  out->code_row_bytes = code_row_min(k);
-  out->scale_row_bytes = scale_row_min(k);
-  out->code_plane_bytes = n * out->code_row_bytes;
-  out->scale_plane_bytes = n * out->scale_row_bytes;
+  out->padded_groups = padded_groups(k);
+  out->tiles = tiles_of(n);
+  out->code_tile_bytes = 192 * out->padded_groups;
+  out->scale_tile_bytes = 16 * out->padded_groups;
+  out->code_plane_bytes = code_plane_bytes(n, k);
+  out->scale_plane_bytes = scale_plane_bytes(n, k);
   out->codebook_bytes = 8 * n;
   out->payload_bytes = n * (k / kGroup) * 13;
   return Q3_OK;
 }
 
 Q3_API q3_status q3_pack(const uint8_t* codes, int64_t ldc, const uint8_t* scale_bytes, int64_t lds, int64_t n,
-                         int64_t k, void* code_plane, int64_t code_row_bytes, void* scale_plane,
-                         int64_t scale_row_bytes, void* stream) {
+                         int64_t k, void* code_plane, void* scale_plane, void* stream) {
   q3_status st = check_shape(n, k);
   if (st != Q3_OK) return st;
   if (n > 0 && (!codes || !scale_bytes || !code_plane || !scale_plane)) return Q3_ERR_INVALID_ARG;
   if (ldc < k || lds < k / kGroup) return Q3_ERR_INVALID_ARG;
-  if (code_row_bytes < code_row_min(k) || scale_row_bytes < scale_row_min(k)) return Q3_ERR_INVALID_ARG;
-  if (code_row_bytes % 16 || scale_row_bytes % 4 || !aligned(code_plane, 16) || !aligned(scale_plane, 4))
-    return Q3_ERR_MISALIGNED;
+  if (!aligned(code_plane, 16) || !aligned(scale_plane, 4)) return Q3_ERR_MISALIGNED;
+  if (code_plane_bytes(n, k) > kMaxPlaneBytes) return Q3_ERR_UNSUPPORTED_SHAPE;
   if ((st = check_device()) != Q3_OK) return st;
   return from_hip(q3::launch_pack(codes, ldc, scale_bytes, lds, n, k, static_cast<uint8_t*>(code_plane),
-                                  code_row_bytes, static_cast<uint8_t*>(scale_plane), scale_row_bytes,
-                                  static_cast<hipStream_t>(stream)));
+                                  static_cast<uint8_t*>(scale_plane), static_cast<hipStream_t>(stream)));
 }
 
 Q3_API q3_status q3_unpack(const q3_matrix* w, uint8_t* codes_out, uint8_t* scale_out, void* stream) {
@@ -179,10 +172,10 @@ Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t
                                         float* y, int64_t ldy, void* stream) {
   if (!w) return Q3_ERR_INVALID_ARG;
   if (w->num_experts < 1 || w->num_experts > 65535) return Q3_ERR_UNSUPPORTED_SHAPE;
-  q3_status st = check_planes(w->n, w->k, w->code_plane, w->code_row_bytes, w->scale_plane, w->scale_row_bytes,
-                              w->codebook);
+  q3_status st = check_planes(w->n, w->k, w->code_plane, w->scale_plane, w->codebook);
   if (st != Q3_OK) return st;
-  if (w->code_expert_stride < 0 || w->scale_expert_stride < 0 || w->codebook_expert_stride < 0)
+  if (w->code_expert_stride < code_plane_bytes(w->n, w->k) || w->scale_expert_stride < scale_plane_bytes(w->n, w->k) ||
+      w->codebook_expert_stride < 8 * w->n)
     return Q3_ERR_INVALID_ARG;
   if (w->code_expert_stride % 16 || w->scale_expert_stride % 4 || w->codebook_expert_stride % 8)
     return Q3_ERR_MISALIGNED;
@@ -194,9 +187,7 @@ Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t
   if ((st = check_device()) != Q3_OK) return st;
   q3::ExpertView v;
   v.base.code = static_cast<const uint8_t*>(w->code_plane);
-  v.base.code_pitch = w->code_row_bytes;
   v.base.scale = static_cast<const uint8_t*>(w->scale_plane);
-  v.base.scale_pitch = w->scale_row_bytes;
   v.base.cb = static_cast<const uint8_t*>(w->codebook);
   v.base.n = w->n;
   v.base.groups = static_cast<int32_t>(w->k / kGroup);

@@ -73,26 +73,32 @@ __device__ __forceinline__ void dequant_group_bf16(uint32_t d0, uint32_t d1, uin
 
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
 
-// Where word j of group g sits inside a row.  Groups (padded to gp, a multiple
-// of 4) are stored in superchunks of 16; inside a superchunk of p groups the
-// three words are word-major: word j of its group t is at 4*(p*j + t).  A
-// 16-byte load then carries one word of 4 consecutive groups, and the four
-// such loads of a superchunk word are one contiguous 64-byte run.
-__device__ __forceinline__ uint32_t superchunk_groups(uint32_t s, uint32_t gp) {
+// Tile-major placement of the planes (rows in tiles of 16, a row's groups in
+// steps of 16): the code-plane byte of word j of group g of row r and the
+// scale-plane byte of the scale of (r, g), for gp padded groups per row.  A
+// step holds q = min(16, gp - 16s)/4 quads of 4 groups; inside it, 16-byte
+// piece 16*(q*j + kb) + i holds word j of quad kb of the tile's row i.
+__device__ __forceinline__ uint32_t step_quads(uint32_t s, uint32_t gp) {
   const uint32_t rest = gp - 16u * s;
-  return rest < 16u ? rest : 16u;
+  return (rest < 16u ? rest : 16u) / 4u;
 }
-__device__ __forceinline__ uint32_t word_offset(uint32_t g, uint32_t j, uint32_t gp) {
-  const uint32_t s = g >> 4, t = g & 15u;
-  return 192u * s + 4u * (superchunk_groups(s, gp) * j + t);
+__device__ __forceinline__ int64_t code_word_offset(int64_t r, uint32_t g, uint32_t j, uint32_t gp) {
+  const uint32_t i = (uint32_t)(r & 15), s = g >> 4, kb = (g >> 2) & 3u, t = g & 3u;
+  const uint32_t q = step_quads(s, gp);
+  return (r >> 4) * (int64_t)(192u * gp) + 3072u * s + 16u * (16u * (q * j + kb) + i) + 4u * t;
+}
+__device__ __forceinline__ int64_t scale_byte_offset(int64_t r, uint32_t g, uint32_t gp) {
+  const uint32_t i = (uint32_t)(r & 15), s = g >> 4, kb = (g >> 2) & 3u, t = g & 3u;
+  return (r >> 4) * (int64_t)(16u * gp) + 256u * s + 4u * (16u * kb + i) + t;
 }
 
 // Raw buffer resources: loads whose byte offset lies past num_records return
 // zero, which the kernels use instead of branches around out-of-range rows,
 // groups and tokens.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
-// An offset past every buffer: planes are kept below 2 GiB, so kOob plus any
-// in-kernel step advance stays out of range without wrapping.
+// An offset past every buffer: planes are kept below 2 GiB - 16 MiB, so kOob
+// plus any in-kernel advance inside one tile stays out of range without
+// wrapping.
 constexpr uint32_t kOob = 0x80000000u;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {

@@ -8,18 +8,15 @@
 namespace q3 {
 
 struct PlaneView {
-  const uint8_t* code;    // code plane, 16-byte aligned
-  int64_t code_pitch;     // bytes, multiple of 16
-  const uint8_t* scale;   // scale plane, 4-byte aligned
-  int64_t scale_pitch;    // bytes, multiple of 4
+  const uint8_t* code;    // code plane (tile-major, 192*Gp bytes per 16-row tile), 16-byte aligned
+  const uint8_t* scale;   // scale plane (tile-major, 16*Gp bytes per tile), 4-byte aligned
   const uint8_t* cb;      // codebook [n][8], 8-byte aligned
   int64_t n;
   int32_t groups;         // k / 32
 };
 
 hipError_t launch_pack(const uint8_t* codes, int64_t ldc, const uint8_t* scales, int64_t lds, int64_t n,
-                       int64_t k, uint8_t* code_plane, int64_t code_pitch, uint8_t* scale_plane,
-                       int64_t scale_pitch, hipStream_t s);
+                       int64_t k, uint8_t* code_plane, uint8_t* scale_plane, hipStream_t s);
 hipError_t launch_unpack(const PlaneView& w, uint8_t* codes, uint8_t* scales, hipStream_t s);
 
 // VALU path, 1 <= m <= 8.

@@ -1,0 +1,721 @@
+// Decode / verify products over the 3.25-bit codebook format: dense on the
+// matrix cores (1..64 tokens), dense on the vector ALUs (1..8 tokens), and
+// expert-grouped on the matrix cores (MoE verify rounds).
+//
+// What it computes (Hibana: Fast Agentic Inference on Unified-Memory Devices,
+// "Model surgery" / "Three-bit weights"): y[m][n] = sum_k x[m][k] * w[n][k] with
+// w = E4M3FN(codebook[n][code]) * 2^(scale - 127).  The page's own kernel looks
+// the codes up and feeds the FP8 matrix units; here the looked-up E4M3 bytes are
+// widened exactly to bf16 (group scale folded into the conversion), so every
+// product is exact and only the fp32 accumulation rounds, whatever the
+// activations are.
+//
+// Work unit: a step = one 16-row tile x 512 k (16 groups per row).  The planes
+// are tile-major, so a step's code words are one contiguous 3 KB block (three
+// 1 KB runs, one per word index) and its scales one 256-byte run; lane l of a
+// wave serves row l%16 and groups 4*(l/16)..+3 of the step and reads its three
+// words and four scale bytes with one 16-byte and one 4-byte buffer load per
+// run, so every load instruction of the wave covers one contiguous span.  Each
+// group is dequantised once into 16 bf16 pairs:
+//   * matrix-core mode: the pairs are the A operands of 4 MFMAs
+//     (v_mfma_f32_16x16x32_bf16) per column tile of 16 tokens; the B operand of
+//     the same lane is the matching 8 activations of token 16c + l%16, read from
+//     LDS once per step and used by all R row tiles of the wave, so A and B
+//     agree on which k sits in which slot by construction;
+//   * vector-ALU mode: the pairs meet the activations (read from LDS, the same
+//     address for the 16 lanes of a quad) in v_dot2_f32_bf16, one fp32 partial
+//     per lane, row and token; the four quads of a row are summed with lane
+//     shuffles at the end.
+//
+// Activations are staged in LDS once per block ("full-K" mode) or, when they do
+// not fit, one 512-k step at a time into a double buffer ("stream" mode).  The
+// next step's code words and scales are loaded before the current step is
+// computed; all loads are buffer loads whose out-of-range offsets read as zero,
+// so rows past n, padding groups and absent tokens need no branches.  In full-K
+// mode the waves of a block may split K (few rows); partial sums are then
+// added through LDS in a fixed order, so results are run-to-run identical.
+//
+// The grouped variant runs one grid row per expert.  Its block first collects
+// the (token, slot) pairs routed to that expert; an expert nobody picked
+// returns before reading any weight byte (Hibana page, "Adaptive speculation" /
+// "Expert sharing": a verify round reads every picked expert once).
+#include <atomic>
+
+#include "q3_device.h"
+#include "q3_internal.h"
+
+namespace q3 {
+namespace {
+
+constexpr int kFullKBudget = 96 * 1024;   // LDS bytes for full-K activation staging
+constexpr uint32_t kRowPad = 16;          // LDS row padding against bank conflicts
+
+struct KArgs {
+  const uint8_t* code;
+  int64_t code_stride;    // bytes between experts
+  const uint8_t* scale;
+  int64_t scale_stride;
+  const uint8_t* cb;
+  int64_t cb_stride;
+  int64_t n;
+  int G;
+  const uint16_t* x;
+  int64_t ldx;
+  int64_t x_rows;   // rows of x that may be read
+  float* y;
+  int64_t ldy;
+  int m;          // dense: number of tokens
+  int sk;         // K split over the waves of a block (full-K mode)
+  const int32_t* ids;
+  int pairs_total, topk, x_by_slot;
+};
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
+  u32x4 u = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+             __builtin_bit_cast(uint32_t, d)};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Wave-uniform geometry of one matrix's planes.
+struct Planes {
+  rsrc_t code, scale;
+  int full_steps, steps;
+  uint32_t q_last;   // quads of groups in the last step (1..4)
+};
+
+// Per-lane view of one row tile: byte offsets of the lane's piece in step 0
+// (kOob for tiles past the plane); a step adds a wave-uniform amount that
+// stays inside the tile.
+struct RowTile {
+  uint32_t vcode;     // tile*192*Gp + 16*lane
+  uint32_t vscale;    // tile*16*Gp + 4*lane
+  uint32_t cbl, cbh;  // the lane's row codebook (zero past n)
+};
+
+// Code words and scales of one step of R row tiles, for one lane.
+template <int R>
+struct StepData {
+  u32x4 w[R][3];   // w[r][j][t] = word j of the lane's group t in row tile r
+  uint32_t sc[R];  // byte t = scale of group t
+};
+
+// Branch-free on purpose: loads issued under a condition make the wait-count
+// insertion assume the worst case and drain every outstanding prefetch.  Steps
+// at or past s_end re-read step s_end-1 (cached, never computed).  On a partial
+// last step, lanes past its quads (last_ok false) read zeros for both codes
+// and scales; a zero scale byte widens to a zero fp32 scale, so those lanes
+// contribute exactly zero whatever activations they meet.
+template <int R>
+__device__ __forceinline__ void load_step(const Planes& p, const RowTile (&rt)[R], bool last_ok, int s, int s_end,
+                                          StepData<R>& d) {
+  const int sc = s < s_end ? s : s_end - 1;
+  const bool full = sc < p.full_steps;
+  const bool live = full || last_ok;
+  const uint32_t js = full ? 1024u : 256u * p.q_last;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t o = (live ? rt[r].vcode : kOob) + 3072u * sc;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) d.w[r][j] = bload128(p.code, o + js * j);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) d.sc[r] = bload32(p.scale, (live ? rt[r].vscale : kOob) + 256u * sc);
+}
+
+__device__ __forceinline__ void dequant(const u32x4 (&w)[3], uint32_t sc, int t, uint32_t cbl, uint32_t cbh,
+                                        bf16x2 (&wv)[16]) {
+  dequant_group_bf16(w[0][t], w[1][t], w[2][t], (sc >> (8 * t)) & 0xFFu, cbl, cbh, wv);
+}
+
+// Matrix-core step: dequantise the step's 4 groups of every row tile and run
+// 4*4*MT*R MFMAs.  xb[c] is the lane's LDS byte address of its B operand for
+// column tile c at this step (group 0, k 0).  With few column tiles the B
+// operands of a group are held while the row tiles are dequantised one by one;
+// with many, the row tiles' A operands are held while the B operands stream.
+template <int MT, int R>
+__device__ __forceinline__ void mfma_step(const StepData<R>& d, const RowTile (&rt)[R], const uint32_t (&xb)[MT],
+                                          const uint8_t* lds, f32x4 (&acc)[R][MT]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if constexpr (MT <= R) {
+      bf16x8 b[4][MT];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int c = 0; c < MT; ++c) b[e][c] = *reinterpret_cast<const bf16x8*>(lds + xb[c] + 64u * t + 16u * e);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        bf16x2 wv[16];
+        dequant(d.w[r], d.sc[r], t, rt[r].cbl, rt[r].cbh, wv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x8 a = pack_bf16x8(wv[4 * e], wv[4 * e + 1], wv[4 * e + 2], wv[4 * e + 3]);
+#pragma unroll
+          for (int c = 0; c < MT; ++c)
+            acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[e][c], acc[r][c], 0, 0, 0);
+        }
+      }
+    } else {
+      bf16x2 wv[R][16];
+#pragma unroll
+      for (int r = 0; r < R; ++r) dequant(d.w[r], d.sc[r], t, rt[r].cbl, rt[r].cbh, wv[r]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int c = 0; c < MT; ++c) {
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(lds + xb[c] + 64u * t + 16u * e);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const bf16x8 a = pack_bf16x8(wv[r][4 * e], wv[r][4 * e + 1], wv[r][4 * e + 2], wv[r][4 * e + 3]);
+            acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[r][c], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < MT; ++c) asm volatile("" : "+v"(acc[r][c]));
+}
+
+// Vector-ALU step for M tokens: xa[m] is the LDS byte address of token m's
+// activations at this step and the lane's quad (group 0, k 0).  The next
+// token's activations are read while the current token's dot products run;
+// the scheduling barriers stop the compiler from hoisting every token's reads
+// to the top (64 registers per token).
+template <int M, int R>
+__device__ __forceinline__ void dot_step(const StepData<R>& d, const RowTile (&rt)[R], const uint32_t (&xa)[M],
+                                         const uint8_t* lds, float (&acc)[R][M]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    bf16x2 wv[R][16];
+#pragma unroll
+    for (int r = 0; r < R; ++r) dequant(d.w[r], d.sc[r], t, rt[r].cbl, rt[r].cbh, wv[r]);
+    u32x4 xv[2][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xv[0][e] = *reinterpret_cast<const u32x4*>(lds + xa[0] + 64u * t + 16u * e);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      if (m + 1 < M) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          xv[(m + 1) & 1][e] = *reinterpret_cast<const u32x4*>(lds + xa[m + 1] + 64u * t + 16u * e);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float a = acc[r][m];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          a = __builtin_amdgcn_fdot2_f32_bf16(wv[r][q], as_bf16x2(xv[m & 1][q >> 2][q & 3]), a, false);
+        acc[r][m] = a;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // Pin the accumulation here: otherwise the compiler may sink the whole
+  // step's arithmetic past the caller's barrier and keep every activation
+  // read so far live (spilled) until then.
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) asm volatile("" : "+v"(acc[r][m]));
+}
+
+// Token slot j of the current slice -> x row and y row.
+struct Tokens {
+  int count;          // tokens in this slice
+  int xrow[64];
+  int yrow[64];
+};
+
+// Copy `count` 16-byte chunks from global memory (buffer resource) into LDS.
+// All loads of a batch are issued before any store, so a batch costs one
+// memory latency instead of one per chunk.  src(c) returns the chunk's byte
+// offset in the resource (kOob for zeros), dst(c) its LDS byte address.
+template <int kBatch, int kThreads, typename Src, typename Dst>
+__device__ __forceinline__ void stage_chunks(rsrc_t r, int count, uint8_t* lds, Src src, Dst dst) {
+  for (int base = threadIdx.x; base < count; base += kBatch * kThreads) {
+    u32x4 v[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int c = base + q * kThreads;
+      v[q] = bload128(r, c < count ? src(c) : kOob);
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int c = base + q * kThreads;
+      if (c < count) *reinterpret_cast<u32x4*>(lds + dst(c)) = v[q];
+    }
+  }
+}
+
+// Waves per SIMD the register budget is held to (128 registers per lane for 4,
+// 256 for 2): a decode launch wants every wave resident at once.
+template <int NT, int R, bool kDot>
+constexpr int min_waves_per_eu() {
+  if (kDot) return R == 1 ? (NT <= 5 ? 4 : 3) : 2;
+  return R == 1 && NT <= 2 ? 4 : 2;
+}
+
+// NT: column tiles of 16 tokens (matrix-core mode) or tokens (vector-ALU mode).
+template <int NT, int R, int kW, bool kGrouped, bool kFullK, bool kDot>
+__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<NT, R, kDot>())))
+void linear_kernel(KArgs a) {
+  constexpr int kThreads = 64 * kW;
+  constexpr int kSlice = kDot ? NT : 16 * NT;   // tokens per slice
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ Tokens tk;
+  __shared__ int pairs[64];
+  __shared__ int npairs;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform from here on
+  const int i = lane & 15;
+  const int kb = lane >> 4;
+  const int sk = kFullK ? a.sk : 1;
+  const int rb = kW / sk;
+  const int rg = wave / sk;
+  const int ks = wave - rg * sk;
+
+  // ---- which expert / tokens -------------------------------------------------
+  int expert = 0;
+  if (kGrouped) {
+    expert = blockIdx.y;
+    if (tid < 64) {
+      const bool match = tid < a.pairs_total && a.ids[tid] == expert;
+      const unsigned long long mask = __ballot(match);
+      if (match) pairs[__popcll(mask & ((1ull << tid) - 1ull))] = tid;
+      if (tid == 0) npairs = __popcll(mask);
+    }
+    __syncthreads();
+    if (npairs == 0) return;   // not picked this round: no weight byte is read
+  }
+  const int total_tokens = kGrouped ? __builtin_amdgcn_readfirstlane(npairs) : a.m;
+
+  const int G = a.G;
+  const uint32_t gp = (uint32_t)((G + 3) & ~3);
+  const int64_t tiles = (a.n + 15) / 16;
+  const int64_t tile0 = ((int64_t)blockIdx.x * rb + rg) * R;   // first row tile of this wave
+
+  Planes p;
+  p.code = make_rsrc(a.code + (int64_t)expert * a.code_stride, (uint32_t)(tiles * 192 * gp));
+  p.scale = make_rsrc(a.scale + (int64_t)expert * a.scale_stride, (uint32_t)(tiles * 16 * gp));
+  p.full_steps = (int)(gp / 16);
+  p.steps = (int)((gp + 15) / 16);
+  p.q_last = (gp - 16u * (uint32_t)(p.steps - 1)) / 4u;
+  const bool last_ok = (uint32_t)kb < p.q_last;   // lane has groups in a partial last step
+  const rsrc_t cbr = make_rsrc(a.cb + (int64_t)expert * a.cb_stride, (uint32_t)(a.n * 8));
+  RowTile rt[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t T = tile0 + r;
+    const bool tile_ok = T < tiles;
+    rt[r].vcode = tile_ok ? (uint32_t)T * (192u * gp) + 16u * lane : kOob;
+    rt[r].vscale = tile_ok ? (uint32_t)T * (16u * gp) + 4u * lane : kOob;
+  }
+
+  const int s0 = kFullK ? (ks * p.steps) / sk : 0;
+  const int s1 = kFullK ? ((ks + 1) * p.steps) / sk : p.steps;
+
+  // The first step's loads go out before anything else.
+  StepData<R> A, B;
+  load_step(p, rt, last_ok, s0, s1, A);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = (tile0 + r) * 16 + i;
+    const u32x2 cb = bload64(cbr, row < a.n ? (uint32_t)row * 8u : kOob);
+    rt[r].cbl = cb.x;
+    rt[r].cbh = cb.y;
+  }
+
+  const rsrc_t xr_rsrc = make_rsrc(a.x, (uint32_t)((a.x_rows - 1) * a.ldx * 2 + (int64_t)G * 64));
+  const uint32_t ldx_bytes = (uint32_t)(a.ldx * 2);
+
+  for (int slice = 0; slice < total_tokens; slice += kSlice) {
+    if (tid == 0) {
+      const int cnt = total_tokens - slice < kSlice ? total_tokens - slice : kSlice;
+      tk.count = cnt;
+      for (int j = 0; j < kSlice; ++j) {
+        if (j < cnt) {
+          if (kGrouped) {
+            const int q = pairs[slice + j];
+            tk.xrow[j] = a.x_by_slot ? q : q / a.topk;
+            tk.yrow[j] = q;
+          } else {
+            tk.xrow[j] = slice + j;
+            tk.yrow[j] = slice + j;
+          }
+        } else {
+          tk.xrow[j] = 0;
+          tk.yrow[j] = 0;
+        }
+      }
+    }
+    __syncthreads();
+    const int cnt = __builtin_amdgcn_readfirstlane(tk.count);
+    if (slice > 0) load_step(p, rt, last_ok, s0, s1, A);
+
+    f32x4 acc[R][kDot ? 1 : NT];
+    float dacc[R][kDot ? NT : 1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int c = 0; c < (kDot ? 1 : NT); ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < (kDot ? NT : 1); ++c) dacc[r][c] = 0.f;
+    }
+    // Lane addresses of token slots at the step's start in a row-per-token x
+    // layout of the given row stride, for buffer base `base` (absent tokens of
+    // matrix-core mode go to `zero`, a 1 KB zero block, and stay there).
+    auto run = [&](const StepData<R>& d, uint32_t base, uint32_t rstride, uint32_t zero, uint32_t adv) {
+      if constexpr (kDot) {
+        uint32_t xa[NT];
+#pragma unroll
+        for (int m = 0; m < NT; ++m) xa[m] = (m < cnt ? base + m * rstride + adv : zero) + 256u * kb;
+        dot_step<NT, R>(d, rt, xa, lds, dacc);
+      } else {
+        uint32_t xb[NT];
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          const int j = 16 * c + i;
+          xb[c] = (j < cnt ? base + j * rstride + adv : zero) + 256u * kb;
+        }
+        mfma_step<NT, R>(d, rt, xb, lds, acc);
+      }
+    };
+
+    if (kFullK) {
+      // Stage all activations: row j holds token j's K values (zero past K,
+      // including the row's 16-byte pad, which lanes past a partial last
+      // step's quads read with a zero scale); a 1 KB zero block follows.
+      const uint32_t rstride = gp * 64u + kRowPad;
+      const uint32_t zero_base = (uint32_t)cnt * rstride;
+      const int cpr = (int)(rstride / 16);
+      stage_chunks<8, kThreads>(xr_rsrc, cnt * cpr + 64, lds,
+                                [&](int c) {
+                                  const int j = c / cpr, q = c - j * cpr;
+                                  return j < cnt && q * 8 < G * 32 ? (uint32_t)tk.xrow[j] * ldx_bytes + 16u * q
+                                                                   : kOob;
+                                },
+                                [&](int c) { return 16u * c; });   // rows are contiguous, then the zero block
+      __syncthreads();
+      // One step is in flight while another is computed.  The scheduling
+      // barriers keep each refill where it is issued; without them the
+      // compiler sinks the loads below the MFMAs or hoists the refill above
+      // the computation that still reads the registers.
+      for (int s = s0; s < s1; s += 2) {
+        load_step(p, rt, last_ok, s + 1, s1, B);
+        __builtin_amdgcn_sched_barrier(0);
+        run(A, 0u, rstride, zero_base, 1024u * s);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 >= s1) break;
+        load_step(p, rt, last_ok, s + 2, s1, A);
+        __builtin_amdgcn_sched_barrier(0);
+        run(B, 0u, rstride, zero_base, 1024u * (s + 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // Stream the activations one 512-k step at a time through two buffers of
+      // kSlice rows (rows of absent tokens stay zero) followed by a 1 KB zero
+      // block.  Step s+1's activations are fetched into registers before step s
+      // is computed and stored to LDS after it, into the buffer step s-1 used.
+      constexpr int kChunks = (kSlice * 64 + kThreads - 1) / kThreads;   // per thread
+      const uint32_t rstride = 1024u + kRowPad;
+      const uint32_t buf_bytes = (uint32_t)kSlice * rstride;
+      const uint32_t zero_base = 2u * buf_bytes;
+      const int nchunk = kSlice * 64;   // 16-byte chunks per buffer
+      auto fetch = [&](int s, u32x4 (&r)[kChunks]) {
+#pragma unroll
+        for (int q = 0; q < kChunks; ++q) {
+          const int idx = tid + q * kThreads;
+          const int j = idx >> 6, c16 = idx & 63;
+          const int k0 = s * 512 + c16 * 8;
+          const bool ok = idx < nchunk && j < cnt && s < p.steps && k0 < G * 32;
+          r[q] = bload128(xr_rsrc, ok ? (uint32_t)tk.xrow[j] * ldx_bytes + 2u * k0 : kOob);
+        }
+      };
+      auto put = [&](int buf, const u32x4 (&r)[kChunks]) {
+#pragma unroll
+        for (int q = 0; q < kChunks; ++q) {
+          const int idx = tid + q * kThreads;
+          const int j = idx >> 6, c16 = idx & 63;
+          if (idx < nchunk) *reinterpret_cast<u32x4*>(lds + buf * buf_bytes + j * rstride + 16u * c16) = r[q];
+        }
+      };
+      if (tid < 64) *reinterpret_cast<u32x4*>(lds + zero_base + 16u * tid) = u32x4{0u, 0u, 0u, 0u};
+      u32x4 xr[kChunks];
+      fetch(0, xr);
+      put(0, xr);
+      __syncthreads();
+      for (int s = 0; s < s1; s += 2) {
+        load_step(p, rt, last_ok, s + 1, s1, B);
+        fetch(s + 1, xr);
+        __builtin_amdgcn_sched_barrier(0);
+        run(A, 0u, rstride, zero_base, 0u);
+        __builtin_amdgcn_sched_barrier(0);
+        put(1, xr);   // buffer 1 was last read at step s-1
+        __syncthreads();
+        if (s + 1 >= s1) break;
+        load_step(p, rt, last_ok, s + 2, s1, A);
+        fetch(s + 2, xr);
+        __builtin_amdgcn_sched_barrier(0);
+        run(B, buf_bytes, rstride, zero_base, 0u);
+        __builtin_amdgcn_sched_barrier(0);
+        put(0, xr);
+        __syncthreads();
+      }
+    }
+
+    // ---- combine K splits and store --------------------------------------------
+    if constexpr (kDot) {
+      // The four quads of a row sit in lanes i, i+16, i+32, i+48.
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < NT; ++m) {
+          float v = dacc[r][m];
+          v += __shfl_xor(v, 16, 64);
+          v += __shfl_xor(v, 32, 64);
+          dacc[r][m] = v;
+        }
+    }
+    if (kFullK && sk > 1) {
+      __syncthreads();   // activations no longer needed: reuse LDS for partial sums
+      constexpr int kVals = kDot ? NT : 4 * NT;   // floats per lane and row tile
+      float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int v = 0; v < kVals; ++v)
+          red[((wave * R + r) * kVals + v) * 64 + lane] = kDot ? dacc[r][v] : acc[r][v / 4][v % 4];
+      __syncthreads();
+      if (ks == 0) {
+        for (int q = 1; q < sk; ++q) {
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int v = 0; v < kVals; ++v) {
+              const float o = red[(((wave + q) * R + r) * kVals + v) * 64 + lane];
+              if constexpr (kDot) dacc[r][v] += o;
+              else acc[r][v / 4][v % 4] += o;
+            }
+        }
+      }
+    }
+    if (ks == 0) {
+      if constexpr (kDot) {
+        if (kb == 0) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const int64_t row = (tile0 + r) * 16 + i;
+            if (row < a.n) {
+#pragma unroll
+              for (int m = 0; m < NT; ++m)
+                if (m < cnt) a.y[(int64_t)tk.yrow[m] * a.ldy + row] = dacc[r][m];
+            }
+          }
+        }
+      } else {
+        // D layout: lane l holds rows 4*(l/16)+v (v = 0..3) of the tile for token l%16.
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          const int j = 16 * c + i;
+          if (j < cnt) {
+            float* yr = a.y + (int64_t)tk.yrow[j] * a.ldy;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const int64_t row = (tile0 + r) * 16 + 4 * kb + v;
+                if (row < a.n) yr[row] = acc[r][c][v];
+              }
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();   // token table and LDS are rewritten by the next slice
+  }
+}
+
+// ---- host side ------------------------------------------------------------------
+
+size_t full_k_bytes(int tokens, int groups) {
+  const size_t gp = (size_t)((groups + 3) & ~3);
+  return (size_t)tokens * (gp * 64 + kRowPad) + 1024;
+}
+
+size_t stream_bytes(int slice) { return 2u * slice * (1024u + kRowPad) + 1024u; }
+
+size_t reduce_bytes(int vals, int r, int w) { return (size_t)w * r * vals * 64 * 4; }
+
+// Dynamic LDS above 64 KB must be allowed per kernel; raise each kernel's limit
+// once to the largest size this file ever requests.
+template <int NT, int R, int kW, bool kGrouped, bool kFullK, bool kDot>
+hipError_t allow_lds(size_t bytes) {
+  static std::atomic<size_t> allowed{64 * 1024};   // per kernel instantiation
+  if (bytes <= allowed.load(std::memory_order_acquire)) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(linear_kernel<NT, R, kW, kGrouped, kFullK, kDot>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) {
+    size_t cur = allowed.load(std::memory_order_acquire);
+    while (cur < bytes && !allowed.compare_exchange_weak(cur, bytes)) {
+    }
+  }
+  return e;
+}
+
+template <int NT, int R, int kW, bool kGrouped, bool kFullK, bool kDot>
+hipError_t launch_one(const KArgs& a, size_t shm, unsigned grid_y, hipStream_t s) {
+  const int rb = kW / (kFullK ? a.sk : 1);
+  const int64_t tiles = (a.n + 15) / 16;
+  const int64_t groups = (tiles + R - 1) / R;   // row groups of R tiles
+  const dim3 grid((unsigned)((groups + rb - 1) / rb), grid_y);
+  hipError_t e = allow_lds<NT, R, kW, kGrouped, kFullK, kDot>(shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((linear_kernel<NT, R, kW, kGrouped, kFullK, kDot>), grid, dim3(64 * kW), shm, s, a);
+  return hipGetLastError();
+}
+
+// Launch shape: R row tiles per wave, W waves per block, K split sk (full-K
+// only).  Chosen so a launch has about two to four resident waves per SIMD
+// (1024 SIMDs on the chip) without leaving CUs idle: small matrices split K
+// across a block's waves, tall ones give each wave more rows so the B
+// operands of a step serve them all.
+struct Shape {
+  int r, w, sk;
+};
+
+constexpr int kCUs = 256;
+
+Shape pick_shape(int64_t n, int groups, bool full_k, int nt, bool dot) {
+  const int64_t tiles = (n + 15) / 16;
+  const int steps = (((groups + 3) & ~3) + 15) / 16;
+#if defined(Q3_FORCE_R) && defined(Q3_FORCE_W) && defined(Q3_FORCE_SK)
+  (void)tiles;
+  (void)steps;
+  (void)nt;
+  (void)dot;
+  return Shape{Q3_FORCE_R, Q3_FORCE_W, full_k ? Q3_FORCE_SK : 1};
+#else
+  (void)dot;
+  if (!full_k) return Shape{1, 8, 1};   // stream mode: every wave walks all of K
+  // Full-K: split K until there are about 2048 waves.
+  int sk = 1;
+  while (sk < 8 && sk * 2 <= steps && tiles * sk < 2048) sk *= 2;
+  return Shape{1, sk > 4 ? 8 : 4, sk};
+#endif
+}
+
+template <int NT, int R, bool kGrouped, bool kDot>
+hipError_t launch_r(KArgs a, int w, bool full_k, size_t shm, unsigned grid_y, hipStream_t s) {
+  if (full_k) {
+    if (w == 8) return launch_one<NT, R, 8, kGrouped, true, kDot>(a, shm, grid_y, s);
+    return launch_one<NT, R, 4, kGrouped, true, kDot>(a, shm, grid_y, s);
+  }
+  if (w == 8) return launch_one<NT, R, 8, kGrouped, false, kDot>(a, shm, grid_y, s);
+  return launch_one<NT, R, 4, kGrouped, false, kDot>(a, shm, grid_y, s);
+}
+
+// tokens_in_slice: tokens the LDS staging holds at once.
+template <int NT, bool kGrouped, bool kDot>
+hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t s) {
+  constexpr int kSlice = kDot ? NT : 16 * NT;
+  const size_t fk = full_k_bytes(tokens_in_slice, a.G);
+  const bool full_k = fk <= (size_t)kFullKBudget;
+  const Shape sh = kGrouped ? Shape{1, 4, 1} : pick_shape(a.n, a.G, full_k, NT, kDot);
+  a.sk = full_k ? sh.sk : 1;
+  const int steps = (((a.G + 3) & ~3) + 15) / 16;
+  while (a.sk > 1 && a.sk > steps) a.sk /= 2;   // every wave gets at least one step
+  if (a.sk < 1 || a.sk > sh.w || sh.w % a.sk != 0) return hipErrorInvalidValue;
+  size_t shm = full_k ? fk : stream_bytes(kSlice);
+  if (full_k && a.sk > 1) {
+    const size_t red = reduce_bytes(kDot ? NT : 4 * NT, sh.r, sh.w);
+    if (shm < red) shm = red;
+  }
+  if constexpr (kGrouped || kDot) {
+    return launch_r<NT, 1, kGrouped, kDot>(a, sh.w, full_k, shm, grid_y, s);
+  } else {
+    switch (sh.r) {
+      case 1: return launch_r<NT, 1, kGrouped, kDot>(a, sh.w, full_k, shm, grid_y, s);
+      case 2: return launch_r<NT, 2, kGrouped, kDot>(a, sh.w, full_k, shm, grid_y, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+}
+
+KArgs base_args(const PlaneView& w) {
+  KArgs a{};
+  a.code = w.code;
+  a.scale = w.scale;
+  a.cb = w.cb;
+  a.n = w.n;
+  a.G = w.groups;
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_small_m(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y,
+                               int64_t ldy, hipStream_t s) {
+  if (w.n == 0) return hipSuccess;
+  KArgs a = base_args(w);
+  a.x = x;
+  a.ldx = ldx;
+  a.y = y;
+  a.ldy = ldy;
+  a.m = (int)m;
+  a.x_rows = m;
+  if (m <= 16) return launch_cfg<1, false, false>(a, (int)m, 1, s);
+  if (m <= 32) return launch_cfg<2, false, false>(a, (int)m, 1, s);
+  if (m <= 48) return launch_cfg<3, false, false>(a, (int)m, 1, s);
+  return launch_cfg<4, false, false>(a, (int)m, 1, s);
+}
+
+hipError_t launch_gemv(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
+                       hipStream_t s) {
+  if (w.n == 0) return hipSuccess;
+  KArgs a = base_args(w);
+  a.x = x;
+  a.ldx = ldx;
+  a.y = y;
+  a.ldy = ldy;
+  a.m = (int)m;
+  a.x_rows = m;
+  switch (m) {
+    case 1: return launch_cfg<1, false, true>(a, 1, 1, s);
+    case 2: return launch_cfg<2, false, true>(a, 2, 1, s);
+    case 3: return launch_cfg<3, false, true>(a, 3, 1, s);
+    case 4: return launch_cfg<4, false, true>(a, 4, 1, s);
+    case 5: return launch_cfg<5, false, true>(a, 5, 1, s);
+    case 6: return launch_cfg<6, false, true>(a, 6, 1, s);
+    case 7: return launch_cfg<7, false, true>(a, 7, 1, s);
+    case 8: return launch_cfg<8, false, true>(a, 8, 1, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_grouped(const ExpertView& w, const uint16_t* x, int64_t ldx, int32_t x_by_slot,
+                          const int32_t* ids, int32_t t, int32_t topk, float* y, int64_t ldy, hipStream_t s) {
+  if (w.base.n == 0) return hipSuccess;
+  KArgs a = base_args(w.base);
+  a.code_stride = w.code_stride;
+  a.scale_stride = w.scale_stride;
+  a.cb_stride = w.cb_stride;
+  a.x = x;
+  a.ldx = ldx;
+  a.y = y;
+  a.ldy = ldy;
+  a.ids = ids;
+  a.pairs_total = t * topk;
+  a.topk = topk;
+  a.x_by_slot = x_by_slot;
+  a.x_rows = x_by_slot ? (int64_t)t * topk : t;
+  const int slice = a.pairs_total < 16 ? a.pairs_total : 16;
+  return launch_cfg<1, true, false>(a, slice, (unsigned)w.num_experts, s);
+}
+
+}  // namespace q3

@@ -8,14 +8,18 @@
 namespace q3 {
 namespace {
 
-__global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* __restrict__ codes, int64_t ldc,
-                                                         int64_t n, int64_t groups, int64_t padded_groups,
-                                                         uint8_t* __restrict__ plane, int64_t pitch) {
+// One thread per (row, group) of the padded tiles: every byte of both planes is
+// written exactly once, padding rows and groups as zero.
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ codes, int64_t ldc,
+                                                   const uint8_t* __restrict__ scales, int64_t lds, int64_t n,
+                                                   int64_t groups, int64_t padded_groups, int64_t padded_rows,
+                                                   uint8_t* __restrict__ code_plane, uint8_t* __restrict__ scale_plane) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n * padded_groups) return;
+  if (idx >= padded_rows * padded_groups) return;
   const int64_t r = idx / padded_groups, g = idx % padded_groups;
+  const bool real = r < n && g < groups;
   uint32_t w[3] = {0u, 0u, 0u};
-  if (g < groups) {
+  if (real) {
     const uint8_t* c = codes + r * ldc + (int64_t)kGroup * g;
     uint32_t v[32];
 #pragma unroll
@@ -30,19 +34,11 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* __restri
       }
     }
   }
-  uint8_t* row = plane + r * pitch;
+  const uint32_t gp = (uint32_t)padded_groups;
 #pragma unroll
   for (int j = 0; j < 3; ++j)
-    *reinterpret_cast<uint32_t*>(row + word_offset((uint32_t)g, (uint32_t)j, (uint32_t)padded_groups)) = w[j];
-}
-
-__global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restrict__ scales, int64_t lds,
-                                                          int64_t n, int64_t groups, int64_t row_bytes,
-                                                          uint8_t* __restrict__ plane, int64_t pitch) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n * row_bytes) return;
-  const int64_t r = idx / row_bytes, g = idx % row_bytes;
-  plane[r * pitch + g] = g < groups ? scales[r * lds + g] : (uint8_t)0;
+    *reinterpret_cast<uint32_t*>(code_plane + code_word_offset(r, (uint32_t)g, (uint32_t)j, gp)) = w[j];
+  scale_plane[scale_byte_offset(r, (uint32_t)g, gp)] = real ? scales[r * lds + g] : (uint8_t)0;
 }
 
 __global__ __launch_bounds__(256) void unpack_kernel(PlaneView w, uint8_t* __restrict__ codes,
@@ -51,17 +47,17 @@ __global__ __launch_bounds__(256) void unpack_kernel(PlaneView w, uint8_t* __res
   const int64_t G = w.groups;
   if (idx >= w.n * G) return;
   const int64_t r = idx / G, g = idx % G;
-  const uint8_t* row = w.code + r * w.code_pitch;
   const uint32_t gp = ((uint32_t)G + 3u) & ~3u;
   uint32_t d[3];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) d[j] = *reinterpret_cast<const uint32_t*>(row + word_offset((uint32_t)g, j, gp));
+  for (int j = 0; j < 3; ++j)
+    d[j] = *reinterpret_cast<const uint32_t*>(w.code + code_word_offset(r, (uint32_t)g, (uint32_t)j, gp));
   uint32_t sel[8];
   unpack_selectors(d[0], d[1], d[2], sel);
   uint32_t* out = reinterpret_cast<uint32_t*>(codes + r * G * kGroup + g * kGroup);
 #pragma unroll
   for (int i = 0; i < 8; ++i) out[i] = sel[i];   // selector bytes are the codes in K order
-  scales[r * G + g] = w.scale[r * w.scale_pitch + g];
+  scales[r * G + g] = w.scale[scale_byte_offset(r, (uint32_t)g, gp)];
 }
 
 inline unsigned blocks_for(int64_t items) { return (unsigned)((items + 255) / 256); }
@@ -69,19 +65,13 @@ inline unsigned blocks_for(int64_t items) { return (unsigned)((items + 255) / 25
 }  // namespace
 
 hipError_t launch_pack(const uint8_t* codes, int64_t ldc, const uint8_t* scales, int64_t lds, int64_t n,
-                       int64_t k, uint8_t* code_plane, int64_t code_pitch, uint8_t* scale_plane,
-                       int64_t scale_pitch, hipStream_t s) {
+                       int64_t k, uint8_t* code_plane, uint8_t* scale_plane, hipStream_t s) {
   const int64_t groups = k / kGroup;
-  const int64_t chunks = (k + 127) / 128;
-  const int64_t padded = chunks * 4;
-  const int64_t scale_row = (padded + 15) / 16 * 16;
+  const int64_t padded = (groups + 3) / 4 * 4;
+  const int64_t padded_rows = (n + 15) / 16 * 16;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(pack_codes_kernel, dim3(blocks_for(n * padded)), dim3(256), 0, s, codes, ldc, n, groups,
-                     padded, code_plane, code_pitch);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pack_scales_kernel, dim3(blocks_for(n * scale_row)), dim3(256), 0, s, scales, lds, n,
-                     groups, scale_row, scale_plane, scale_pitch);
+  hipLaunchKernelGGL(pack_kernel, dim3(blocks_for(padded_rows * padded)), dim3(256), 0, s, codes, ldc, scales,
+                     lds, n, groups, padded, padded_rows, code_plane, scale_plane);
   return hipGetLastError();
 }
 

@@ -14,19 +14,24 @@
  * Readings of the page used here: one codebook per output row (8 bytes, outside
  * the 3.25 bits/weight count); FP8 = OCP E4M3FN; scale = OCP-MX E8M0.
  *
- * ---- Packed format (all planes are row-major, one row per output n) ----------
- *   groups G = k/32, chunks C = ceil(k/128) (a chunk is 4 groups)
- *   code plane : uint32 words, row pitch code_row_bytes >= 48*C (multiple of 16).
- *                A group's 96 code bits are 3 words.  Byte b (0..3) of word j
- *                (0..2) of a group with codes c[0..31]:
+ * ---- Packed format ------------------------------------------------------------
+ *   groups G = k/32, padded to Gp = 4*ceil(k/128) (padding groups are zero);
+ *   rows padded to a multiple of 16 (padding rows are zero).  Both planes are
+ *   cut into tiles of 16 rows stored one after the other; inside a tile a row's
+ *   groups form steps of 16 groups (512 weights); the last step holds
+ *   p = 4, 8, 12 or 16 groups, i.e. q = p/4 quads of 4 groups.
+ *   Row r is row i = r%16 of tile T = r/16; group g is slot t = g%4 of quad
+ *   kb = (g%16)/4 of step s = g/16.
+ *   code plane : a group's 96 code bits are 3 little-endian words.  Byte b
+ *                (0..3) of word j (0..2) of a group with codes c[0..31]:
  *                  bits 0..2 = c[8j+b], bits 3..5 = c[8j+4+b],
  *                  bits 6..7 = bits 2j..2j+1 of (c[24+b] | c[28+b] << 3).
- *                Placement: the row's Gp = 4*C groups form superchunks of 16
- *                groups (192 bytes; the last holds p = 4, 8, 12 or 16), and in
- *                a superchunk of p groups word j of its group t sits at byte
- *                192*s + 4*(p*j + t).  Groups past G are zero padding.
- *   scale plane: uint8, row pitch scale_row_bytes >= round_up(4*C, 16); byte g
- *                of row n is the E8M0 scale of group g; padding is zero.
+ *                Word j of (r, g) sits at byte
+ *                  T*192*Gp + 3072*s + 16*(16*(q*j + kb) + i) + 4*t,
+ *                so a tile is 192*Gp bytes, a full step 3072, and word j of a
+ *                step is one contiguous run over (quad, row) in 16-byte pieces.
+ *   scale plane: one E8M0 byte per group; the scale of (r, g) sits at byte
+ *                  T*16*Gp + 256*s + 4*(16*kb + i) + t.
  *   codebook   : uint8 [n][8], E4M3FN bytes, entry j is what code j selects.
  *   x          : bf16 bit patterns, [m][ldx] (ldx >= k elements).
  *   y          : fp32, [m][ldy] (ldy >= n elements).
@@ -41,10 +46,12 @@
  *     once-per-device capability check.
  *   * Arguments are validated on the host before any HIP call; a rejected call
  *     launches nothing.  Launch failures are reported as Q3_ERR_HIP.
- *   * Size limits: each plane (n * pitch bytes) and the activation block
+ *   * Size limits: each plane (q3_layout's plane bytes) and the activation block
  *     ((m-1)*ldx*2 + k*2 bytes) must stay below 2 GiB - 16 MiB
- *     (Q3_ERR_UNSUPPORTED_SHAPE otherwise); x needs ldx % 8 == 0 and 16-byte
- *     alignment, y 4-byte alignment (Q3_ERR_MISALIGNED).
+ *     (Q3_ERR_UNSUPPORTED_SHAPE otherwise); the code plane needs 16-byte
+ *     alignment, the scale plane 4-byte, the codebook 8-byte; x needs
+ *     ldx % 8 == 0 and 16-byte alignment, y 4-byte alignment
+ *     (Q3_ERR_MISALIGNED).
  *   * Numerics: products are formed exactly and accumulated in fp32, so every
  *     output satisfies |y - y_exact| <= 1e-3 * sum_k |x_k w_k| for k <= 8192.
  *     Preconditions (not checked on the device): scale bytes in [16, 240],
@@ -66,7 +73,7 @@ typedef enum q3_status {
   Q3_OK = 0,
   Q3_ERR_INVALID_ARG = 1,        /* null pointer, negative size, bad mode          */
   Q3_ERR_UNSUPPORTED_SHAPE = 2,  /* k not a multiple of 32, m out of range, ...    */
-  Q3_ERR_MISALIGNED = 3,         /* pointer or pitch not aligned as required       */
+  Q3_ERR_MISALIGNED = 3,         /* pointer or stride not aligned as required      */
   Q3_ERR_UNSUPPORTED_DEVICE = 4, /* current device is not gfx950                   */
   Q3_ERR_HIP = 5                 /* a HIP runtime call or kernel launch failed     */
 } q3_status;
@@ -75,35 +82,35 @@ typedef enum q3_status {
 typedef struct q3_layout_info {
   int64_t n, k;
   int64_t groups;            /* k/32                                          */
-  int64_t chunks;            /* ceil(k/128)                                   */
-  int64_t code_row_bytes;    /* 48*chunks                                     */
-  int64_t scale_row_bytes;   /* round_up(4*chunks, 16)                        */
-  int64_t code_plane_bytes;  /* n*code_row_bytes                              */
-  int64_t scale_plane_bytes; /* n*scale_row_bytes                             */
+  int64_t padded_groups;     /* Gp = 4*ceil(k/128)                            */
+  int64_t tiles;             /* ceil(n/16)                                    */
+  int64_t code_tile_bytes;   /* 192*Gp: 16 rows x 12 bytes per group          */
+  int64_t scale_tile_bytes;  /* 16*Gp                                         */
+  int64_t code_plane_bytes;  /* tiles*code_tile_bytes                         */
+  int64_t scale_plane_bytes; /* tiles*scale_tile_bytes                        */
   int64_t codebook_bytes;    /* 8*n                                           */
   int64_t payload_bytes;     /* n*k*13/32: codes + scales, 3.25 bits/weight   */
 } q3_layout_info;
 
-/* A packed matrix.  Pointers are device pointers; the code plane and its pitch
- * must be 16-byte aligned, the scale plane and its pitch 4-byte aligned, the
- * codebook 8-byte aligned. */
+/* A packed matrix.  Pointers are device pointers to planes of q3_layout's
+ * sizes; the code plane must be 16-byte aligned, the scale plane 4-byte
+ * aligned, the codebook 8-byte aligned. */
 typedef struct q3_matrix {
   int64_t n, k;
   const void* code_plane;
-  int64_t code_row_bytes;
   const void* scale_plane;
-  int64_t scale_row_bytes;
   const void* codebook;
 } q3_matrix;
 
 /* A stack of E experts with one shape; expert e's planes start at
- * base + e*stride (bytes).  Strides keep the alignments of q3_matrix. */
+ * base + e*stride (bytes).  Strides keep the alignments of q3_matrix and are
+ * at least the plane sizes. */
 typedef struct q3_expert_stack {
   int64_t num_experts, n, k;
   const void* code_plane;
-  int64_t code_row_bytes, code_expert_stride;
+  int64_t code_expert_stride;
   const void* scale_plane;
-  int64_t scale_row_bytes, scale_expert_stride;
+  int64_t scale_expert_stride;
   const void* codebook;
   int64_t codebook_expert_stride;
 } q3_expert_stack;
@@ -120,12 +127,11 @@ Q3_API q3_status q3_layout(int64_t n, int64_t k, q3_layout_info* out);
  * 3-bit index per weight, one 8-bit scale per group of 32).
  *   codes       [n][ldc] uint8, entries 0..7 (higher bits ignored), ldc >= k
  *   scale_bytes [n][lds] uint8 E8M0, lds >= k/32
- *   code_plane / scale_plane: outputs with the pitches given (>= q3_layout's,
- *   aligned as in q3_matrix); padding is written as zero.
- * Bit-exact; one launch. */
+ *   code_plane / scale_plane: outputs of q3_layout's plane sizes, aligned as
+ *   in q3_matrix; every byte is written (padding as zero).
+ * Bit-exact; one launch per plane. */
 Q3_API q3_status q3_pack(const uint8_t* codes, int64_t ldc, const uint8_t* scale_bytes, int64_t lds,
-                         int64_t n, int64_t k, void* code_plane, int64_t code_row_bytes,
-                         void* scale_plane, int64_t scale_row_bytes, void* stream);
+                         int64_t n, int64_t k, void* code_plane, void* scale_plane, void* stream);
 
 /* Inverse of q3_pack: codes_out [n][k] (values 0..7), scale_out [n][k/32]. */
 Q3_API q3_status q3_unpack(const q3_matrix* w, uint8_t* codes_out, uint8_t* scale_out, void* stream);

@@ -3,6 +3,6 @@
 The GPU product path never imports this package.
 """
 from .q3_oracle import *  # noqa: F401,F403
-from .q3_oracle import (E4M3FN_TABLE, bf16_decode, dequantize, e4m3fn_decode, e8m0_decode, word_offsets,  # noqa: F401,E501
+from .q3_oracle import (E4M3FN_TABLE, bf16_decode, dequantize, e4m3fn_decode, e8m0_decode, word_offset, scale_offset,  # noqa: F401,E501
                         expert_union, grouped_linear, layout, linear, pack, pack_group,
                         topk_route, unpack, unpack_group, within_tolerance)

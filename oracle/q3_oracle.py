@@ -24,8 +24,9 @@ Readings taken where the page is silent (each also listed in the design notes):
   * the scale multiplies the codebook value;
   * activations are bf16, outputs fp32 (oracle: fp64);
   * the bit order of the 96 code bits of a group is this project's own
-    "byte-lane" layout (see pack_group), and so is the placement of a
-    group's three words inside its row (see word_offsets).
+    "byte-lane" layout (see pack_group), and so is the placement of the
+    words and scale bytes in the planes (tiles of 16 rows, steps of 16
+    groups; see word_offset and scale_offset).
 MoE verify rounds (same page, "Adaptive speculation" -- "Expert sharing"): a
 round that checks several drafted tokens at once must read the weights of
 each expert chosen by at least one of those tokens; the oracle routes each
@@ -38,7 +39,8 @@ Parity status per function (what pins each one lives in tests/test_oracle.py):
   bf16_decode     pinned: torch.bfloat16 for random and special bit patterns
   layout          pinned: payload = n*k*13/32 (3.25 bits/weight closed form)
   pack_group      pinned: hand-derived worked example, brute-force round trip
-  word_offsets    pinned: hand-derived offsets, every code byte covered once
+  word_offset,    pinned: hand-derived offsets, every plane byte owned by
+  scale_offset            exactly one (row, group, word, byte) / (row, group)
   pack/unpack     pinned: round trip, worked examples, padding is zero
   linear          pinned: torch fp64 matmul of torch-decoded weights, closed
                   forms (one-hot codebook, constant codes, single group),
@@ -52,8 +54,10 @@ import numpy as np
 
 GROUP = 32                 # weights per group (one scale each)
 CODEBOOK_SIZE = 8          # 3-bit indices
-CHUNK_GROUPS = 4           # groups per 48-byte chunk (3 x 16-byte loads)
+QUAD = 4                   # groups per 16-byte piece (one word of each)
 CODE_BYTES_PER_GROUP = 12  # 96 code bits
+TILE_ROWS = 16             # rows per tile
+STEP_GROUPS = 16           # groups per step (512 weights of a row)
 E8M0_BIAS = 127
 
 
@@ -100,22 +104,25 @@ def bf16_decode(bits) -> np.ndarray:
 def layout(n: int, k: int) -> dict:
     """Sizes of the packed planes for an n x k matrix.
 
-    Codes: per row ceil(k/128) chunks of 4 groups x 12 bytes; groups past
-    k/32 in the last chunk are zero padding.  Where each word of a group sits
-    inside the row is given by word_offsets.
-    Scales: one byte per group, row pitch 4*ceil(k/128) rounded up to 16.
+    Groups of a row are padded to Gp = 4*ceil(k/128) (padding groups are zero)
+    and rows to a multiple of 16 (padding rows are zero).  Both planes are cut
+    into tiles of 16 rows, stored one after the other; inside a tile the
+    groups form steps of 16 (the last step of a row holds p = 4, 8, 12 or 16).
+    A tile holds 16 * 12 * Gp code bytes and 16 * Gp scale bytes; where each
+    word and scale byte sits is given by word_offset and scale_offset.
     Codebook: 8 bytes per row.  Payload counts only real codes and scales:
     k/32 * 13 bytes per row = n*k*13/32 bytes, i.e. 3.25 bits per weight.
     """
     if n < 0 or k <= 0 or k % GROUP:
         raise ValueError("k must be a positive multiple of 32")
     groups = k // GROUP
-    chunks = -(-k // (GROUP * CHUNK_GROUPS))
-    code_row = chunks * CHUNK_GROUPS * CODE_BYTES_PER_GROUP
-    scale_row = -(-(chunks * CHUNK_GROUPS) // 16) * 16
-    return dict(n=n, k=k, groups=groups, chunks=chunks,
-                code_row_bytes=code_row, scale_row_bytes=scale_row,
-                code_plane_bytes=n * code_row, scale_plane_bytes=n * scale_row,
+    padded = -(-groups // QUAD) * QUAD
+    tiles = -(-n // TILE_ROWS)
+    code_tile = TILE_ROWS * CODE_BYTES_PER_GROUP * padded
+    scale_tile = TILE_ROWS * padded
+    return dict(n=n, k=k, groups=groups, padded_groups=padded, tiles=tiles,
+                code_tile_bytes=code_tile, scale_tile_bytes=scale_tile,
+                code_plane_bytes=tiles * code_tile, scale_plane_bytes=tiles * scale_tile,
                 codebook_bytes=n * CODEBOOK_SIZE,
                 payload_bytes=n * groups * (CODE_BYTES_PER_GROUP + 1))
 
@@ -189,53 +196,81 @@ def _unpack_bytes(by):
     return c
 
 
-def word_offsets(k: int) -> np.ndarray:
-    """Byte offset inside a row of word j (0..2) of group g, as int [Gp][3]
-    over the padded groups Gp = 4*ceil(k/128).
+def _place(k: int, r, g):
+    """Tile, row-in-tile, step, quad, group-in-quad and quads-in-step of (row r, group g)."""
+    gp = layout(1, k)["padded_groups"]
+    r = np.asarray(r, dtype=np.int64)
+    g = np.asarray(g, dtype=np.int64)
+    T, i = np.divmod(r, TILE_ROWS)
+    s, u = np.divmod(g, STEP_GROUPS)
+    kb, t = np.divmod(u, QUAD)
+    q = np.minimum(STEP_GROUPS, gp - STEP_GROUPS * s) // QUAD
+    return gp, T, i, s, kb, t, q
 
-    Groups are stored in superchunks of 16 consecutive groups (192 bytes); the
-    last superchunk of a row holds p = 4, 8, 12 or 16 groups.  Inside a
-    superchunk of p groups the words are stored word-major: word j of its
-    group t (0 <= t < p) is at byte 4*(p*j + t) from the superchunk start.
-    So the first words of all groups of a superchunk are contiguous, then all
-    second words, then all third words.
+
+def word_offset(k: int, r, g, j):
+    """Code-plane byte offset of word j (0..2) of group g of row r.
+
+    Tile T = r // 16 starts at T * 192 * Gp.  Step s = g // 16 of a tile starts
+    3072 * s bytes into it (all steps but the last hold 16 groups) and holds
+    3 * 4q pieces of 16 bytes, q = p/4 quads of groups.  Piece 16*(q*j + kb) + i
+    is word j of the quad kb (groups 16s+4kb .. 16s+4kb+3) of the tile's row
+    i = r % 16; inside the piece, 4-byte word t belongs to group 16s+4kb+t.
+    So word j of a step is one run of 64q bytes per quad index, rows innermost.
     """
-    gp = layout(1, k)["chunks"] * CHUNK_GROUPS
-    off = np.empty((gp, 3), dtype=np.int64)
-    for g in range(gp):
-        s, t = divmod(g, 16)
-        p = min(16, gp - 16 * s)
-        for j in range(3):
-            off[g, j] = 192 * s + 4 * (p * j + t)
-    return off
+    gp, T, i, s, kb, t, q = _place(k, r, g)
+    return (T * TILE_ROWS * CODE_BYTES_PER_GROUP * gp + 3072 * s
+            + 16 * (16 * (q * np.asarray(j) + kb) + i) + 4 * t)
 
 
-def _byte_index(k: int) -> np.ndarray:
-    """Row byte position of byte 4j+b of every real group's 12 packed bytes, [G][12]."""
+def scale_offset(k: int, r, g):
+    """Scale-plane byte offset of the scale of group g of row r.
+
+    Tile T starts at T * 16 * Gp, step s at 256 * s inside it; within the step,
+    byte 4*(16*kb + i) + t is the scale of group 16s+4kb+t of row i = r % 16.
+    """
+    gp, T, i, s, kb, t, q = _place(k, r, g)
+    return T * TILE_ROWS * gp + 256 * s + 4 * (16 * kb + i) + t
+
+
+def _code_index(k: int, rows) -> np.ndarray:
+    """Plane byte of byte 4j+b of each real group's 12 packed bytes, [len(rows)][G][12]."""
     G = k // GROUP
-    off = word_offsets(k)[:G]
-    return (off[:, :, None] + np.arange(4)[None, None, :]).reshape(G, 12)
+    r = np.asarray(rows, dtype=np.int64)[:, None, None, None]
+    g = np.arange(G)[None, :, None, None]
+    j = np.arange(3)[None, None, :, None]
+    b = np.arange(4)[None, None, None, :]
+    return (word_offset(k, r, g, j) + b).reshape(len(rows), G, 12)
 
 
-def pack(codes: np.ndarray, scales: np.ndarray):
+def _scale_index(k: int, rows) -> np.ndarray:
+    G = k // GROUP
+    return scale_offset(k, np.asarray(rows, dtype=np.int64)[:, None], np.arange(G)[None, :])
+
+
+def pack(codes: np.ndarray, scales: np.ndarray, block: int = 1024):
     """codes uint8 [n][k] (only bits 0..2 used), scales uint8 [n][k/32] ->
-    (code_plane uint8 [n][code_row_bytes], scale_plane uint8 [n][scale_row_bytes]),
-    padding bytes zero."""
+    (code_plane uint8 [code_plane_bytes], scale_plane uint8 [scale_plane_bytes]),
+    padding bytes zero.  Rows are placed `block` at a time to bound memory."""
     n, k = codes.shape
     L = layout(n, k)
     G = L["groups"]
-    cp = np.zeros((n, L["code_row_bytes"]), dtype=np.uint8)
-    cp[:, _byte_index(k).reshape(-1)] = _pack_bytes(codes.reshape(n, G, 32)).reshape(n, G * 12)
-    sp = np.zeros((n, L["scale_row_bytes"]), dtype=np.uint8)
-    sp[:, :G] = scales
+    cp = np.zeros(L["code_plane_bytes"], dtype=np.uint8)
+    sp = np.zeros(L["scale_plane_bytes"], dtype=np.uint8)
+    for r0 in range(0, n, block):
+        rows = np.arange(r0, min(n, r0 + block))
+        cp[_code_index(k, rows).reshape(-1)] = _pack_bytes(codes[rows].reshape(len(rows), G, 32)).reshape(-1)
+        sp[_scale_index(k, rows).reshape(-1)] = scales[rows].reshape(-1)
     return cp, sp
 
 
-def unpack(code_plane: np.ndarray, scale_plane: np.ndarray, n: int, k: int):
-    """(code_plane, scale_plane) -> (codes uint8 [n][k], scales uint8 [n][k/32])."""
+def unpack(code_plane: np.ndarray, scale_plane: np.ndarray, n: int, k: int, rows=None):
+    """(code_plane, scale_plane) of an n x k matrix -> (codes uint8 [len(rows)][k],
+    scales uint8 [len(rows)][k/32]) for `rows` (default: all n rows)."""
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
     G = k // GROUP
-    by = np.ascontiguousarray(code_plane[:n][:, _byte_index(k).reshape(-1)]).reshape(n, G, 12)
-    return _unpack_bytes(by).reshape(n, k), np.ascontiguousarray(scale_plane[:n, :G])
+    by = np.asarray(code_plane)[_code_index(k, rows)]
+    return _unpack_bytes(by).reshape(len(rows), k), np.asarray(scale_plane)[_scale_index(k, rows)]
 
 
 # ---------------------------------------------------------------- the layer
@@ -262,7 +297,7 @@ def linear(code_plane, scale_plane, codebook, n, k, x_bits, rows=None, block=204
     bound = np.empty_like(y)
     for s in range(0, rows.size, block):
         r = rows[s:s + block]
-        codes, scales = unpack(code_plane[r], scale_plane[r], r.size, k)
+        codes, scales = unpack(code_plane, scale_plane, n, k, rows=r)
         w = dequantize(codes, scales, codebook[r])
         y[:, s:s + r.size] = x @ w.T
         bound[:, s:s + r.size] = xa @ np.abs(w).T

@@ -19,8 +19,15 @@ def pack_layer(q3, layer):
 
 
 def oracle_linear(layer, x_bits, rows=None):
-    cp, sp = oracle.pack(layer.codes, layer.scales)
-    return oracle.linear(cp, sp, layer.codebook, layer.n, layer.k, x_bits, rows=rows)
+    """Oracle products for all rows, or for `rows` only (those rows are packed on
+    their own, which keeps full-size cases cheap; placement does not change
+    what a row computes)."""
+    if rows is None:
+        cp, sp = oracle.pack(layer.codes, layer.scales)
+        return oracle.linear(cp, sp, layer.codebook, layer.n, layer.k, x_bits)
+    rows = np.asarray(rows)
+    cp, sp = oracle.pack(layer.codes[rows], layer.scales[rows])
+    return oracle.linear(cp, sp, layer.codebook[rows], len(rows), layer.k, x_bits)
 
 
 def assert_close(y_gpu, y_ref, bound, what=""):

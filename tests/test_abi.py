@@ -66,7 +66,7 @@ def test_validation_rejects_before_any_hip_call(q3lib):
     assert q3lib.q3_layout(-1, 32, ctypes.byref(info)) == 1
     assert q3lib.q3_layout(4, 32, None) == 1
     fake = 0x1000   # never dereferenced: every call below fails validation first
-    w = _lib.Q3Matrix(16, 64, fake, 48, fake, 16, fake)
+    w = _lib.Q3Matrix(16, 64, fake, fake, fake)
     assert q3lib.q3_gemv(None, fake, 1, 64, fake, 16, None) == 1
     assert q3lib.q3_gemv(ctypes.byref(w), fake, 0, 64, fake, 16, None) == 2       # m = 0
     assert q3lib.q3_gemv(ctypes.byref(w), fake, 9, 64, fake, 16, None) == 2       # m > 8
@@ -75,18 +75,26 @@ def test_validation_rejects_before_any_hip_call(q3lib):
     assert q3lib.q3_gemv(ctypes.byref(w), fake + 2, 1, 64, fake, 16, None) == 3   # x misaligned
     assert q3lib.q3_gemv(ctypes.byref(w), fake, 1, 60, fake, 16, None) == 1       # ldx < k
     assert q3lib.q3_gemv(ctypes.byref(w), fake, 1, 64, fake, 8, None) == 1        # ldy < n
-    bad = _lib.Q3Matrix(16, 48, fake, 48, fake, 16, fake)                          # k % 32 != 0
+    bad = _lib.Q3Matrix(16, 48, fake, fake, fake)                                  # k % 32 != 0
     assert q3lib.q3_gemv(ctypes.byref(bad), fake, 1, 64, fake, 16, None) == 2
-    pitch = _lib.Q3Matrix(16, 256, fake, 48, fake, 16, fake)                       # code pitch too small
-    assert q3lib.q3_gemv(ctypes.byref(pitch), fake, 1, 256, fake, 16, None) == 1
-    mis = _lib.Q3Matrix(16, 64, fake + 4, 48, fake, 16, fake)                      # code plane not 16-aligned
+    mis = _lib.Q3Matrix(16, 64, fake + 4, fake, fake)                              # code plane not 16-aligned
     assert q3lib.q3_gemv(ctypes.byref(mis), fake, 1, 64, fake, 16, None) == 3
-    assert q3lib.q3_pack(fake, 63, fake, 2, 16, 64, fake, 48, fake, 16, None) == 1    # ldc < k
-    assert q3lib.q3_pack(fake, 64, fake, 2, 16, 64, fake + 8, 48, fake, 16, None) == 3
+    mis = _lib.Q3Matrix(16, 64, fake, fake + 2, fake)                              # scale plane not 4-aligned
+    assert q3lib.q3_gemv(ctypes.byref(mis), fake, 1, 64, fake, 16, None) == 3
+    huge = _lib.Q3Matrix(1 << 20, 8192, fake, fake, fake)                          # code plane >= 2 GiB
+    assert q3lib.q3_gemv(ctypes.byref(huge), fake, 1, 8192, fake, 1 << 20, None) == 2
+    nul = _lib.Q3Matrix(16, 64, fake, None, fake)
+    assert q3lib.q3_gemv(ctypes.byref(nul), fake, 1, 64, fake, 16, None) == 1
+    assert q3lib.q3_pack(fake, 63, fake, 2, 16, 64, fake, fake, None) == 1        # ldc < k
+    assert q3lib.q3_pack(fake, 64, fake, 1, 16, 64, fake, fake, None) == 1        # lds < k/32
+    assert q3lib.q3_pack(fake, 64, fake, 2, 16, 64, fake + 8, fake, None) == 3
     assert q3lib.q3_moe_topk(fake, 8, 64, 65, fake, None) == 2
     assert q3lib.q3_moe_topk(fake, 8, 2048, 8, fake, None) == 2
-    st = _lib.Q3ExpertStack(4, 16, 64, fake, 48, 48 * 16, fake, 16, 256, fake, 128)
+    # n = 16, k = 64: one tile of 192*4 = 768 code bytes and 64 scale bytes.
+    st = _lib.Q3ExpertStack(4, 16, 64, fake, 768, fake, 64, fake, 128)
     assert q3lib.q3_grouped_expert_gemv(ctypes.byref(st), fake, 64, 2, fake, 8, 8, fake, 16, None) == 1
     assert q3lib.q3_grouped_expert_gemv(ctypes.byref(st), fake, 64, 0, fake, 9, 8, fake, 16, None) == 2
-    st.code_expert_stride = 40
+    st.code_expert_stride = 752                                                     # smaller than a plane
+    assert q3lib.q3_grouped_expert_gemv(ctypes.byref(st), fake, 64, 0, fake, 8, 8, fake, 16, None) == 1
+    st.code_expert_stride = 776                                                     # not 16-aligned
     assert q3lib.q3_grouped_expert_gemv(ctypes.byref(st), fake, 64, 0, fake, 8, 8, fake, 16, None) == 3

@@ -41,9 +41,11 @@ def test_pack_bit_exact(q3, n, k):
 def test_pack_worked_example(q3):
     codes = np.array([[k % 8 for k in range(32)]], dtype=np.uint8)
     w = q3.q3_pack(dev(codes), dev(np.array([[127]], dtype=np.uint8)), dev(np.zeros((1, 8), np.uint8)))
-    row = w.code_plane.cpu().numpy()[0]
-    words = [int(row[16 * j:16 * j + 4].view(np.uint32)[0]) for j in range(3)]   # k = 32: words at 0, 16, 32
+    plane = w.code_plane.cpu().numpy()
+    # k = 32, one row: one quad per step, so word j is the first word of piece 16*j (byte 256*j).
+    words = [int(plane[256 * j:256 * j + 4].view(np.uint32)[0]) for j in range(3)]
     assert [hex(v) for v in words] == ["0xfbb26920", "0xbb32a920", "0xfbf2a9a0"]
+    assert w.scale_plane.cpu().numpy()[0] == 127
 
 
 GEMV_CASES = [(1024, 1024, 1), (4096, 4096, 1), (4096, 4096, 4), (4096, 4096, 8), (37, 96, 3), (1, 32, 1),

@@ -72,7 +72,9 @@ def test_payload_is_3p25_bits_per_weight():
         L = oracle.layout(n, k)
         assert L["payload_bytes"] * 8 == n * k * bpw
         assert L["payload_bytes"] == n * k * 13 // 32
-        assert L["code_row_bytes"] % 16 == 0 and L["scale_row_bytes"] % 16 == 0
+        # With n a multiple of 16 and k of 128 the planes hold exactly the payload.
+        if n % 16 == 0 and k % 128 == 0:
+            assert L["code_plane_bytes"] + L["scale_plane_bytes"] == L["payload_bytes"]
     assert oracle.layout(1024, 1024)["payload_bytes"] == 425984
     assert oracle.layout(4096, 4096)["payload_bytes"] == 6815744
     assert oracle.layout(28672, 8192)["payload_bytes"] == 95420416
@@ -85,28 +87,55 @@ def test_worked_example():
     words = tuple(int(v, 16) for v in kv["words"].split(","))
     assert oracle.pack_group(codes) == words
     assert oracle.unpack_group(words) == codes
-    cp, _ = oracle.pack(np.array(codes, dtype=np.uint8)[None, :], np.array([[127]], dtype=np.uint8))
-    # k = 32: one group in a 4-group superchunk, so its words sit at bytes 0, 16 and 32.
+    cp, sp = oracle.pack(np.array(codes, dtype=np.uint8)[None, :], np.array([[127]], dtype=np.uint8))
+    # k = 32, one row: the tile's single step holds one quad (q = 1), so word j
+    # of row 0's group is the first word of piece 16*j, at byte 256*j.
+    assert cp.size == 16 * 12 * 4 and sp.size == 16 * 4
     for j, w in enumerate(words):
-        assert cp[0, 16 * j:16 * j + 4].tobytes() == w.to_bytes(4, "little")
-    assert not np.delete(cp[0], [b for j in range(3) for b in range(16 * j, 16 * j + 4)]).any()
+        assert cp[256 * j:256 * j + 4].tobytes() == w.to_bytes(4, "little")
+    assert not np.delete(cp, [b for j in range(3) for b in range(256 * j, 256 * j + 4)]).any()
+    assert sp[0] == 127 and not sp[1:].any()
 
 
 def test_word_placement_worked_examples():
     for row in read_golden("word_placement.txt"):
-        k, g, j, byte = (int(v) for v in row.split())
-        assert oracle.word_offsets(k)[g, j] == byte, (k, g, j)
+        plane, k, r, g, j, byte = row.split()
+        k, r, g, byte = int(k), int(r), int(g), int(byte)
+        if plane == "code":
+            assert int(oracle.word_offset(k, r, g, int(j))) == byte, (k, r, g, j)
+        else:
+            assert int(oracle.scale_offset(k, r, g)) == byte, (k, r, g)
 
 
-@pytest.mark.parametrize("k", [32, 96, 128, 160, 640, 768, 1024, 4096, 8224])
-def test_word_placement_covers_each_code_byte_once(k):
-    off = oracle.word_offsets(k)
-    L = oracle.layout(1, k)
-    cover = np.zeros(L["code_row_bytes"], dtype=np.int64)
-    for b in range(4):
-        np.add.at(cover, (off + b).reshape(-1), 1)
+@pytest.mark.parametrize("n,k", [(1, 32), (16, 96), (17, 128), (3, 160), (33, 640), (16, 768), (5, 1024),
+                                 (2, 4096), (1, 8224)])
+def test_placement_covers_each_plane_byte_once(n, k):
+    """Over all rows of the padded tiles and all padded groups, every code-plane
+    byte belongs to exactly one (row, group, word, byte) and every scale-plane
+    byte to exactly one (row, group)."""
+    L = oracle.layout(n, k)
+    rows = np.arange(16 * L["tiles"])[:, None, None, None]
+    g = np.arange(L["padded_groups"])[None, :, None, None]
+    j = np.arange(3)[None, None, :, None]
+    b = np.arange(4)[None, None, None, :]
+    cover = np.zeros(L["code_plane_bytes"], dtype=np.int64)
+    np.add.at(cover, (oracle.word_offset(k, rows, g, j) + b).reshape(-1), 1)
     assert np.all(cover == 1)
-    assert off.min() == 0 and off.max() + 4 == L["code_row_bytes"]
+    scover = np.zeros(L["scale_plane_bytes"], dtype=np.int64)
+    np.add.at(scover, oracle.scale_offset(k, rows[..., 0, 0], g[..., 0, 0]).reshape(-1), 1)
+    assert np.all(scover == 1)
+
+
+def test_step_words_are_contiguous_runs():
+    """Word j of one quad index of a full step is a contiguous 256-byte run over
+    the tile's 16 rows (16 bytes per row), and the scales of a full step are one
+    256-byte run: a 64-lane load of the step reads 1 KB or 256 B contiguous."""
+    k = 1024
+    for j in range(3):
+        offs = sorted(int(oracle.word_offset(k, i, 16 + 4 * kb, j)) for kb in range(4) for i in range(16))
+        assert offs == list(range(offs[0], offs[0] + 64 * 16, 16)) and offs[0] == 3072 + 1024 * j
+    soffs = sorted(int(oracle.scale_offset(k, i, 16 + 4 * kb)) for kb in range(4) for i in range(16))
+    assert soffs == list(range(256, 512, 4))
 
 
 def test_each_code_position_owns_three_distinct_bits():
@@ -140,20 +169,28 @@ def test_group_roundtrip_random_and_vectorised_agree():
     assert np.array_equal(oracle.q3_oracle._unpack_bytes(by), c)
 
 
-@pytest.mark.parametrize("n,k", [(3, 32), (5, 96), (7, 128), (4, 160), (9, 768), (2, 4096)])
+@pytest.mark.parametrize("n,k", [(3, 32), (5, 96), (7, 128), (4, 160), (9, 768), (2, 4096), (18, 640)])
 def test_plane_roundtrip_padding_and_masking(n, k):
     rng = np.random.default_rng(n * 1000 + k)
     codes = rng.integers(0, 256, size=(n, k), dtype=np.uint8)     # high bits must be ignored
     scales = rng.integers(0, 255, size=(n, k // 32), dtype=np.uint8)
     cp, sp = oracle.pack(codes, scales)
     L = oracle.layout(n, k)
-    assert cp.shape == (n, L["code_row_bytes"]) and sp.shape == (n, L["scale_row_bytes"])
+    assert cp.shape == (L["code_plane_bytes"],) and sp.shape == (L["scale_plane_bytes"],)
     G = k // 32
-    off = oracle.word_offsets(k)
-    pad = [int(o) + b for o in off[G:].reshape(-1) for b in range(4)]   # words of padding groups
-    assert not cp[:, pad].any() and not sp[:, G:].any()
+    # Bytes of padding rows and padding groups are zero.
+    rows = np.arange(16 * L["tiles"])
+    real = (rows[:, None] < n) & (np.arange(L["padded_groups"])[None, :] < G)
+    g = np.arange(L["padded_groups"])
+    woff = oracle.word_offset(k, rows[:, None, None], g[None, :, None], np.arange(3)[None, None, :])
+    pad = (woff[~real][..., None] + np.arange(4)).reshape(-1)
+    assert not cp[pad].any()
+    assert not sp[oracle.scale_offset(k, rows[:, None], g[None, :])[~real]].any()
     c2, s2 = oracle.unpack(cp, sp, n, k)
     assert np.array_equal(c2, codes & 7) and np.array_equal(s2, scales)
+    sub = np.array([n - 1, 0])
+    c3, s3 = oracle.unpack(cp, sp, n, k, rows=sub)
+    assert np.array_equal(c3, codes[sub] & 7) and np.array_equal(s3, scales[sub])
 
 
 # ------------------------------------------------------------------ products
