@@ -401,10 +401,11 @@ void linear_kernel(KArgs a) {
                                 },
                                 [&](int c) { return 16u * c; });   // rows are contiguous, then the zero block
       __syncthreads();
-      // One step is in flight while another is computed.  The scheduling
-      // barriers keep each refill where it is issued; without them the
-      // compiler sinks the loads below the MFMAs or hoists the refill above
-      // the computation that still reads the registers.
+      // One step is in flight while another is computed (measured: issuing
+      // more steps ahead is slower on this pattern).  The scheduling barriers
+      // keep each refill where it is issued; without them the compiler sinks
+      // the loads below the MFMAs or hoists the refill above the computation
+      // that still reads the registers.
       for (int s = s0; s < s1; s += 2) {
         load_step(p, rt, last_ok, s + 1, s1, B);
         __builtin_amdgcn_sched_barrier(0);
@@ -581,31 +582,31 @@ hipError_t launch_one(const KArgs& a, size_t shm, unsigned grid_y, hipStream_t s
 }
 
 // Launch shape: R row tiles per wave, W waves per block, K split sk (full-K
-// only).  Chosen so a launch has about two to four resident waves per SIMD
-// (1024 SIMDs on the chip) without leaving CUs idle: small matrices split K
-// across a block's waves, tall ones give each wave more rows so the B
-// operands of a step serve them all.
+// only).  Measured on MI355X over the decode shapes: tall matrices stream best
+// with fewer, longer-lived waves that each own two row tiles (a 4096 x 4096
+// launch already fills the chip with one row tile per wave and a 4-way K
+// split); activations that do not fit in LDS stream through 8-wave blocks.
 struct Shape {
   int r, w, sk;
 };
 
-constexpr int kCUs = 256;
-
-Shape pick_shape(int64_t n, int groups, bool full_k, int nt, bool dot) {
+Shape pick_shape(int64_t n, int groups, bool full_k, int tokens, bool dot) {
   const int64_t tiles = (n + 15) / 16;
   const int steps = (((groups + 3) & ~3) + 15) / 16;
 #if defined(Q3_FORCE_R) && defined(Q3_FORCE_W) && defined(Q3_FORCE_SK)
   (void)tiles;
   (void)steps;
-  (void)nt;
+  (void)tokens;
   (void)dot;
   return Shape{Q3_FORCE_R, Q3_FORCE_W, full_k ? Q3_FORCE_SK : 1};
 #else
-  (void)dot;
-  if (!full_k) return Shape{1, 8, 1};   // stream mode: every wave walks all of K
-  // Full-K: split K until there are about 2048 waves.
+  if (!full_k) return Shape{!dot && tokens > 32 && tiles >= 4096 ? 2 : 1, 8, 1};
+  if (tiles >= 1024) return Shape{dot ? 1 : 2, 4, 1};
+  // Small matrices: split K over the block's waves up to about 1024 waves
+  // (2048 when each wave has several tokens to multiply).
+  const int64_t target = tokens > 4 ? 2048 : 1024;
   int sk = 1;
-  while (sk < 8 && sk * 2 <= steps && tiles * sk < 2048) sk *= 2;
+  while (sk < 8 && sk * 2 <= steps && tiles * sk < target) sk *= 2;
   return Shape{1, sk > 4 ? 8 : 4, sk};
 #endif
 }
@@ -626,7 +627,7 @@ hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t
   constexpr int kSlice = kDot ? NT : 16 * NT;
   const size_t fk = full_k_bytes(tokens_in_slice, a.G);
   const bool full_k = fk <= (size_t)kFullKBudget;
-  const Shape sh = kGrouped ? Shape{1, 4, 1} : pick_shape(a.n, a.G, full_k, NT, kDot);
+  const Shape sh = kGrouped ? Shape{1, 4, 1} : pick_shape(a.n, a.G, full_k, tokens_in_slice, kDot);
   a.sk = full_k ? sh.sk : 1;
   const int steps = (((a.G + 3) & ~3) + 15) / 16;
   while (a.sk > 1 && a.sk > steps) a.sk /= 2;   // every wave gets at least one step
