@@ -48,6 +48,12 @@ namespace q3 {
 namespace {
 
 constexpr int kFullKBudget = 96 * 1024;   // LDS bytes for full-K activation staging
+
+// How a block holds the activations.
+enum Mode : int {
+  kShared = 0,   // all of K for all tokens, staged once per block
+  kStream = 1,   // one 512-k step at a time, double-buffered
+};
 constexpr uint32_t kRowPad = 16;          // LDS row padding against bank conflicts
 
 struct KArgs {
@@ -222,13 +228,6 @@ __device__ __forceinline__ void dot_step(const StepData<R>& d, const RowTile (&r
     for (int m = 0; m < M; ++m) asm volatile("" : "+v"(acc[r][m]));
 }
 
-// Token slot j of the current slice -> x row and y row.
-struct Tokens {
-  int count;          // tokens in this slice
-  int xrow[64];
-  int yrow[64];
-};
-
 // Copy `count` 16-byte chunks from global memory (buffer resource) into LDS.
 // All loads of a batch are issued before any store, so a batch costs one
 // memory latency instead of one per chunk.  src(c) returns the chunk's byte
@@ -259,13 +258,12 @@ constexpr int min_waves_per_eu() {
 }
 
 // NT: column tiles of 16 tokens (matrix-core mode) or tokens (vector-ALU mode).
-template <int NT, int R, int kW, bool kGrouped, bool kFullK, bool kDot>
+template <int NT, int R, int kW, bool kGrouped, int kMode, bool kDot>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<NT, R, kDot>())))
 void linear_kernel(KArgs a) {
   constexpr int kThreads = 64 * kW;
   constexpr int kSlice = kDot ? NT : 16 * NT;   // tokens per slice
   extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ Tokens tk;
   __shared__ int pairs[64];
   __shared__ int npairs;
 
@@ -274,7 +272,7 @@ void linear_kernel(KArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform from here on
   const int i = lane & 15;
   const int kb = lane >> 4;
-  const int sk = kFullK ? a.sk : 1;
+  const int sk = kMode != kStream ? a.sk : 1;
   const int rb = kW / sk;
   const int rg = wave / sk;
   const int ks = wave - rg * sk;
@@ -316,47 +314,21 @@ void linear_kernel(KArgs a) {
     rt[r].vscale = tile_ok ? (uint32_t)T * (16u * gp) + 4u * lane : kOob;
   }
 
-  const int s0 = kFullK ? (ks * p.steps) / sk : 0;
-  const int s1 = kFullK ? ((ks + 1) * p.steps) / sk : p.steps;
+  const int s0 = kMode != kStream ? (ks * p.steps) / sk : 0;
+  const int s1 = kMode != kStream ? ((ks + 1) * p.steps) / sk : p.steps;
 
-  // The first step's loads go out before anything else.
   StepData<R> A, B;
-  load_step(p, rt, last_ok, s0, s1, A);
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t row = (tile0 + r) * 16 + i;
-    const u32x2 cb = bload64(cbr, row < a.n ? (uint32_t)row * 8u : kOob);
-    rt[r].cbl = cb.x;
-    rt[r].cbh = cb.y;
-  }
-
   const rsrc_t xr_rsrc = make_rsrc(a.x, (uint32_t)((a.x_rows - 1) * a.ldx * 2 + (int64_t)G * 64));
   const uint32_t ldx_bytes = (uint32_t)(a.ldx * 2);
 
   for (int slice = 0; slice < total_tokens; slice += kSlice) {
-    if (tid == 0) {
-      const int cnt = total_tokens - slice < kSlice ? total_tokens - slice : kSlice;
-      tk.count = cnt;
-      for (int j = 0; j < kSlice; ++j) {
-        if (j < cnt) {
-          if (kGrouped) {
-            const int q = pairs[slice + j];
-            tk.xrow[j] = a.x_by_slot ? q : q / a.topk;
-            tk.yrow[j] = q;
-          } else {
-            tk.xrow[j] = slice + j;
-            tk.yrow[j] = slice + j;
-          }
-        } else {
-          tk.xrow[j] = 0;
-          tk.yrow[j] = 0;
-        }
-      }
-    }
-    __syncthreads();
-    const int cnt = __builtin_amdgcn_readfirstlane(tk.count);
-    if (slice > 0) load_step(p, rt, last_ok, s0, s1, A);
-
+    const int cnt = total_tokens - slice < kSlice ? total_tokens - slice : kSlice;
+    // Token slot j of this slice -> its x row and y row.
+    auto xrow = [&](int j) -> int {
+      if (kGrouped) return a.x_by_slot ? pairs[slice + j] : pairs[slice + j] / a.topk;
+      return slice + j;
+    };
+    auto yrow = [&](int j) -> int { return kGrouped ? pairs[slice + j] : slice + j; };
     f32x4 acc[R][kDot ? 1 : NT];
     float dacc[R][kDot ? NT : 1];
 #pragma unroll
@@ -366,6 +338,20 @@ void linear_kernel(KArgs a) {
 #pragma unroll
       for (int c = 0; c < (kDot ? NT : 1); ++c) dacc[r][c] = 0.f;
     }
+    // The slice's first weight step (and, once, the codebooks) is requested
+    // right after the activations it will meet.
+    auto begin_slice = [&](int sl) {
+      load_step(p, rt, last_ok, s0, s1, A);
+      if (sl == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int64_t row = (tile0 + r) * 16 + i;
+          const u32x2 cb = bload64(cbr, row < a.n ? (uint32_t)row * 8u : kOob);
+          rt[r].cbl = cb.x;
+          rt[r].cbh = cb.y;
+        }
+      }
+    };
     // Lane addresses of token slots at the step's start in a row-per-token x
     // layout of the given row stride, for buffer base `base` (absent tokens of
     // matrix-core mode go to `zero`, a 1 KB zero block, and stay there).
@@ -386,20 +372,38 @@ void linear_kernel(KArgs a) {
       }
     };
 
-    if (kFullK) {
+    if (kMode == kShared) {
       // Stage all activations: row j holds token j's K values (zero past K,
       // including the row's 16-byte pad, which lanes past a partial last
-      // step's quads read with a zero scale); a 1 KB zero block follows.
+      // step's quads read with a zero scale); a 1 KB zero block follows.  The
+      // first batch of activation loads goes out before the weight loads:
+      // loads complete in issue order, so activations queued behind a step of
+      // weights would hold up every wave of the block at the barrier below.
       const uint32_t rstride = gp * 64u + kRowPad;
       const uint32_t zero_base = (uint32_t)cnt * rstride;
       const int cpr = (int)(rstride / 16);
-      stage_chunks<8, kThreads>(xr_rsrc, cnt * cpr + 64, lds,
-                                [&](int c) {
-                                  const int j = c / cpr, q = c - j * cpr;
-                                  return j < cnt && q * 8 < G * 32 ? (uint32_t)tk.xrow[j] * ldx_bytes + 16u * q
-                                                                   : kOob;
-                                },
-                                [&](int c) { return 16u * c; });   // rows are contiguous, then the zero block
+      const int nchunk = cnt * cpr + 64;   // rows are contiguous, then the zero block
+      auto src = [&](int c) {
+        const int j = c / cpr, q = c - j * cpr;
+        return j < cnt && q * 8 < G * 32 ? (uint32_t)xrow(j) * ldx_bytes + 16u * q : kOob;
+      };
+      constexpr int kFirst = 4;
+      u32x4 xv[kFirst];
+#pragma unroll
+      for (int q = 0; q < kFirst; ++q) {
+        const int c = tid + q * kThreads;
+        xv[q] = bload128(xr_rsrc, c < nchunk ? src(c) : kOob);
+      }
+      begin_slice(slice);
+#pragma unroll
+      for (int q = 0; q < kFirst; ++q) {
+        const int c = tid + q * kThreads;
+        if (c < nchunk) *reinterpret_cast<u32x4*>(lds + 16u * c) = xv[q];
+      }
+      if (nchunk > kFirst * kThreads)
+        stage_chunks<4, kThreads>(xr_rsrc, nchunk - kFirst * kThreads, lds + 16 * kFirst * kThreads,
+                                  [&](int c) { return src(c + kFirst * kThreads); },
+                                  [&](int c) { return 16u * c; });
       __syncthreads();
       // One step is in flight while another is computed (measured: issuing
       // more steps ahead is slower on this pattern).  The scheduling barriers
@@ -434,7 +438,7 @@ void linear_kernel(KArgs a) {
           const int j = idx >> 6, c16 = idx & 63;
           const int k0 = s * 512 + c16 * 8;
           const bool ok = idx < nchunk && j < cnt && s < p.steps && k0 < G * 32;
-          r[q] = bload128(xr_rsrc, ok ? (uint32_t)tk.xrow[j] * ldx_bytes + 2u * k0 : kOob);
+          r[q] = bload128(xr_rsrc, ok ? (uint32_t)xrow(j) * ldx_bytes + 2u * k0 : kOob);
         }
       };
       auto put = [&](int buf, const u32x4 (&r)[kChunks]) {
@@ -445,9 +449,10 @@ void linear_kernel(KArgs a) {
           if (idx < nchunk) *reinterpret_cast<u32x4*>(lds + buf * buf_bytes + j * rstride + 16u * c16) = r[q];
         }
       };
-      if (tid < 64) *reinterpret_cast<u32x4*>(lds + zero_base + 16u * tid) = u32x4{0u, 0u, 0u, 0u};
       u32x4 xr[kChunks];
       fetch(0, xr);
+      begin_slice(slice);
+      if (tid < 64) *reinterpret_cast<u32x4*>(lds + zero_base + 16u * tid) = u32x4{0u, 0u, 0u, 0u};
       put(0, xr);
       __syncthreads();
       for (int s = 0; s < s1; s += 2) {
@@ -482,7 +487,7 @@ void linear_kernel(KArgs a) {
           dacc[r][m] = v;
         }
     }
-    if (kFullK && sk > 1) {
+    if (kMode != kStream && sk > 1) {
       __syncthreads();   // activations no longer needed: reuse LDS for partial sums
       constexpr int kVals = kDot ? NT : 4 * NT;   // floats per lane and row tile
       float* red = reinterpret_cast<float*>(lds);
@@ -514,7 +519,7 @@ void linear_kernel(KArgs a) {
             if (row < a.n) {
 #pragma unroll
               for (int m = 0; m < NT; ++m)
-                if (m < cnt) a.y[(int64_t)tk.yrow[m] * a.ldy + row] = dacc[r][m];
+                if (m < cnt) a.y[(int64_t)yrow(m) * a.ldy + row] = dacc[r][m];
             }
           }
         }
@@ -524,7 +529,7 @@ void linear_kernel(KArgs a) {
         for (int c = 0; c < NT; ++c) {
           const int j = 16 * c + i;
           if (j < cnt) {
-            float* yr = a.y + (int64_t)tk.yrow[j] * a.ldy;
+            float* yr = a.y + (int64_t)yrow(j) * a.ldy;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
 #pragma unroll
@@ -537,7 +542,7 @@ void linear_kernel(KArgs a) {
         }
       }
     }
-    __syncthreads();   // token table and LDS are rewritten by the next slice
+    __syncthreads();   // LDS is rewritten by the next slice
   }
 }
 
@@ -554,12 +559,12 @@ size_t reduce_bytes(int vals, int r, int w) { return (size_t)w * r * vals * 64 *
 
 // Dynamic LDS above 64 KB must be allowed per kernel; raise each kernel's limit
 // once to the largest size this file ever requests.
-template <int NT, int R, int kW, bool kGrouped, bool kFullK, bool kDot>
+template <int NT, int R, int kW, bool kGrouped, int kMode, bool kDot>
 hipError_t allow_lds(size_t bytes) {
   static std::atomic<size_t> allowed{64 * 1024};   // per kernel instantiation
   if (bytes <= allowed.load(std::memory_order_acquire)) return hipSuccess;
   const hipError_t e =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(linear_kernel<NT, R, kW, kGrouped, kFullK, kDot>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(linear_kernel<NT, R, kW, kGrouped, kMode, kDot>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e == hipSuccess) {
     size_t cur = allowed.load(std::memory_order_acquire);
@@ -569,15 +574,15 @@ hipError_t allow_lds(size_t bytes) {
   return e;
 }
 
-template <int NT, int R, int kW, bool kGrouped, bool kFullK, bool kDot>
+template <int NT, int R, int kW, bool kGrouped, int kMode, bool kDot>
 hipError_t launch_one(const KArgs& a, size_t shm, unsigned grid_y, hipStream_t s) {
-  const int rb = kW / (kFullK ? a.sk : 1);
+  const int rb = kW / (kMode != kStream ? a.sk : 1);
   const int64_t tiles = (a.n + 15) / 16;
   const int64_t groups = (tiles + R - 1) / R;   // row groups of R tiles
   const dim3 grid((unsigned)((groups + rb - 1) / rb), grid_y);
-  hipError_t e = allow_lds<NT, R, kW, kGrouped, kFullK, kDot>(shm);
+  hipError_t e = allow_lds<NT, R, kW, kGrouped, kMode, kDot>(shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((linear_kernel<NT, R, kW, kGrouped, kFullK, kDot>), grid, dim3(64 * kW), shm, s, a);
+  hipLaunchKernelGGL((linear_kernel<NT, R, kW, kGrouped, kMode, kDot>), grid, dim3(64 * kW), shm, s, a);
   return hipGetLastError();
 }
 
@@ -612,13 +617,15 @@ Shape pick_shape(int64_t n, int groups, bool full_k, int tokens, bool dot) {
 }
 
 template <int NT, int R, bool kGrouped, bool kDot>
-hipError_t launch_r(KArgs a, int w, bool full_k, size_t shm, unsigned grid_y, hipStream_t s) {
-  if (full_k) {
-    if (w == 8) return launch_one<NT, R, 8, kGrouped, true, kDot>(a, shm, grid_y, s);
-    return launch_one<NT, R, 4, kGrouped, true, kDot>(a, shm, grid_y, s);
+hipError_t launch_r(KArgs a, int w, int mode, size_t shm, unsigned grid_y, hipStream_t s) {
+  switch (mode) {
+    case kShared:
+      if (w == 8) return launch_one<NT, R, 8, kGrouped, kShared, kDot>(a, shm, grid_y, s);
+      return launch_one<NT, R, 4, kGrouped, kShared, kDot>(a, shm, grid_y, s);
+    default:
+      if (w == 8) return launch_one<NT, R, 8, kGrouped, kStream, kDot>(a, shm, grid_y, s);
+      return launch_one<NT, R, 4, kGrouped, kStream, kDot>(a, shm, grid_y, s);
   }
-  if (w == 8) return launch_one<NT, R, 8, kGrouped, false, kDot>(a, shm, grid_y, s);
-  return launch_one<NT, R, 4, kGrouped, false, kDot>(a, shm, grid_y, s);
 }
 
 // tokens_in_slice: tokens the LDS staging holds at once.
@@ -632,17 +639,18 @@ hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t
   const int steps = (((a.G + 3) & ~3) + 15) / 16;
   while (a.sk > 1 && a.sk > steps) a.sk /= 2;   // every wave gets at least one step
   if (a.sk < 1 || a.sk > sh.w || sh.w % a.sk != 0) return hipErrorInvalidValue;
-  size_t shm = full_k ? fk : stream_bytes(kSlice);
-  if (full_k && a.sk > 1) {
+  const int mode = full_k ? kShared : kStream;
+  size_t shm = mode == kShared ? fk : stream_bytes(kSlice);
+  if (mode != kStream && a.sk > 1) {
     const size_t red = reduce_bytes(kDot ? NT : 4 * NT, sh.r, sh.w);
     if (shm < red) shm = red;
   }
   if constexpr (kGrouped || kDot) {
-    return launch_r<NT, 1, kGrouped, kDot>(a, sh.w, full_k, shm, grid_y, s);
+    return launch_r<NT, 1, kGrouped, kDot>(a, sh.w, mode, shm, grid_y, s);
   } else {
     switch (sh.r) {
-      case 1: return launch_r<NT, 1, kGrouped, kDot>(a, sh.w, full_k, shm, grid_y, s);
-      case 2: return launch_r<NT, 2, kGrouped, kDot>(a, sh.w, full_k, shm, grid_y, s);
+      case 1: return launch_r<NT, 1, kGrouped, kDot>(a, sh.w, mode, shm, grid_y, s);
+      case 2: return launch_r<NT, 2, kGrouped, kDot>(a, sh.w, mode, shm, grid_y, s);
       default: return hipErrorInvalidValue;
     }
   }

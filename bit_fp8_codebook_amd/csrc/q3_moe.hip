@@ -16,48 +16,30 @@ __device__ __forceinline__ bool ranks_before(float a, int ia, float b, int ib) {
   return a > b || (a == b && ia < ib);
 }
 
-// One wave per token: every lane holds up to 16 logits; each round takes the
-// wave-wide best (highest logit, then lowest index) among those not yet taken.
-__global__ __launch_bounds__(64) void topk_kernel(const float* __restrict__ logits, int E, int topk,
-                                                  int32_t* __restrict__ ids) {
+// One block per token, one thread per expert: the token's logits go to LDS and
+// every thread counts the experts that rank before its own (higher logit, or
+// an equal logit at a lower index).  That count is the expert's rank, unique
+// per expert, so the threads with rank < topk write ids[rank] directly: no
+// sorting and no cross-thread reduction.
+__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ logits, int E, int topk,
+                                                    int32_t* __restrict__ ids) {
+  __shared__ float v[1024];
   const int t = blockIdx.x;
-  const int lane = threadIdx.x;
-  float v[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int e = lane + 64 * q;
-    v[q] = e < E ? logits[(int64_t)t * E + e] : 0.f;
-  }
-  uint32_t taken = 0u;
-  for (int r = 0; r < topk; ++r) {
-    float bv = -__builtin_inff();
-    int be = 0x7FFFFFFF;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int e = lane + 64 * q;
-      if (e < E && !((taken >> q) & 1u) && ranks_before(v[q], e, bv, be)) {
-        bv = v[q];
-        be = e;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oe = __shfl_xor(be, o, 64);
-      if (ranks_before(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if (lane == 0) ids[(int64_t)t * topk + r] = be;
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-  }
+  const int e = threadIdx.x;
+  const float mine = e < E ? logits[(int64_t)t * E + e] : 0.f;
+  if (e < E) v[e] = mine;
+  __syncthreads();
+  if (e >= E) return;
+  int rank = 0;
+  for (int o = 0; o < E; ++o) rank += ranks_before(v[o], o, mine, e) ? 1 : 0;
+  if (rank < topk) ids[(int64_t)t * topk + rank] = e;
 }
 
 }  // namespace
 
 hipError_t launch_moe_topk(const float* logits, int32_t t, int32_t e, int32_t topk, int32_t* ids, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)t), dim3(64), 0, s, logits, (int)e, (int)topk, ids);
+  const unsigned threads = (unsigned)((e + 63) / 64 * 64);
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)t), dim3(threads), 0, s, logits, (int)e, (int)topk, ids);
   return hipGetLastError();
 }
 

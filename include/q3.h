@@ -155,7 +155,8 @@ Q3_API q3_status q3_gemm_small_m(const q3_matrix* w, const uint16_t* x, int64_t 
  * "Expert sharing": a verify round reads the weights of each expert chosen by
  * at least one of its drafted tokens).  logits fp32 [t][num_experts] (row pitch num_experts) ->
  * topk_ids int32 [t][topk], highest logit first, ties to the lower expert
- * index.  1 <= topk <= num_experts <= 1024, t >= 1. */
+ * index.  1 <= topk <= num_experts <= 1024, t >= 1; logits must not be NaN
+ * (not checked).  One block per token ranks all experts at once. */
 Q3_API q3_status q3_moe_topk(const float* logits, int32_t t, int32_t num_experts, int32_t topk,
                              int32_t* topk_ids, void* stream);
 
