@@ -122,10 +122,10 @@ __device__ __forceinline__ void load_step(const Planes& p, const RowTile (&rt)[R
   for (int r = 0; r < R; ++r) {
     const uint32_t o = (live ? rt[r].vcode : kOob) + 3072u * sc;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) d.w[r][j] = bload128(p.code, o + js * j);
+    for (int j = 0; j < 3; ++j) d.w[r][j] = bload128_stream(p.code, o + js * j);
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) d.sc[r] = bload32(p.scale, (live ? rt[r].vscale : kOob) + 256u * sc);
+  for (int r = 0; r < R; ++r) d.sc[r] = bload32_stream(p.scale, (live ? rt[r].vscale : kOob) + 256u * sc);
 }
 
 __device__ __forceinline__ void dequant(const u32x4 (&w)[3], uint32_t sc, int t, uint32_t cbl, uint32_t cbh,
@@ -634,7 +634,11 @@ hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t
   constexpr int kSlice = kDot ? NT : 16 * NT;
   const size_t fk = full_k_bytes(tokens_in_slice, a.G);
   const bool full_k = fk <= (size_t)kFullKBudget;
+#if defined(Q3_FORCE_R) && defined(Q3_FORCE_W) && defined(Q3_FORCE_SK)
+  const Shape sh = pick_shape(a.n, a.G, full_k, tokens_in_slice, kDot);
+#else
   const Shape sh = kGrouped ? Shape{1, 4, 1} : pick_shape(a.n, a.G, full_k, tokens_in_slice, kDot);
+#endif
   a.sk = full_k ? sh.sk : 1;
   const int steps = (((a.G + 3) & ~3) + 15) / 16;
   while (a.sk > 1 && a.sk > steps) a.sk /= 2;   // every wave gets at least one step
