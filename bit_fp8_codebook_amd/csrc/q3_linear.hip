@@ -40,6 +40,7 @@
 // returns before reading any weight byte (Hibana page, "Adaptive speculation" /
 // "Expert sharing": a verify round reads every picked expert once).
 #include <atomic>
+#include <type_traits>
 
 #include "q3_device.h"
 #include "q3_internal.h"
@@ -52,7 +53,7 @@ constexpr int kFullKBudget = 96 * 1024;   // LDS bytes for full-K activation sta
 // How a block holds the activations.
 enum Mode : int {
   kShared = 0,   // all of K for all tokens, staged once per block
-  kStream = 1,   // one 512-k step at a time, double-buffered
+  kStream = 1,   // one 512-k step at a time, double-buffered through registers
 };
 constexpr uint32_t kRowPad = 16;          // LDS row padding against bank conflicts
 
@@ -71,6 +72,7 @@ struct KArgs {
   float* y;
   int64_t ldy;
   int m;          // dense: number of tokens
+  int vec_y;      // y rows 16-byte aligned: four consecutive outputs go out as one store
   int sk;         // K split over the waves of a block (full-K mode)
   const int32_t* ids;
   int pairs_total, topk, x_by_slot;
@@ -183,6 +185,81 @@ __device__ __forceinline__ void mfma_step(const StepData<R>& d, const RowTile (&
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int c = 0; c < MT; ++c) asm volatile("" : "+v"(acc[r][c]));
+}
+
+// Matrix-core step for one wave per SIMD holding many row tiles, software
+// pipelined: the step is a sequence of 4*R units (group t, row tile r), and
+// the vector-ALU dequantisation of unit u+1 is interleaved with the MFMAs of
+// unit u (one MFMA, then a few ALU instructions), so the matrix core does not
+// wait for the conversion.  The B operands of group t are held across its R
+// units; those of group t+1 are read from LDS during the last unit of group t,
+// each right after the MFMAs that last read the registers it replaces.  The
+// next step's kLoads memory loads are handed out a few per unit through
+// issue(integral_constant<Q>): a wave that issues them all at once stalls
+// until the memory pipeline has room, and with one wave per SIMD the matrix
+// core would stall with it.
+template <int Q, int Q1, typename Issue>
+__device__ __forceinline__ void issue_range(Issue& issue) {
+  if constexpr (Q < Q1) {
+    issue(std::integral_constant<int, Q>{});
+    issue_range<Q + 1, Q1>(issue);
+  }
+}
+
+template <int U, int MT, int R, int kLoads, typename Issue>
+__device__ __forceinline__ void pipe_unit(const StepData<R>& d, const RowTile (&rt)[R], const uint32_t (&xb)[MT],
+                                          const uint8_t* lds, f32x4 (&acc)[R][MT], bf16x8 (&b)[4][MT],
+                                          bf16x2 (&wv)[2][16], Issue& issue) {
+  constexpr int kUnits = 4 * R;
+  if constexpr (U < kUnits) {
+    constexpr int t = U / R, r = U % R, cur = U & 1;
+    constexpr int kMfma = 4 * MT;                     // MFMAs per unit
+    constexpr int kValu = (48 + kMfma - 1) / kMfma;   // ALU instructions after each of them
+    constexpr int q0 = U * kLoads / kUnits, q1 = (U + 1) * kLoads / kUnits;
+    issue_range<q0, q1>(issue);
+    if constexpr (U + 1 < kUnits) {
+      constexpr int t1 = (U + 1) / R, r1 = (U + 1) % R;
+      dequant(d.w[r1], d.sc[r1], t1, rt[r1].cbl, rt[r1].cbh, wv[cur ^ 1]);
+    }
+    constexpr bool refill = r == R - 1 && t < 3;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x8 a = pack_bf16x8(wv[cur][4 * e], wv[cur][4 * e + 1], wv[cur][4 * e + 2], wv[cur][4 * e + 3]);
+#pragma unroll
+      for (int c = 0; c < MT; ++c) acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[e][c], acc[r][c], 0, 0, 0);
+      if constexpr (refill) {
+#pragma unroll
+        for (int c = 0; c < MT; ++c)
+          b[e][c] = *reinterpret_cast<const bf16x8*>(lds + xb[c] + 64u * (t + 1) + 16u * e);
+      }
+    }
+    if constexpr (q1 > q0) __builtin_amdgcn_sched_group_barrier(0x020, q1 - q0, 0);   // this unit's loads first
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+      for (int c = 0; c < MT; ++c) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);   // then vector ALU work
+      }
+      if constexpr (refill) __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);   // this e's B reads for t+1
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pipe_unit<U + 1, MT, R, kLoads>(d, rt, xb, lds, acc, b, wv, issue);
+  }
+}
+
+template <int MT, int R, int kLoads, typename Issue>
+__device__ __forceinline__ void mfma_step_pipe(const StepData<R>& d, const RowTile (&rt)[R], const uint32_t (&xb)[MT],
+                                               const uint8_t* lds, f32x4 (&acc)[R][MT], Issue&& issue) {
+  bf16x8 b[4][MT];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int c = 0; c < MT; ++c) b[e][c] = *reinterpret_cast<const bf16x8*>(lds + xb[c] + 16u * e);
+  bf16x2 wv[2][16];
+  dequant(d.w[0], d.sc[0], 0, rt[0].cbl, rt[0].cbh, wv[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  pipe_unit<0, MT, R, kLoads>(d, rt, xb, lds, acc, b, wv, issue);
 }
 
 // Vector-ALU step for M tokens: xa[m] is the LDS byte address of token m's
@@ -372,7 +449,7 @@ void linear_kernel(KArgs a) {
       }
     };
 
-    if (kMode == kShared) {
+    if constexpr (kMode == kShared) {
       // Stage all activations: row j holds token j's K values (zero past K,
       // including the row's 16-byte pad, which lanes past a partial last
       // step's quads read with a zero scale); a 1 KB zero block follows.  The
@@ -532,10 +609,13 @@ void linear_kernel(KArgs a) {
             float* yr = a.y + (int64_t)yrow(j) * a.ldy;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
+              const int64_t row0 = (tile0 + r) * 16 + 4 * kb;
+              if (a.vec_y && row0 + 3 < a.n) {
+                *reinterpret_cast<f32x4*>(yr + row0) = acc[r][c];
+              } else {
 #pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                const int64_t row = (tile0 + r) * 16 + 4 * kb + v;
-                if (row < a.n) yr[row] = acc[r][c][v];
+                for (int v = 0; v < 4; ++v)
+                  if (row0 + v < a.n) yr[row0 + v] = acc[r][c][v];
               }
             }
           }
@@ -543,6 +623,152 @@ void linear_kernel(KArgs a) {
       }
     }
     __syncthreads();   // LDS is rewritten by the next slice
+  }
+}
+
+// Wide products: dense, 17..64 tokens per slice (2..4 column tiles), whole
+// 512-k steps.  One wave per SIMD (a block of 4 waves) owns kWideRows row
+// tiles, so each activation element staged in LDS meets kWideRows weight tiles
+// and a launch on a vocabulary-sized matrix has about one row group per SIMD
+// per round.  Activations stream through two LDS buffers with direct-to-LDS
+// loads (one load instruction moves one token's 1 KB step slice; lane l's 16
+// bytes land at 16*l), weights through two register sets, and the step's
+// matrix-core work is software-pipelined against the dequantisation.  Step
+// advances ride in scalar offsets, so the loop does no vector address work.
+#ifdef Q3_WIDE_ROWS
+constexpr int kWideRows = Q3_WIDE_ROWS;
+#else
+constexpr int kWideRows = 5;
+#endif
+#ifdef Q3_WIDE_MIN_NT
+constexpr int kWideMinNT = Q3_WIDE_MIN_NT;
+#else
+constexpr int kWideMinNT = 2;
+#endif
+constexpr int kWideWaves = 4;
+
+template <int NT>
+__global__ __launch_bounds__(64 * kWideWaves) __attribute__((amdgpu_waves_per_eu(1)))
+void wide_kernel(KArgs a) {
+  constexpr int R = kWideRows, kW = kWideWaves, kSlice = 16 * NT;
+  constexpr uint32_t rstride = 1024u + kRowPad;
+  constexpr uint32_t buf_bytes = (uint32_t)kSlice * rstride;
+  constexpr uint32_t zero_base = 2u * buf_bytes;
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 15, kb = lane >> 4;
+
+  const uint32_t gp = (uint32_t)a.G;   // a multiple of 16 here
+  const int64_t tiles = (a.n + 15) / 16;
+  const int64_t tile0 = ((int64_t)blockIdx.x * kW + wave) * R;
+  Planes p;
+  p.code = make_rsrc(a.code, (uint32_t)(tiles * 192 * gp));
+  p.scale = make_rsrc(a.scale, (uint32_t)(tiles * 16 * gp));
+  p.full_steps = p.steps = (int)(gp / 16);
+  p.q_last = 4;
+  const rsrc_t cbr = make_rsrc(a.cb, (uint32_t)(a.n * 8));
+  RowTile rt[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t T = tile0 + r;
+    const bool tile_ok = T < tiles;
+    rt[r].vcode = tile_ok ? (uint32_t)T * (192u * gp) + 16u * lane : kOob;
+    rt[r].vscale = tile_ok ? (uint32_t)T * (16u * gp) + 4u * lane : kOob;
+    const int64_t row = T * 16 + i;
+    const u32x2 cb = bload64(cbr, row < a.n ? (uint32_t)row * 8u : kOob);
+    rt[r].cbl = cb.x;
+    rt[r].cbh = cb.y;
+  }
+  const rsrc_t xr = make_rsrc(a.x, (uint32_t)((a.x_rows - 1) * a.ldx * 2 + (int64_t)a.G * 64));
+  const uint32_t ldx_bytes = (uint32_t)(a.ldx * 2);
+  const uint32_t lane16 = 16u * (uint32_t)lane;
+  if (tid < 64) *reinterpret_cast<u32x4*>(lds + zero_base + 16u * tid) = u32x4{0u, 0u, 0u, 0u};
+
+  for (int slice = 0; slice < a.m; slice += kSlice) {
+    const int cnt = a.m - slice < kSlice ? a.m - slice : kSlice;
+    uint32_t xb0[NT], xb1[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      const int j = 16 * c + i;
+      xb0[c] = (j < cnt ? (uint32_t)j * rstride : zero_base) + 256u * kb;
+      xb1[c] = (j < cnt ? buf_bytes + (uint32_t)j * rstride : zero_base) + 256u * kb;
+    }
+    f32x4 acc[R][NT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < NT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // The loads of step sn: weights into dst, activations into the LDS buffer
+    // at buf.  Every wave moves kSlice/kW activation rows per step; rows of
+    // absent tokens, and every load when sn is past the last step, read out
+    // of range (zeros, no memory traffic) and are never used.
+    constexpr int kLoads = 4 * R + kSlice / kW;
+    auto loads_of = [&](StepData<R>& dst, uint32_t buf, int sn) {
+      const bool live = sn < p.steps;
+      const uint32_t sc = (uint32_t)(live ? sn : p.steps - 1);
+      return [&, buf, live, sc](auto q) {
+        constexpr int Q = decltype(q)::value;
+        if constexpr (Q < 3 * R) {
+          constexpr int r = Q / 3, j = Q % 3;
+          dst.w[r][j] = __builtin_amdgcn_raw_buffer_load_b128(p.code, live ? rt[r].vcode + 1024u * j : kOob, 3072u * sc,
+                                                              Q3_STREAM_POLICY);
+        } else if constexpr (Q < 4 * R) {
+          constexpr int r = Q - 3 * R;
+          dst.sc[r] = __builtin_amdgcn_raw_buffer_load_b32(p.scale, live ? rt[r].vscale : kOob, 256u * sc,
+                                                           Q3_STREAM_POLICY);
+        } else {
+          const int j = wave + kW * (Q - 4 * R);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              xr, (__attribute__((address_space(3))) void*)(lds + buf + (uint32_t)j * rstride), 16,
+              live && j < cnt ? lane16 : kOob, (uint32_t)(slice + (j < cnt ? j : 0)) * ldx_bytes + 1024u * sc, 0, 0);
+        }
+      };
+    };
+    // Pairs of steps (A/B register sets, LDS buffers 0/1); an odd last step
+    // runs after the loop, so the loop has a single exit (an exit between the
+    // halves doubles the accumulators' register footprint).
+    StepData<R> A, B;
+    {
+      auto first = loads_of(A, 0u, 0);
+      issue_range<0, kLoads>(first);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int s = 0;
+    for (; s + 1 < p.steps; s += 2) {
+      mfma_step_pipe<NT, R, kLoads>(A, rt, xb0, lds, acc, loads_of(B, buf_bytes, s + 1));
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      mfma_step_pipe<NT, R, kLoads>(B, rt, xb1, lds, acc, loads_of(A, 0u, s + 2));
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    if (s < p.steps) mfma_step_pipe<NT, R, 0>(A, rt, xb0, lds, acc, [](auto) {});
+
+    // D layout: lane l holds rows 4*(l/16)+v (v = 0..3) of the tile for token l%16.
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      const int j = 16 * c + i;
+      if (j < cnt) {
+        float* yr = a.y + (int64_t)(slice + j) * a.ldy;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int64_t row0 = (tile0 + r) * 16 + 4 * kb;
+          if (a.vec_y && row0 + 3 < a.n) {
+            *reinterpret_cast<f32x4*>(yr + row0) = acc[r][c];
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (row0 + v < a.n) yr[row0 + v] = acc[r][c][v];
+          }
+        }
+      }
+    }
   }
 }
 
@@ -583,6 +809,23 @@ hipError_t launch_one(const KArgs& a, size_t shm, unsigned grid_y, hipStream_t s
   hipError_t e = allow_lds<NT, R, kW, kGrouped, kMode, kDot>(shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((linear_kernel<NT, R, kW, kGrouped, kMode, kDot>), grid, dim3(64 * kW), shm, s, a);
+  return hipGetLastError();
+}
+
+template <int NT>
+hipError_t launch_wide(const KArgs& a, hipStream_t s) {
+  constexpr int kRowsPerBlock = kWideRows * kWideWaves;
+  const size_t shm = stream_bytes(16 * NT);
+  static std::atomic<bool> allowed{false};
+  if (!allowed.load(std::memory_order_acquire)) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(wide_kernel<NT>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    allowed.store(true, std::memory_order_release);
+  }
+  const int64_t tiles = (a.n + 15) / 16;
+  const dim3 grid((unsigned)((tiles + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL((wide_kernel<NT>), grid, dim3(64 * kWideWaves), shm, s, a);
   return hipGetLastError();
 }
 
@@ -644,6 +887,13 @@ hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t
   while (a.sk > 1 && a.sk > steps) a.sk /= 2;   // every wave gets at least one step
   if (a.sk < 1 || a.sk > sh.w || sh.w % a.sk != 0) return hipErrorInvalidValue;
   const int mode = full_k ? kShared : kStream;
+#ifndef Q3_NO_WIDE
+  // Two or more column tiles of streamed activations on whole steps: the wide
+  // kernel (one wave per SIMD, many row tiles, activations loaded into LDS).
+  if constexpr (!kGrouped && !kDot && NT >= kWideMinNT) {
+    if (mode == kStream && a.G % 16 == 0) return launch_wide<NT>(a, s);
+  }
+#endif
   size_t shm = mode == kShared ? fk : stream_bytes(kSlice);
   if (mode != kStream && a.sk > 1) {
     const size_t red = reduce_bytes(kDot ? NT : 4 * NT, sh.r, sh.w);
@@ -682,6 +932,7 @@ hipError_t launch_gemm_small_m(const PlaneView& w, const uint16_t* x, int64_t m,
   a.ldy = ldy;
   a.m = (int)m;
   a.x_rows = m;
+  a.vec_y = ((uintptr_t)y % 16 == 0) && (ldy % 4 == 0);
   if (m <= 16) return launch_cfg<1, false, false>(a, (int)m, 1, s);
   if (m <= 32) return launch_cfg<2, false, false>(a, (int)m, 1, s);
   if (m <= 48) return launch_cfg<3, false, false>(a, (int)m, 1, s);
@@ -726,6 +977,7 @@ hipError_t launch_grouped(const ExpertView& w, const uint16_t* x, int64_t ldx, i
   a.pairs_total = t * topk;
   a.topk = topk;
   a.x_by_slot = x_by_slot;
+  a.vec_y = ((uintptr_t)y % 16 == 0) && (ldy % 4 == 0);
   a.x_rows = x_by_slot ? (int64_t)t * topk : t;
   const int slice = a.pairs_total < 16 ? a.pairs_total : 16;
   return launch_cfg<1, true, false>(a, slice, (unsigned)w.num_experts, s);

@@ -63,7 +63,8 @@ def test_gemv_parity(q3, n, k, m):
 
 MFMA_CASES = [(1024, 1024, 1), (4096, 4096, 1), (4096, 4096, 4), (4096, 4096, 8), (4096, 4096, 16),
               (100, 96, 3), (17, 32, 16), (333, 1024, 17), (200, 768, 33), (513, 2048, 64), (64, 8224, 5),
-              (2000, 8192, 16), (48, 4096, 48)]
+              (2000, 8192, 16), (48, 4096, 48), (77, 2048, 40), (250, 4096, 24), (1290, 3072, 64),
+              (300, 2080, 64)]
 
 
 @pytest.mark.parametrize("n,k,m", MFMA_CASES)
@@ -87,6 +88,21 @@ def test_strided_x_and_y(q3, fn):
     assert np.all(yb[:, 70:] == 7.0)
     y_ref, bound = oracle_linear(layer, x)
     assert_close(yb[:, :70], y_ref, bound, fn)
+
+
+@pytest.mark.parametrize("m", [16, 64])
+def test_aligned_y_ragged_rows(q3, m):
+    # y rows 16-byte aligned (four outputs per store) with a row count that ends
+    # inside a group of four: the last outputs go out one by one, the pad stays.
+    n, k = 1290, 2048
+    layer, x = synth.make_linear(n, k, m, seed=m + 1)
+    w = pack_layer(q3, layer)
+    ybig = torch.full((m, n + 6), 7.0, dtype=torch.float32, device="cuda")
+    q3.q3_gemm_small_m(w, dev(x), ybig[:, :n])
+    yb = ybig.cpu().numpy()
+    assert np.all(yb[:, n:] == 7.0)
+    y_ref, bound = oracle_linear(layer, x)
+    assert_close(yb[:, :n], y_ref, bound, f"aligned y m={m}")
 
 
 @pytest.mark.parametrize("fn,m", [("q3_gemv", 1), ("q3_gemv", 8), ("q3_gemm_small_m", 16), ("q3_gemm_small_m", 64)])
