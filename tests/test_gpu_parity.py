@@ -180,6 +180,20 @@ def test_config4_full_size_sampled_rows(q3):
     assert_close(y[:, rows], y_ref, bound, "config 4")
 
 
+@pytest.mark.parametrize("n,k,m", [(90000, 1024, 64), (90000, 1536, 40), (90000, 2048, 33)])
+def test_many_row_groups_sampled_rows(q3, n, k, m):
+    # More row groups than a launch has blocks: blocks walk several groups;
+    # with an even step count a group's first step is loaded during the
+    # previous group's last one.
+    layer, x = synth.make_linear(n, k, m, seed=k + m)
+    w = pack_layer(q3, layer)
+    y = q3.q3_gemm_small_m(w, dev(x)).cpu().numpy()
+    rng = np.random.default_rng(k)
+    rows = np.sort(np.concatenate([rng.choice(n, 120, replace=False), [0, 15, 16, 81919, 81920, n - 1]]))
+    y_ref, bound = oracle_linear(layer, x, rows=rows)
+    assert_close(y[:, rows], y_ref, bound, f"n={n} k={k} m={m}")
+
+
 @pytest.mark.parametrize("m", [1, 4, 8])
 def test_config1_full_gemv_and_mfma(q3, m):
     layer, x = synth.make_linear(4096, 4096, m, seed=0)
