@@ -14,6 +14,10 @@ Distributions (one per tensor, all seeded):
                 integers -10..-4 (a power-of-two scale per 32-weight group)
   * x:          uint16 [m][k], bf16 bit patterns of N(0,1) draws (RNE)
   * logits:     float32 [t][E], N(0,1) (MoE router scores)
+  Two-bit draft head (make_head): codes uniform over 0..3, a 4-entry E4M3FN
+  codebook per row from N(0,1), scales as above; the FP8 head's elements are
+  N(0,1) draws rounded to E4M3FN with one scale byte per 32 drawn like the
+  group scales; the two heads are drawn independently.
 
 Each tensor gets its own child stream of numpy's PCG64, spawned from
 SeedSequence(seed) in a fixed order, so a tensor never depends on the shape
@@ -127,3 +131,27 @@ def digest(*arrays) -> str:
         h.update(str(a.shape).encode())
         h.update(a.tobytes())
     return h.hexdigest()[:16]
+
+
+@dataclass
+class Head:
+    """A two-bit draft head and its FP8 (MXFP8) counterpart, unpacked.
+    w2[n][k] = E4M3(cb4[n][codes[n][k]]) * 2^(scales[n][k/32]-127);
+    w8[n][k] = E4M3(e8[n][k]) * 2^(s8[n][k/32]-127)."""
+    n: int
+    k: int
+    codes: np.ndarray      # uint8 [n][k], 0..3
+    codebook: np.ndarray   # uint8 [n][4]
+    scales: np.ndarray     # uint8 [n][k/32]
+    e8: np.ndarray         # uint8 [n][k]
+    s8: np.ndarray         # uint8 [n][k/32]
+
+
+def make_head(n: int, k: int, m: int, seed: int = 0):
+    """A draft head and bf16 activations x[m][k]; streams in the order codes,
+    codebook, scales, FP8 elements, FP8 scales, x."""
+    rs = _streams(seed, 6)
+    head = Head(n, k, rs[0].integers(0, 4, size=(n, k), dtype=np.uint8),
+                round_to_e4m3fn_bytes(rs[1].standard_normal((n, 4))), draw_scales(rs[2], n, k),
+                round_to_e4m3fn_bytes(rs[3].standard_normal((n, k))), draw_scales(rs[4], n, k))
+    return head, draw_x(rs[5], m, k)
