@@ -31,6 +31,11 @@ class Q3Matrix(ctypes.Structure):
     _fields_ = [("n", c_i64), ("k", c_i64), ("code_plane", c_vp), ("scale_plane", c_vp), ("codebook", c_vp)]
 
 
+class Q3Mxfp8Matrix(ctypes.Structure):
+    _fields_ = [("n", c_i64), ("k", c_i64), ("elements", c_vp), ("ld_elements", c_i64), ("scales", c_vp),
+                ("ld_scales", c_i64)]
+
+
 class Q3ExpertStack(ctypes.Structure):
     _fields_ = [("num_experts", c_i64), ("n", c_i64), ("k", c_i64),
                 ("code_plane", c_vp), ("code_expert_stride", c_i64),
@@ -49,6 +54,17 @@ SIGNATURES = {
     "q3_moe_topk": (ctypes.c_int, [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "q3_grouped_expert_gemv": (ctypes.c_int, [ctypes.POINTER(Q3ExpertStack), c_vp, c_i64, c_i32, c_vp, c_i32,
                                               c_i32, c_vp, c_i64, c_vp]),
+    "q3_layout2": (ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(Q3LayoutInfo)]),
+    "q3_pack2": (ctypes.c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp]),
+    "q3_unpack2": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), c_vp, c_vp, c_vp]),
+    "q3_head2_scores": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), c_vp, c_i64, c_i64, c_vp, c_i64, c_vp]),
+    "q3_shortlist_workspace_bytes": (c_i64, [c_i64]),
+    "q3_shortlist": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
+    "q3_rescore_fp8": (ctypes.c_int, [ctypes.POINTER(Q3Mxfp8Matrix), c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp,
+                                      c_vp]),
+    "q3_draft_head_workspace_bytes": (c_i64, [c_i64, c_i64]),
+    "q3_draft_head": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), ctypes.POINTER(Q3Mxfp8Matrix), c_vp, c_i64, c_i64,
+                                     c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
 }
 
 STATUS = {0: "Q3_OK", 1: "Q3_ERR_INVALID_ARG", 2: "Q3_ERR_UNSUPPORTED_SHAPE", 3: "Q3_ERR_MISALIGNED",
@@ -87,6 +103,12 @@ def _check(fn, status):
 
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ld(t: torch.Tensor) -> int:
+    """Row pitch in elements of a 2-D tensor with contiguous rows; a single row's
+    pitch is meaningless to torch (it may report 0), so pass the row length."""
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
 
 
 def _dev(t: torch.Tensor, name: str):
@@ -140,7 +162,7 @@ def q3_pack(codes: torch.Tensor, scales: torch.Tensor, codebook: torch.Tensor, o
         raise ValueError("codes and scales rows must be contiguous")
     w = out if out is not None else empty_packed(n, k, codes.device)
     w.codebook.copy_(codebook)
-    _check("q3_pack", lib().q3_pack(codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0), n, k,
+    _check("q3_pack", lib().q3_pack(codes.data_ptr(), _ld(codes), scales.data_ptr(), _ld(scales), n, k,
                                     w.code_plane.data_ptr(), w.scale_plane.data_ptr(), _stream(codes)))
     return w
 
@@ -177,7 +199,7 @@ def q3_gemv(w: PackedMatrix, x: torch.Tensor, y: torch.Tensor = None) -> torch.T
     m = x.shape[0]
     y = _out(y, m, w.n, x.device)
     d = w.desc()
-    _check("q3_gemv", lib().q3_gemv(ctypes.byref(d), x.data_ptr(), m, x.stride(0), y.data_ptr(), y.stride(0),
+    _check("q3_gemv", lib().q3_gemv(ctypes.byref(d), x.data_ptr(), m, _ld(x), y.data_ptr(), _ld(y),
                                     _stream(x)))
     return y
 
@@ -188,8 +210,8 @@ def q3_gemm_small_m(w: PackedMatrix, x: torch.Tensor, y: torch.Tensor = None) ->
     m = x.shape[0]
     y = _out(y, m, w.n, x.device)
     d = w.desc()
-    _check("q3_gemm_small_m", lib().q3_gemm_small_m(ctypes.byref(d), x.data_ptr(), m, x.stride(0), y.data_ptr(),
-                                                    y.stride(0), _stream(x)))
+    _check("q3_gemm_small_m", lib().q3_gemm_small_m(ctypes.byref(d), x.data_ptr(), m, _ld(x), y.data_ptr(),
+                                                    _ld(y), _stream(x)))
     return y
 
 
@@ -250,6 +272,130 @@ def q3_grouped_expert_gemv(stack: ExpertStack, x: torch.Tensor, topk_ids: torch.
     y = _out(y, t * topk, stack.n, x.device)
     d = stack.desc()
     _check("q3_grouped_expert_gemv",
-           lib().q3_grouped_expert_gemv(ctypes.byref(d), x.data_ptr(), x.stride(0), 1 if x_by_slot else 0,
-                                        topk_ids.data_ptr(), t, topk, y.data_ptr(), y.stride(0), _stream(x)))
+           lib().q3_grouped_expert_gemv(ctypes.byref(d), x.data_ptr(), _ld(x), 1 if x_by_slot else 0,
+                                        topk_ids.data_ptr(), t, topk, y.data_ptr(), _ld(y), _stream(x)))
     return y
+
+
+# ------------------------------------------------------- two-bit draft head
+
+def q3_layout2(n: int, k: int) -> dict:
+    info = Q3LayoutInfo()
+    _check("q3_layout2", lib().q3_layout2(n, k, ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in Q3LayoutInfo._fields_}
+
+
+@dataclass
+class PackedHead2:
+    """Device-resident 2-bit copy of a draft head (planes as uint8 tensors, codebook [n][4])."""
+    n: int
+    k: int
+    code_plane: torch.Tensor
+    scale_plane: torch.Tensor
+    codebook: torch.Tensor
+
+    def desc(self) -> Q3Matrix:
+        return Q3Matrix(self.n, self.k, self.code_plane.data_ptr(), self.scale_plane.data_ptr(),
+                        self.codebook.data_ptr())
+
+    @property
+    def payload_bytes(self) -> int:
+        return self.n * self.k * 9 // 32
+
+
+@dataclass
+class Mxfp8Head:
+    """The FP8 (MXFP8) head: elements uint8 [n][k] E4M3FN, scales uint8 [n][k/32] E8M0."""
+    n: int
+    k: int
+    elements: torch.Tensor
+    scales: torch.Tensor
+
+    def desc(self) -> Q3Mxfp8Matrix:
+        return Q3Mxfp8Matrix(self.n, self.k, self.elements.data_ptr(), _ld(self.elements),
+                             self.scales.data_ptr(), _ld(self.scales))
+
+
+def q3_pack2(codes: torch.Tensor, scales: torch.Tensor, codebook: torch.Tensor) -> PackedHead2:
+    """codes uint8 [n][k] (0..3), scales uint8 [n][k/32], codebook uint8 [n][4] -> PackedHead2."""
+    _dev(codes, "codes"), _dev(scales, "scales"), _dev(codebook, "codebook")
+    n, k = codes.shape
+    if codes.stride(1) != 1 or scales.stride(1) != 1:
+        raise ValueError("codes and scales rows must be contiguous")
+    L = q3_layout2(n, k)
+    w = PackedHead2(n, k, torch.empty(L["code_plane_bytes"], dtype=torch.uint8, device=codes.device),
+                    torch.empty(L["scale_plane_bytes"], dtype=torch.uint8, device=codes.device),
+                    codebook.contiguous().clone())
+    _check("q3_pack2", lib().q3_pack2(codes.data_ptr(), _ld(codes), scales.data_ptr(), _ld(scales), n, k,
+                                      w.code_plane.data_ptr(), w.scale_plane.data_ptr(), _stream(codes)))
+    return w
+
+
+def q3_unpack2(w: PackedHead2):
+    codes = torch.empty((w.n, w.k), dtype=torch.uint8, device=w.code_plane.device)
+    scales = torch.empty((w.n, w.k // 32), dtype=torch.uint8, device=w.code_plane.device)
+    d = w.desc()
+    _check("q3_unpack2", lib().q3_unpack2(ctypes.byref(d), codes.data_ptr(), scales.data_ptr(),
+                                          _stream(w.code_plane)))
+    return codes, scales
+
+
+def q3_head2_scores(w: PackedHead2, x: torch.Tensor, y: torch.Tensor = None) -> torch.Tensor:
+    """2-bit scores of every row: y[m][n] = x[m] . w2[n], m <= 16."""
+    x = _tokens(x, w.k)
+    m = x.shape[0]
+    y = _out(y, m, w.n, x.device)
+    d = w.desc()
+    _check("q3_head2_scores", lib().q3_head2_scores(ctypes.byref(d), x.data_ptr(), m, _ld(x), y.data_ptr(),
+                                                    _ld(y), _stream(x)))
+    return y
+
+
+def q3_shortlist(scores: torch.Tensor, size: int = 16, workspace: torch.Tensor = None):
+    """Per query the `size` rows with the largest scores (ties to the lower row) -> (ids int32, vals fp32)."""
+    _dev(scores, "scores")
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be float32 [m][n] with contiguous rows")
+    m, n = scores.shape
+    if workspace is None:
+        workspace = torch.empty(lib().q3_shortlist_workspace_bytes(m), dtype=torch.uint8, device=scores.device)
+    ids = torch.empty((m, size), dtype=torch.int32, device=scores.device)
+    vals = torch.empty((m, size), dtype=torch.float32, device=scores.device)
+    _check("q3_shortlist", lib().q3_shortlist(scores.data_ptr(), m, n, _ld(scores), size, workspace.data_ptr(),
+                                              ids.data_ptr(), vals.data_ptr(), _stream(scores)))
+    return ids, vals
+
+
+def q3_rescore_fp8(h: Mxfp8Head, x: torch.Tensor, ids: torch.Tensor):
+    """FP8 scores of listed rows and the decision -> (y8 fp32 [m][size], best int32 [m])."""
+    x = _tokens(x, h.k)
+    _dev(ids, "ids")
+    if ids.dtype != torch.int32 or not ids.is_contiguous():
+        raise ValueError("ids must be contiguous int32 [m][size]")
+    m, size = ids.shape
+    y = torch.empty((m, size), dtype=torch.float32, device=x.device)
+    best = torch.empty(m, dtype=torch.int32, device=x.device)
+    d = h.desc()
+    _check("q3_rescore_fp8", lib().q3_rescore_fp8(ctypes.byref(d), x.data_ptr(), m, _ld(x), ids.data_ptr(), size,
+                                                  y.data_ptr(), best.data_ptr(), _stream(x)))
+    return y, best
+
+
+def draft_head_workspace(m: int, n: int, device) -> torch.Tensor:
+    return torch.empty(lib().q3_draft_head_workspace_bytes(m, n), dtype=torch.uint8, device=device)
+
+
+def q3_draft_head(w2: PackedHead2, h: Mxfp8Head, x: torch.Tensor, size: int = 16, workspace: torch.Tensor = None):
+    """2-bit shortlist, FP8 rescoring and decision -> (ids int32 [m][size], y8 fp32 [m][size], best int32 [m])."""
+    x = _tokens(x, w2.k)
+    m = x.shape[0]
+    if workspace is None:
+        workspace = draft_head_workspace(m, w2.n, x.device)
+    ids = torch.empty((m, size), dtype=torch.int32, device=x.device)
+    y8 = torch.empty((m, size), dtype=torch.float32, device=x.device)
+    best = torch.empty(m, dtype=torch.int32, device=x.device)
+    d2, d8 = w2.desc(), h.desc()
+    _check("q3_draft_head", lib().q3_draft_head(ctypes.byref(d2), ctypes.byref(d8), x.data_ptr(), m, _ld(x),
+                                                size, workspace.data_ptr(), ids.data_ptr(), y8.data_ptr(),
+                                                best.data_ptr(), _stream(x)))
+    return ids, y8, best

@@ -17,6 +17,7 @@ int64_t padded_groups(int64_t k) { return (k / kGroup + 3) / 4 * 4; }
 int64_t tiles_of(int64_t n) { return (n + 15) / 16; }
 int64_t code_plane_bytes(int64_t n, int64_t k) { return tiles_of(n) * 192 * padded_groups(k); }
 int64_t scale_plane_bytes(int64_t n, int64_t k) { return tiles_of(n) * 16 * padded_groups(k); }
+int64_t code_plane_bytes2(int64_t n, int64_t k) { return tiles_of(n) * 128 * padded_groups(k); }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -37,6 +38,31 @@ q3_status check_planes(int64_t n, int64_t k, const void* code, const void* scale
   if (code_plane_bytes(n, k) > kMaxPlaneBytes || n * 8 > kMaxPlaneBytes) return Q3_ERR_UNSUPPORTED_SHAPE;
   return Q3_OK;
 }
+
+// The two-bit draft head's planes: 4-byte codebook rows.
+q3_status check_planes2(int64_t n, int64_t k, const void* code, const void* scale, const void* cb) {
+  q3_status st = check_shape(n, k);
+  if (st != Q3_OK) return st;
+  if (n > 0 && (!code || !scale || !cb)) return Q3_ERR_INVALID_ARG;
+  if (!aligned(code, 16) || !aligned(scale, 4) || !aligned(cb, 4)) return Q3_ERR_MISALIGNED;
+  if (code_plane_bytes2(n, k) > kMaxPlaneBytes || n * 4 > kMaxPlaneBytes) return Q3_ERR_UNSUPPORTED_SHAPE;
+  return Q3_OK;
+}
+
+q3_status check_mxfp8(const q3_mxfp8_matrix* h) {
+  if (!h) return Q3_ERR_INVALID_ARG;
+  q3_status st = check_shape(h->n, h->k);
+  if (st != Q3_OK) return st;
+  if (h->n < 1 || !h->elements || !h->scales) return Q3_ERR_INVALID_ARG;
+  if (h->ld_elements < h->k || h->ld_scales < h->k / kGroup) return Q3_ERR_INVALID_ARG;
+  if (h->ld_elements % 16 || !aligned(h->elements, 16)) return Q3_ERR_MISALIGNED;
+  if (h->n * h->ld_elements > kMaxPlaneBytes || h->n * h->ld_scales > kMaxPlaneBytes) return Q3_ERR_UNSUPPORTED_SHAPE;
+  return Q3_OK;
+}
+
+constexpr int64_t kShortlistPairBytes = 8;   // (score, row)
+int64_t shortlist_ws(int64_t m) { return m * q3::kShortlistChunks * q3::kShortlistMax * kShortlistPairBytes; }
+int64_t align8(int64_t b) { return (b + 7) / 8 * 8; }
 
 q3_status check_matrix(const q3_matrix* w) {
   if (!w) return Q3_ERR_INVALID_ARG;
@@ -126,7 +152,7 @@ Q3_API q3_status q3_pack(const uint8_t* codes, int64_t ldc, const uint8_t* scale
   if (code_plane_bytes(n, k) > kMaxPlaneBytes) return Q3_ERR_UNSUPPORTED_SHAPE;
   if ((st = check_device()) != Q3_OK) return st;
   return from_hip(q3::launch_pack(codes, ldc, scale_bytes, lds, n, k, static_cast<uint8_t*>(code_plane),
-                                  static_cast<uint8_t*>(scale_plane), static_cast<hipStream_t>(stream)));
+                                  static_cast<uint8_t*>(scale_plane), static_cast<hipStream_t>(stream), 3));
 }
 
 Q3_API q3_status q3_unpack(const q3_matrix* w, uint8_t* codes_out, uint8_t* scale_out, void* stream) {
@@ -135,7 +161,7 @@ Q3_API q3_status q3_unpack(const q3_matrix* w, uint8_t* codes_out, uint8_t* scal
   if (w->n > 0 && (!codes_out || !scale_out)) return Q3_ERR_INVALID_ARG;
   if (!aligned(codes_out, 4)) return Q3_ERR_MISALIGNED;
   if ((st = check_device()) != Q3_OK) return st;
-  return from_hip(q3::launch_unpack(view_of(w), codes_out, scale_out, static_cast<hipStream_t>(stream)));
+  return from_hip(q3::launch_unpack(view_of(w), codes_out, scale_out, static_cast<hipStream_t>(stream), 3));
 }
 
 Q3_API q3_status q3_gemv(const q3_matrix* w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
@@ -197,6 +223,114 @@ Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t
   v.num_experts = static_cast<int32_t>(w->num_experts);
   return from_hip(q3::launch_grouped(v, x, ldx, x_by_slot, topk_ids, t, topk, y, ldy,
                                      static_cast<hipStream_t>(stream)));
+}
+
+Q3_API q3_status q3_layout2(int64_t n, int64_t k, q3_layout_info* out) {
+  if (!out) return Q3_ERR_INVALID_ARG;
+  q3_status st = check_shape(n, k);
+  if (st != Q3_OK) return st;
+  out->n = n;
+  out->k = k;
+  out->groups = k / kGroup;
+  out->padded_groups = padded_groups(k);
+  out->tiles = tiles_of(n);
+  out->code_tile_bytes = 128 * out->padded_groups;
+  out->scale_tile_bytes = 16 * out->padded_groups;
+  out->code_plane_bytes = code_plane_bytes2(n, k);
+  out->scale_plane_bytes = scale_plane_bytes(n, k);
+  out->codebook_bytes = 4 * n;
+  out->payload_bytes = n * (k / kGroup) * 9;
+  return Q3_OK;
+}
+
+Q3_API q3_status q3_pack2(const uint8_t* codes, int64_t ldc, const uint8_t* scale_bytes, int64_t lds, int64_t n,
+                          int64_t k, void* code_plane, void* scale_plane, void* stream) {
+  q3_status st = check_shape(n, k);
+  if (st != Q3_OK) return st;
+  if (n > 0 && (!codes || !scale_bytes || !code_plane || !scale_plane)) return Q3_ERR_INVALID_ARG;
+  if (ldc < k || lds < k / kGroup) return Q3_ERR_INVALID_ARG;
+  if (!aligned(code_plane, 16) || !aligned(scale_plane, 4)) return Q3_ERR_MISALIGNED;
+  if (code_plane_bytes2(n, k) > kMaxPlaneBytes) return Q3_ERR_UNSUPPORTED_SHAPE;
+  if ((st = check_device()) != Q3_OK) return st;
+  return from_hip(q3::launch_pack(codes, ldc, scale_bytes, lds, n, k, static_cast<uint8_t*>(code_plane),
+                                  static_cast<uint8_t*>(scale_plane), static_cast<hipStream_t>(stream), 2));
+}
+
+Q3_API q3_status q3_unpack2(const q3_matrix* w, uint8_t* codes_out, uint8_t* scale_out, void* stream) {
+  if (!w) return Q3_ERR_INVALID_ARG;
+  q3_status st = check_planes2(w->n, w->k, w->code_plane, w->scale_plane, w->codebook);
+  if (st != Q3_OK) return st;
+  if (w->n > 0 && (!codes_out || !scale_out)) return Q3_ERR_INVALID_ARG;
+  if (!aligned(codes_out, 4)) return Q3_ERR_MISALIGNED;
+  if ((st = check_device()) != Q3_OK) return st;
+  return from_hip(q3::launch_unpack(view_of(w), codes_out, scale_out, static_cast<hipStream_t>(stream), 2));
+}
+
+Q3_API q3_status q3_head2_scores(const q3_matrix* w2, const uint16_t* x, int64_t m, int64_t ldx, float* y,
+                                 int64_t ldy, void* stream) {
+  if (!w2) return Q3_ERR_INVALID_ARG;
+  q3_status st = check_planes2(w2->n, w2->k, w2->code_plane, w2->scale_plane, w2->codebook);
+  if (st != Q3_OK) return st;
+  if ((st = check_tokens(w2->k, w2->n, x, m, ldx, y, ldy, 16)) != Q3_OK) return st;
+  if ((st = check_device()) != Q3_OK) return st;
+  return from_hip(q3::launch_head2_scores(view_of(w2), x, m, ldx, y, ldy, static_cast<hipStream_t>(stream)));
+}
+
+Q3_API int64_t q3_shortlist_workspace_bytes(int64_t m) { return m < 1 ? 0 : shortlist_ws(m); }
+
+Q3_API q3_status q3_shortlist(const float* scores, int64_t m, int64_t n, int64_t ld, int32_t size, void* workspace,
+                              int32_t* ids, float* vals, void* stream) {
+  if (!scores || !workspace || !ids) return Q3_ERR_INVALID_ARG;
+  if (m < 1 || m > 65535 || n < 1 || n > 0x7FFFFFFF || size < 1 || size > q3::kShortlistMax || size > n)
+    return Q3_ERR_UNSUPPORTED_SHAPE;
+  if (ld < n) return Q3_ERR_INVALID_ARG;
+  if (!aligned(scores, 4) || !aligned(workspace, 8) || !aligned(ids, 4) || !aligned(vals, 4)) return Q3_ERR_MISALIGNED;
+  q3_status st = check_device();
+  if (st != Q3_OK) return st;
+  return from_hip(q3::launch_shortlist(scores, m, n, ld, size, workspace, ids, vals, static_cast<hipStream_t>(stream)));
+}
+
+Q3_API q3_status q3_rescore_fp8(const q3_mxfp8_matrix* w8, const uint16_t* x, int64_t m, int64_t ldx,
+                                const int32_t* ids, int32_t size, float* y, int32_t* best, void* stream) {
+  q3_status st = check_mxfp8(w8);
+  if (st != Q3_OK) return st;
+  if (m < 1 || m > 65535 || size < 1 || size > q3::kShortlistMax) return Q3_ERR_UNSUPPORTED_SHAPE;
+  if (!x || !ids || !y || !best) return Q3_ERR_INVALID_ARG;
+  if (ldx < w8->k) return Q3_ERR_INVALID_ARG;
+  if (ldx % 8 || !aligned(x, 16) || !aligned(ids, 4) || !aligned(y, 4) || !aligned(best, 4)) return Q3_ERR_MISALIGNED;
+  if ((st = check_device()) != Q3_OK) return st;
+  q3::Mxfp8View h{static_cast<const uint8_t*>(w8->elements), w8->ld_elements, static_cast<const uint8_t*>(w8->scales),
+                  w8->ld_scales, w8->n, w8->k};
+  return from_hip(q3::launch_rescore(h, x, m, ldx, ids, size, y, best, static_cast<hipStream_t>(stream)));
+}
+
+Q3_API int64_t q3_draft_head_workspace_bytes(int64_t m, int64_t n) {
+  return m < 1 || n < 1 ? 0 : align8(m * n * 4) + shortlist_ws(m);
+}
+
+Q3_API q3_status q3_draft_head(const q3_matrix* w2, const q3_mxfp8_matrix* w8, const uint16_t* x, int64_t m,
+                               int64_t ldx, int32_t size, void* workspace, int32_t* ids, float* y8, int32_t* best,
+                               void* stream) {
+  if (!w2) return Q3_ERR_INVALID_ARG;
+  q3_status st = check_planes2(w2->n, w2->k, w2->code_plane, w2->scale_plane, w2->codebook);
+  if (st != Q3_OK) return st;
+  if ((st = check_mxfp8(w8)) != Q3_OK) return st;
+  if (w8->n != w2->n || w8->k != w2->k) return Q3_ERR_INVALID_ARG;
+  if (!workspace || !ids || !y8 || !best) return Q3_ERR_INVALID_ARG;
+  if (size < 1 || size > q3::kShortlistMax || size > w2->n || w2->n > 0x7FFFFFFF) return Q3_ERR_UNSUPPORTED_SHAPE;
+  float* scores = static_cast<float*>(workspace);
+  if ((st = check_tokens(w2->k, w2->n, x, m, ldx, scores, w2->n, 16)) != Q3_OK) return st;
+  if (!aligned(workspace, 8) || !aligned(ids, 4) || !aligned(y8, 4) || !aligned(best, 4)) return Q3_ERR_MISALIGNED;
+  if ((st = check_device()) != Q3_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = q3::launch_head2_scores(view_of(w2), x, m, ldx, scores, w2->n, s);
+  if (e == hipSuccess)
+    e = q3::launch_shortlist(scores, m, w2->n, w2->n, size, static_cast<uint8_t*>(workspace) + align8(m * w2->n * 4),
+                             ids, nullptr, s);
+  q3::Mxfp8View h{static_cast<const uint8_t*>(w8->elements), w8->ld_elements, static_cast<const uint8_t*>(w8->scales),
+                  w8->ld_scales, w8->n, w8->k};
+  if (e == hipSuccess) e = q3::launch_rescore(h, x, m, ldx, ids, size, y8, best, s);
+  return from_hip(e);
 }
 
 }  // extern "C"

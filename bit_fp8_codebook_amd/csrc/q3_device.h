@@ -71,6 +71,36 @@ __device__ __forceinline__ void dequant_group_bf16(uint32_t d0, uint32_t d1, uin
   }
 }
 
+// Two-bit draft-head groups (the head's 2-bit copy, "Two-bit draft head"):
+// 32 codes in two words, byte b of word j holding code 16j+4q+b in bits
+// 2q..2q+1, looked up in the row's 4-entry codebook (one word, entry j in
+// byte j).  Selector 4j+q = (word j >> 2q) & 0x03 per byte: the codes of
+// weights 16j+4q .. 16j+4q+3.  7 ALU ops per word.
+__device__ __forceinline__ void unpack_selectors2(uint32_t d0, uint32_t d1, uint32_t (&s)[8]) {
+  const uint32_t m2 = 0x03030303u;
+  s[0] = d0 & m2;
+  s[1] = (d0 >> 2) & m2;
+  s[2] = (d0 >> 4) & m2;
+  s[3] = (d0 >> 6) & m2;
+  s[4] = d1 & m2;
+  s[5] = (d1 >> 2) & m2;
+  s[6] = (d1 >> 4) & m2;
+  s[7] = (d1 >> 6) & m2;
+}
+
+__device__ __forceinline__ void dequant_group2_bf16(uint32_t d0, uint32_t d1, uint32_t sbyte, uint32_t cb4,
+                                                    bf16x2 (&w)[16]) {
+  uint32_t sel[8];
+  unpack_selectors2(d0, d1, sel);
+  const float sc = e8m0_to_f32(sbyte);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t q = __builtin_amdgcn_perm(0u, cb4, sel[i]);   // selector bytes 0..3 pick bytes of cb4
+    w[2 * i] = fp8x2_to_bf16x2(q, sc, false);
+    w[2 * i + 1] = fp8x2_to_bf16x2(q, sc, true);
+  }
+}
+
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
 
 // Tile-major placement of the planes (rows in tiles of 16, a row's groups in
@@ -86,6 +116,13 @@ __device__ __forceinline__ int64_t code_word_offset(int64_t r, uint32_t g, uint3
   const uint32_t i = (uint32_t)(r & 15), s = g >> 4, kb = (g >> 2) & 3u, t = g & 3u;
   const uint32_t q = step_quads(s, gp);
   return (r >> 4) * (int64_t)(192u * gp) + 3072u * s + 16u * (16u * (q * j + kb) + i) + 4u * t;
+}
+// The 2-bit head's planes: two words per group, so a tile is 128*Gp bytes and
+// a full step 2048; the piece rule inside a step is the same.
+__device__ __forceinline__ int64_t code_word_offset2(int64_t r, uint32_t g, uint32_t j, uint32_t gp) {
+  const uint32_t i = (uint32_t)(r & 15), s = g >> 4, kb = (g >> 2) & 3u, t = g & 3u;
+  const uint32_t q = step_quads(s, gp);
+  return (r >> 4) * (int64_t)(128u * gp) + 2048u * s + 16u * (16u * (q * j + kb) + i) + 4u * t;
 }
 __device__ __forceinline__ int64_t scale_byte_offset(int64_t r, uint32_t g, uint32_t gp) {
   const uint32_t i = (uint32_t)(r & 15), s = g >> 4, kb = (g >> 2) & 3u, t = g & 3u;

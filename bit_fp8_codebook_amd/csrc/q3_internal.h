@@ -15,9 +15,10 @@ struct PlaneView {
   int32_t groups;         // k / 32
 };
 
+// bits = 3 (the 3.25-bit layer) or 2 (the two-bit draft head).
 hipError_t launch_pack(const uint8_t* codes, int64_t ldc, const uint8_t* scales, int64_t lds, int64_t n,
-                       int64_t k, uint8_t* code_plane, uint8_t* scale_plane, hipStream_t s);
-hipError_t launch_unpack(const PlaneView& w, uint8_t* codes, uint8_t* scales, hipStream_t s);
+                       int64_t k, uint8_t* code_plane, uint8_t* scale_plane, hipStream_t s, int bits);
+hipError_t launch_unpack(const PlaneView& w, uint8_t* codes, uint8_t* scales, hipStream_t s, int bits);
 
 // VALU path, 1 <= m <= 8.
 hipError_t launch_gemv(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
@@ -26,6 +27,29 @@ hipError_t launch_gemv(const PlaneView& w, const uint16_t* x, int64_t m, int64_t
 // MFMA path, 1 <= m <= 64.
 hipError_t launch_gemm_small_m(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y,
                                int64_t ldy, hipStream_t s);
+
+// Two-bit draft head: scores of every row for 1 <= m <= 16 queries (matrix cores).
+hipError_t launch_head2_scores(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
+                               hipStream_t s);
+
+// Shortlist: per query the `size` largest of n fp32 scores (ties to the lower
+// row), in two launches through `cand` (m * kShortlistChunks * size pairs).
+constexpr int kShortlistMax = 16;
+constexpr int kShortlistChunks = 64;
+hipError_t launch_shortlist(const float* scores, int64_t m, int64_t n, int64_t ld, int32_t size, void* cand,
+                            int32_t* ids, float* vals, hipStream_t s);
+
+// MXFP8 rows gathered by ids: y[i][j] = x[i] . w8[ids[i][j]]; best[i] = the
+// listed row with the largest y (ties to the lower row).
+struct Mxfp8View {
+  const uint8_t* e8;   // [n][lde] E4M3FN
+  int64_t lde;
+  const uint8_t* s8;   // [n][lds] E8M0, one per 32 elements
+  int64_t lds;
+  int64_t n, k;
+};
+hipError_t launch_rescore(const Mxfp8View& h, const uint16_t* x, int64_t m, int64_t ldx, const int32_t* ids,
+                          int32_t size, float* y, int32_t* best, hipStream_t s);
 
 hipError_t launch_moe_topk(const float* logits, int32_t t, int32_t e, int32_t topk, int32_t* ids,
                            hipStream_t s);

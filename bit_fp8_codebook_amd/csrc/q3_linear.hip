@@ -95,15 +95,16 @@ struct Planes {
 // (kOob for tiles past the plane); a step adds a wave-uniform amount that
 // stays inside the tile.
 struct RowTile {
-  uint32_t vcode;     // tile*192*Gp + 16*lane
+  uint32_t vcode;     // tile*64*words*Gp + 16*lane (words = 3, or 2 for the 2-bit head)
   uint32_t vscale;    // tile*16*Gp + 4*lane
-  uint32_t cbl, cbh;  // the lane's row codebook (zero past n)
+  uint32_t cbl, cbh;  // the lane's row codebook (zero past n; the 2-bit head's 4 entries in cbl)
 };
 
-// Code words and scales of one step of R row tiles, for one lane.
-template <int R>
+// Code words and scales of one step of R row tiles, for one lane; kWd code
+// words per group (3 for the 3-bit layer, 2 for the 2-bit draft head).
+template <int R, int kWd = 3>
 struct StepData {
-  u32x4 w[R][3];   // w[r][j][t] = word j of the lane's group t in row tile r
+  u32x4 w[R][kWd];   // w[r][j][t] = word j of the lane's group t in row tile r
   uint32_t sc[R];  // byte t = scale of group t
 };
 
@@ -113,18 +114,18 @@ struct StepData {
 // last step, lanes past its quads (last_ok false) read zeros for both codes
 // and scales; a zero scale byte widens to a zero fp32 scale, so those lanes
 // contribute exactly zero whatever activations they meet.
-template <int R>
+template <int R, int kWd>
 __device__ __forceinline__ void load_step(const Planes& p, const RowTile (&rt)[R], bool last_ok, int s, int s_end,
-                                          StepData<R>& d) {
+                                          StepData<R, kWd>& d) {
   const int sc = s < s_end ? s : s_end - 1;
   const bool full = sc < p.full_steps;
   const bool live = full || last_ok;
   const uint32_t js = full ? 1024u : 256u * p.q_last;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const uint32_t o = (live ? rt[r].vcode : kOob) + 3072u * sc;
+    const uint32_t o = (live ? rt[r].vcode : kOob) + 1024u * kWd * sc;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) d.w[r][j] = bload128_stream(p.code, o + js * j);
+    for (int j = 0; j < kWd; ++j) d.w[r][j] = bload128_stream(p.code, o + js * j);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) d.sc[r] = bload32_stream(p.scale, (live ? rt[r].vscale : kOob) + 256u * sc);
@@ -134,14 +135,18 @@ __device__ __forceinline__ void dequant(const u32x4 (&w)[3], uint32_t sc, int t,
                                         bf16x2 (&wv)[16]) {
   dequant_group_bf16(w[0][t], w[1][t], w[2][t], (sc >> (8 * t)) & 0xFFu, cbl, cbh, wv);
 }
+__device__ __forceinline__ void dequant(const u32x4 (&w)[2], uint32_t sc, int t, uint32_t cbl, uint32_t,
+                                        bf16x2 (&wv)[16]) {
+  dequant_group2_bf16(w[0][t], w[1][t], (sc >> (8 * t)) & 0xFFu, cbl, wv);
+}
 
 // Matrix-core step: dequantise the step's 4 groups of every row tile and run
 // 4*4*MT*R MFMAs.  xb[c] is the lane's LDS byte address of its B operand for
 // column tile c at this step (group 0, k 0).  With few column tiles the B
 // operands of a group are held while the row tiles are dequantised one by one;
 // with many, the row tiles' A operands are held while the B operands stream.
-template <int MT, int R>
-__device__ __forceinline__ void mfma_step(const StepData<R>& d, const RowTile (&rt)[R], const uint32_t (&xb)[MT],
+template <int MT, int R, int kWd>
+__device__ __forceinline__ void mfma_step(const StepData<R, kWd>& d, const RowTile (&rt)[R], const uint32_t (&xb)[MT],
                                           const uint8_t* lds, f32x4 (&acc)[R][MT]) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -267,8 +272,8 @@ __device__ __forceinline__ void mfma_step_pipe(const StepData<R>& d, const RowTi
 // token's activations are read while the current token's dot products run;
 // the scheduling barriers stop the compiler from hoisting every token's reads
 // to the top (64 registers per token).
-template <int M, int R>
-__device__ __forceinline__ void dot_step(const StepData<R>& d, const RowTile (&rt)[R], const uint32_t (&xa)[M],
+template <int M, int R, int kWd>
+__device__ __forceinline__ void dot_step(const StepData<R, kWd>& d, const RowTile (&rt)[R], const uint32_t (&xa)[M],
                                          const uint8_t* lds, float (&acc)[R][M]) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -335,9 +340,13 @@ constexpr int min_waves_per_eu() {
 }
 
 // NT: column tiles of 16 tokens (matrix-core mode) or tokens (vector-ALU mode).
-template <int NT, int R, int kW, bool kGrouped, int kMode, bool kDot>
+// kBits: 3 for the 3-bit layer, 2 for the two-bit draft head (two code words
+// per group, a 4-entry codebook per row).
+template <int NT, int R, int kW, bool kGrouped, int kMode, bool kDot, int kBits>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<NT, R, kDot>())))
 void linear_kernel(KArgs a) {
+  constexpr int kWd = kBits == 2 ? 2 : 3;          // code words per group
+  constexpr uint32_t kCbBytes = kBits == 2 ? 4 : 8;   // codebook bytes per row
   constexpr int kThreads = 64 * kW;
   constexpr int kSlice = kDot ? NT : 16 * NT;   // tokens per slice
   extern __shared__ __align__(16) uint8_t lds[];
@@ -375,26 +384,26 @@ void linear_kernel(KArgs a) {
   const int64_t tile0 = ((int64_t)blockIdx.x * rb + rg) * R;   // first row tile of this wave
 
   Planes p;
-  p.code = make_rsrc(a.code + (int64_t)expert * a.code_stride, (uint32_t)(tiles * 192 * gp));
+  p.code = make_rsrc(a.code + (int64_t)expert * a.code_stride, (uint32_t)(tiles * 64 * kWd * gp));
   p.scale = make_rsrc(a.scale + (int64_t)expert * a.scale_stride, (uint32_t)(tiles * 16 * gp));
   p.full_steps = (int)(gp / 16);
   p.steps = (int)((gp + 15) / 16);
   p.q_last = (gp - 16u * (uint32_t)(p.steps - 1)) / 4u;
   const bool last_ok = (uint32_t)kb < p.q_last;   // lane has groups in a partial last step
-  const rsrc_t cbr = make_rsrc(a.cb + (int64_t)expert * a.cb_stride, (uint32_t)(a.n * 8));
+  const rsrc_t cbr = make_rsrc(a.cb + (int64_t)expert * a.cb_stride, (uint32_t)(a.n * kCbBytes));
   RowTile rt[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t T = tile0 + r;
     const bool tile_ok = T < tiles;
-    rt[r].vcode = tile_ok ? (uint32_t)T * (192u * gp) + 16u * lane : kOob;
+    rt[r].vcode = tile_ok ? (uint32_t)T * (64u * kWd * gp) + 16u * lane : kOob;
     rt[r].vscale = tile_ok ? (uint32_t)T * (16u * gp) + 4u * lane : kOob;
   }
 
   const int s0 = kMode != kStream ? (ks * p.steps) / sk : 0;
   const int s1 = kMode != kStream ? ((ks + 1) * p.steps) / sk : p.steps;
 
-  StepData<R> A, B;
+  StepData<R, kWd> A, B;
   const rsrc_t xr_rsrc = make_rsrc(a.x, (uint32_t)((a.x_rows - 1) * a.ldx * 2 + (int64_t)G * 64));
   const uint32_t ldx_bytes = (uint32_t)(a.ldx * 2);
 
@@ -423,16 +432,21 @@ void linear_kernel(KArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int64_t row = (tile0 + r) * 16 + i;
-          const u32x2 cb = bload64(cbr, row < a.n ? (uint32_t)row * 8u : kOob);
-          rt[r].cbl = cb.x;
-          rt[r].cbh = cb.y;
+          if constexpr (kBits == 2) {
+            rt[r].cbl = bload32(cbr, row < a.n ? (uint32_t)row * 4u : kOob);
+            rt[r].cbh = 0u;
+          } else {
+            const u32x2 cb = bload64(cbr, row < a.n ? (uint32_t)row * 8u : kOob);
+            rt[r].cbl = cb.x;
+            rt[r].cbh = cb.y;
+          }
         }
       }
     };
     // Lane addresses of token slots at the step's start in a row-per-token x
     // layout of the given row stride, for buffer base `base` (absent tokens of
     // matrix-core mode go to `zero`, a 1 KB zero block, and stay there).
-    auto run = [&](const StepData<R>& d, uint32_t base, uint32_t rstride, uint32_t zero, uint32_t adv) {
+    auto run = [&](const StepData<R, kWd>& d, uint32_t base, uint32_t rstride, uint32_t zero, uint32_t adv) {
       if constexpr (kDot) {
         uint32_t xa[NT];
 #pragma unroll
@@ -785,12 +799,12 @@ size_t reduce_bytes(int vals, int r, int w) { return (size_t)w * r * vals * 64 *
 
 // Dynamic LDS above 64 KB must be allowed per kernel; raise each kernel's limit
 // once to the largest size this file ever requests.
-template <int NT, int R, int kW, bool kGrouped, int kMode, bool kDot>
+template <int NT, int R, int kW, bool kGrouped, int kMode, bool kDot, int kBits>
 hipError_t allow_lds(size_t bytes) {
   static std::atomic<size_t> allowed{64 * 1024};   // per kernel instantiation
   if (bytes <= allowed.load(std::memory_order_acquire)) return hipSuccess;
   const hipError_t e =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(linear_kernel<NT, R, kW, kGrouped, kMode, kDot>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(linear_kernel<NT, R, kW, kGrouped, kMode, kDot, kBits>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e == hipSuccess) {
     size_t cur = allowed.load(std::memory_order_acquire);
@@ -800,15 +814,15 @@ hipError_t allow_lds(size_t bytes) {
   return e;
 }
 
-template <int NT, int R, int kW, bool kGrouped, int kMode, bool kDot>
+template <int NT, int R, int kW, bool kGrouped, int kMode, bool kDot, int kBits>
 hipError_t launch_one(const KArgs& a, size_t shm, unsigned grid_y, hipStream_t s) {
   const int rb = kW / (kMode != kStream ? a.sk : 1);
   const int64_t tiles = (a.n + 15) / 16;
   const int64_t groups = (tiles + R - 1) / R;   // row groups of R tiles
   const dim3 grid((unsigned)((groups + rb - 1) / rb), grid_y);
-  hipError_t e = allow_lds<NT, R, kW, kGrouped, kMode, kDot>(shm);
+  hipError_t e = allow_lds<NT, R, kW, kGrouped, kMode, kDot, kBits>(shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((linear_kernel<NT, R, kW, kGrouped, kMode, kDot>), grid, dim3(64 * kW), shm, s, a);
+  hipLaunchKernelGGL((linear_kernel<NT, R, kW, kGrouped, kMode, kDot, kBits>), grid, dim3(64 * kW), shm, s, a);
   return hipGetLastError();
 }
 
@@ -859,20 +873,20 @@ Shape pick_shape(int64_t n, int groups, bool full_k, int tokens, bool dot) {
 #endif
 }
 
-template <int NT, int R, bool kGrouped, bool kDot>
+template <int NT, int R, bool kGrouped, bool kDot, int kBits>
 hipError_t launch_r(KArgs a, int w, int mode, size_t shm, unsigned grid_y, hipStream_t s) {
   switch (mode) {
     case kShared:
-      if (w == 8) return launch_one<NT, R, 8, kGrouped, kShared, kDot>(a, shm, grid_y, s);
-      return launch_one<NT, R, 4, kGrouped, kShared, kDot>(a, shm, grid_y, s);
+      if (w == 8) return launch_one<NT, R, 8, kGrouped, kShared, kDot, kBits>(a, shm, grid_y, s);
+      return launch_one<NT, R, 4, kGrouped, kShared, kDot, kBits>(a, shm, grid_y, s);
     default:
-      if (w == 8) return launch_one<NT, R, 8, kGrouped, kStream, kDot>(a, shm, grid_y, s);
-      return launch_one<NT, R, 4, kGrouped, kStream, kDot>(a, shm, grid_y, s);
+      if (w == 8) return launch_one<NT, R, 8, kGrouped, kStream, kDot, kBits>(a, shm, grid_y, s);
+      return launch_one<NT, R, 4, kGrouped, kStream, kDot, kBits>(a, shm, grid_y, s);
   }
 }
 
 // tokens_in_slice: tokens the LDS staging holds at once.
-template <int NT, bool kGrouped, bool kDot>
+template <int NT, bool kGrouped, bool kDot, int kBits = 3>
 hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t s) {
   constexpr int kSlice = kDot ? NT : 16 * NT;
   const size_t fk = full_k_bytes(tokens_in_slice, a.G);
@@ -890,7 +904,7 @@ hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t
 #ifndef Q3_NO_WIDE
   // Two or more column tiles of streamed activations on whole steps: the wide
   // kernel (one wave per SIMD, many row tiles, activations loaded into LDS).
-  if constexpr (!kGrouped && !kDot && NT >= kWideMinNT) {
+  if constexpr (!kGrouped && !kDot && kBits == 3 && NT >= kWideMinNT) {
     if (mode == kStream && a.G % 16 == 0) return launch_wide<NT>(a, s);
   }
 #endif
@@ -900,11 +914,11 @@ hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t
     if (shm < red) shm = red;
   }
   if constexpr (kGrouped || kDot) {
-    return launch_r<NT, 1, kGrouped, kDot>(a, sh.w, mode, shm, grid_y, s);
+    return launch_r<NT, 1, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, s);
   } else {
     switch (sh.r) {
-      case 1: return launch_r<NT, 1, kGrouped, kDot>(a, sh.w, mode, shm, grid_y, s);
-      case 2: return launch_r<NT, 2, kGrouped, kDot>(a, sh.w, mode, shm, grid_y, s);
+      case 1: return launch_r<NT, 1, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, s);
+      case 2: return launch_r<NT, 2, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, s);
       default: return hipErrorInvalidValue;
     }
   }
@@ -937,6 +951,20 @@ hipError_t launch_gemm_small_m(const PlaneView& w, const uint16_t* x, int64_t m,
   if (m <= 32) return launch_cfg<2, false, false>(a, (int)m, 1, s);
   if (m <= 48) return launch_cfg<3, false, false>(a, (int)m, 1, s);
   return launch_cfg<4, false, false>(a, (int)m, 1, s);
+}
+
+hipError_t launch_head2_scores(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
+                               hipStream_t s) {
+  if (w.n == 0) return hipSuccess;
+  KArgs a = base_args(w);
+  a.x = x;
+  a.ldx = ldx;
+  a.y = y;
+  a.ldy = ldy;
+  a.m = (int)m;
+  a.x_rows = m;
+  a.vec_y = ((uintptr_t)y % 16 == 0) && (ldy % 4 == 0);
+  return launch_cfg<1, false, false, 2>(a, (int)m, 1, s);
 }
 
 hipError_t launch_gemv(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,

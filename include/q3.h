@@ -173,6 +173,80 @@ Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t
                                         int32_t x_by_slot, const int32_t* topk_ids, int32_t t,
                                         int32_t topk, float* y, int64_t ldy, void* stream);
 
+/* ---- Two-bit draft head ------------------------------------------------------
+ * (Hibana page, "Model surgery" / "Two-bit draft head": the drafter's output
+ * head scores every vocabulary token; a 2-bit copy of it shortlists candidates
+ * and the FP8 head rescores only those and decides.)  Readings of the page:
+ *   2-bit copy : 2-bit codes into a 4-entry E4M3FN codebook per row and one
+ *                E8M0 scale per group of 32, 2 + 8/32 = 2.25 bits per weight:
+ *                  w2[n][k] = E4M3FN(cb4[n][code]) * 2^(scale[n][k/32] - 127).
+ *                Planes as above with two code words per group: byte b of
+ *                word j (0..1) holds code 16j+4q+b in bits 2q..2q+1; word j of
+ *                (r, g) sits at T*128*Gp + 2048*s + 16*(16*(q*j + kb) + i) + 4*t;
+ *                the scale plane is laid out exactly as the 3-bit one; the
+ *                codebook is uint8 [n][4].  q3_matrix describes such a head
+ *                with `codebook` pointing at [n][4] (4-byte aligned).
+ *   FP8 head   : OCP MXFP8, row-major: elements uint8 [n][ld_elements]
+ *                E4M3FN, scales uint8 [n][ld_scales] E8M0, one per 32
+ *                consecutive elements of a row:
+ *                  w8[n][k] = E4M3FN(e8[n][k]) * 2^(s8[n][k/32] - 127).
+ *   Ranking    : larger score first, equal scores to the lower row index.
+ * Scores are exact products accumulated in fp32, as above. */
+
+typedef struct q3_mxfp8_matrix {
+  int64_t n, k;
+  const void* elements;    /* [n][ld_elements] E4M3FN, 16-byte aligned, ld % 16 == 0 */
+  int64_t ld_elements;
+  const void* scales;      /* [n][ld_scales] E8M0 (ld_scales >= k/32)                */
+  int64_t ld_scales;
+} q3_mxfp8_matrix;
+
+/* Plane sizes of an n x k 2-bit head: code_tile_bytes = 128*Gp, codebook_bytes
+ * = 4*n, payload_bytes = n*k*9/32 (2.25 bits per weight).  Host only. */
+Q3_API q3_status q3_layout2(int64_t n, int64_t k, q3_layout_info* out);
+
+/* Pack / unpack the 2-bit copy: codes [n][ldc] uint8 0..3 (higher bits
+ * ignored), scale_bytes [n][lds]; same conventions as q3_pack / q3_unpack. */
+Q3_API q3_status q3_pack2(const uint8_t* codes, int64_t ldc, const uint8_t* scale_bytes, int64_t lds,
+                          int64_t n, int64_t k, void* code_plane, void* scale_plane, void* stream);
+Q3_API q3_status q3_unpack2(const q3_matrix* w, uint8_t* codes_out, uint8_t* scale_out, void* stream);
+
+/* 2-bit scores of every row for 1 <= m <= 16 queries:
+ * y[m][n] = x[m] . w2[n] (x bf16 [m][ldx], y fp32 [m][ldy]), on the matrix
+ * cores like q3_gemm_small_m. */
+Q3_API q3_status q3_head2_scores(const q3_matrix* w2, const uint16_t* x, int64_t m, int64_t ldx,
+                                 float* y, int64_t ldy, void* stream);
+
+/* Device workspace bytes q3_shortlist needs for m queries (host only). */
+Q3_API int64_t q3_shortlist_workspace_bytes(int64_t m);
+
+/* Shortlist: per query i the `size` rows with the largest scores[i][0..n),
+ * larger first, equal scores to the lower row: ids int32 [m][size] and, if
+ * vals is not NULL, their scores fp32 [m][size].  1 <= size <= 16,
+ * size <= n, 1 <= m <= 65535; scores fp32 [m][ld], finite (not checked);
+ * workspace: q3_shortlist_workspace_bytes(m) bytes of device memory, 8-byte
+ * aligned, owned by the caller (its contents are scratch).  Two launches. */
+Q3_API q3_status q3_shortlist(const float* scores, int64_t m, int64_t n, int64_t ld, int32_t size,
+                              void* workspace, int32_t* ids, float* vals, void* stream);
+
+/* FP8 rescoring of listed rows: y[i][j] = x[i] . w8[ids[i][j]] (fp32 [m][size])
+ * and best[i] = the listed row with the largest y[i][.] (equal: lower row).
+ * Ids outside [0, n) score 0.  1 <= size <= 16, 1 <= m <= 65535; x bf16
+ * [m][ldx] as above.  One block per query. */
+Q3_API q3_status q3_rescore_fp8(const q3_mxfp8_matrix* w8, const uint16_t* x, int64_t m, int64_t ldx,
+                                const int32_t* ids, int32_t size, float* y, int32_t* best, void* stream);
+
+/* The whole draft-head decision for 1 <= m <= 16 queries: 2-bit scores of all
+ * rows, shortlist of `size`, FP8 rescoring and the decision, in four launches.
+ * w2 and w8 must have the same n and k.  workspace:
+ * q3_draft_head_workspace_bytes(m, n) bytes (8-byte aligned; the 2-bit scores
+ * [m][n] then the shortlist scratch).  Outputs: ids [m][size] (the list),
+ * y8 [m][size] (FP8 scores), best [m]. */
+Q3_API int64_t q3_draft_head_workspace_bytes(int64_t m, int64_t n);
+Q3_API q3_status q3_draft_head(const q3_matrix* w2, const q3_mxfp8_matrix* w8, const uint16_t* x, int64_t m,
+                               int64_t ldx, int32_t size, void* workspace, int32_t* ids, float* y8,
+                               int32_t* best, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,10 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(["q3_status_string", "q3_layout", "q3_pack", "q3_unpack", "q3_gemv",
-                                         "q3_gemm_small_m", "q3_moe_topk", "q3_grouped_expert_gemv"])
+                                         "q3_gemm_small_m", "q3_moe_topk", "q3_grouped_expert_gemv",
+                                         "q3_layout2", "q3_pack2", "q3_unpack2", "q3_head2_scores",
+                                         "q3_shortlist_workspace_bytes", "q3_shortlist", "q3_rescore_fp8",
+                                         "q3_draft_head_workspace_bytes", "q3_draft_head"])
 
 
 def test_library_exports_every_declared_symbol(q3lib):
@@ -51,6 +54,48 @@ def test_layout_matches_oracle(q3lib, n, k):
     ref = oracle.layout(n, k)
     for key in ref:
         assert got[key] == ref[key], key
+
+
+@pytest.mark.parametrize("n,k", [(151936, 4096), (1024, 1024), (5, 32), (37, 160), (1, 8224)])
+def test_layout2_matches_oracle(q3lib, n, k):
+    from bit_fp8_codebook_amd import q3_layout2
+    got = q3_layout2(n, k)
+    ref = oracle.layout2(n, k)
+    for key in ref:
+        assert got[key] == ref[key], key
+
+
+def test_workspace_sizes(q3lib):
+    # shortlist scratch: 64 chunk lists of 16 (score, row) pairs per query
+    assert q3lib.q3_shortlist_workspace_bytes(1) == 64 * 16 * 8
+    assert q3lib.q3_shortlist_workspace_bytes(0) == 0
+    # draft head: fp32 scores [m][n] (rounded up to 8 bytes), then the shortlist scratch
+    assert q3lib.q3_draft_head_workspace_bytes(1, 151936) == 151936 * 4 + 64 * 16 * 8
+    assert q3lib.q3_draft_head_workspace_bytes(3, 5) == 64 + 3 * 64 * 16 * 8
+
+
+def test_head_validation_rejects_before_any_hip_call(q3lib):
+    from bit_fp8_codebook_amd import _lib
+    fake = 0x1000
+    w2 = _lib.Q3Matrix(16, 64, fake, fake, fake)
+    assert q3lib.q3_head2_scores(ctypes.byref(w2), fake, 17, 64, fake, 16, None) == 2    # m > 16
+    assert q3lib.q3_head2_scores(ctypes.byref(w2), fake, 0, 64, fake, 16, None) == 2
+    mis = _lib.Q3Matrix(16, 64, fake, fake, fake + 2)                                    # codebook not 4-aligned
+    assert q3lib.q3_head2_scores(ctypes.byref(mis), fake, 1, 64, fake, 16, None) == 3
+    assert q3lib.q3_pack2(fake, 63, fake, 2, 16, 64, fake, fake, None) == 1
+    assert q3lib.q3_shortlist(fake, 1, 100, 100, 17, fake, fake, None, None) == 2         # size > 16
+    assert q3lib.q3_shortlist(fake, 1, 10, 10, 11, fake, fake, None, None) == 2           # size > n
+    assert q3lib.q3_shortlist(fake, 1, 100, 99, 16, fake, fake, None, None) == 1          # ld < n
+    assert q3lib.q3_shortlist(fake, 1, 100, 100, 16, fake + 4, fake, None, None) == 3     # workspace 8-aligned
+    assert q3lib.q3_shortlist(None, 1, 100, 100, 16, fake, fake, None, None) == 1
+    h8 = _lib.Q3Mxfp8Matrix(16, 64, fake, 64, fake, 2)
+    assert q3lib.q3_rescore_fp8(ctypes.byref(h8), fake, 1, 64, fake, 17, fake, fake, None) == 2
+    h8.ld_elements = 72                                                                    # not a multiple of 16
+    assert q3lib.q3_rescore_fp8(ctypes.byref(h8), fake, 1, 64, fake, 16, fake, fake, None) == 3
+    h8.ld_elements = 48                                                                    # < k
+    assert q3lib.q3_rescore_fp8(ctypes.byref(h8), fake, 1, 64, fake, 16, fake, fake, None) == 1
+    h8 = _lib.Q3Mxfp8Matrix(16, 96, fake, 96, fake, 3)                                     # k differs from w2's
+    assert q3lib.q3_draft_head(ctypes.byref(w2), ctypes.byref(h8), fake, 1, 96, 16, fake, fake, fake, fake, None) == 1
 
 
 def test_status_strings(q3lib):
