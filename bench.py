@@ -18,8 +18,10 @@ The same line carries:
   cpu_baseline  the CPU oracle (numpy fp64) on a bounded sample of the same
                 layer, on this host's cores.
   points        per-kernel throughput at M = 1/4/8 (4096 x 4096), M = 16
-                (K=8192, N=28672), M = 64 (K=4096, N=151936) and the
-                expert-grouped MoE verify round, each on cold rotating copies.
+                (K=8192, N=28672), M = 64 (K=4096, N=151936), the
+                expert-grouped MoE verify round and the two-bit draft head
+                (2-bit shortlist of 16 over N=151936, MXFP8 rescore), each on
+                cold rotating copies.
 
 Inputs are synthetic and seeded (codes uniform 0..7, per-row codebooks of
 N(0,1) draws rounded to E4M3, power-of-two group scales 2^-10..2^-4, bf16
@@ -204,6 +206,36 @@ def moe_point(q3, synth, reps=20, warmup=3):
     return pt
 
 
+def draft_head_point(q3, synth, n=151936, k=4096, m=1, size=16, reps=10, warmup=2):
+    """Two-bit draft head on a vocabulary-sized head: 2-bit scores of every row,
+    shortlist of 16, MXFP8 rescoring of the 16 and the decision (four launches),
+    on cold copies of the 2-bit head."""
+    import torch
+    head, x = synth.make_head(n, k, m, seed=0)
+    w0 = q3.q3_pack2(to_dev(head.codes), to_dev(head.scales), to_dev(head.codebook))
+    h8 = q3.Mxfp8Head(n, k, to_dev(head.e8), to_dev(head.s8))
+    del head
+    ncopy = copies_for(w0.payload_bytes)
+    ws = [w0] + [q3.PackedHead2(n, k, w0.code_plane.clone(), w0.scale_plane.clone(), w0.codebook.clone())
+                 for _ in range(ncopy - 1)]
+    xd = to_dev(x)
+    work = q3.draft_head_workspace(m, n, "cuda")
+    stream = torch.cuda.Stream()
+    g = capture(lambda: [q3.q3_draft_head(w, h8, xd, size, work) for w in ws], stream)
+    ms = time_graph(g, stream, reps, warmup)
+    us = ms * 1e3 / len(ws)
+    payload = w0.payload_bytes + m * size * (k + k // 32)     # 2-bit head + the listed MXFP8 rows
+    pt = dict(name="draft head K=4096 N=151936 M=1 (2-bit shortlist of 16, MXFP8 rescore)", n=n, k=k, m=m,
+              shortlist=size, copies=len(ws), us_per_decision=round(us, 2), payload_bytes=payload,
+              payload_GBps=round(payload / us / 1e3, 1),
+              pct_of_8TBps=round(100 * payload / us / 1e3 / HBM_PEAK_GBPS, 1),
+              decisions_per_s=round(m / (us * 1e-6), 1),
+              kernel="2-bit matrix-core scores + two-pass shortlist + MXFP8 rescore")
+    del ws, w0, h8, g, work
+    torch.cuda.empty_cache()
+    return pt
+
+
 # -------------------------------------------------------------- cpu baseline
 
 def cpu_baseline(synth, budget_s=12.0):
@@ -238,8 +270,9 @@ def read_traffic(dot: bool):
     """(kernel name, per-launch HBM bytes) of the M=1 kernel of the measured
     layer from the committed counter file, or (family name, None) when that
     file was taken on other sources.  Kernels are named by their template
-    arguments <tokens or column tiles, row tiles, waves, grouped, full-K,
-    vector-ALU>; the counter run covers only the 4096 x 4096 launches."""
+    arguments <tokens or column tiles, row tiles, waves, grouped, activation
+    mode, vector-ALU, code bits>; the counter run covers only the 4096 x 4096
+    launches."""
     family = "linear_kernel (vector-ALU, M=1)" if dot else "linear_kernel (matrix-core, M=1)"
     try:
         with open(TRAFFIC_FILE) as f:
@@ -249,7 +282,7 @@ def read_traffic(dot: bool):
     if t.get("source_hash") != source_hash():
         return family, None
     cands = [(v.get("dispatches", 0), k, v) for k, v in t.get("kernels", {}).items()
-             if k.startswith("linear_kernel<1, ") and k.endswith(("true>" if dot else "false>"))
+             if k.startswith("linear_kernel<1, ") and k.endswith(("true, 3>" if dot else "false, 3>"))
              and ", false, " in k]
     if not cands:
         return family, None
@@ -364,6 +397,8 @@ def main():
         points.append(linear_point(q3, synth, 151936, 4096, 64, "mfma", reps=5, name="K=4096 N=151936 M=64"))
         log(points[-1])
         points.append(moe_point(q3, synth))
+        log(points[-1])
+        points.append(draft_head_point(q3, synth))
         log(points[-1])
         points.append(linear_point(q3, synth, 1024, 1024, 1, chosen, name="1024x1024 M=1"))
         log(points[-1])

@@ -301,7 +301,8 @@ Q3_API q3_status q3_rescore_fp8(const q3_mxfp8_matrix* w8, const uint16_t* x, in
   if ((st = check_device()) != Q3_OK) return st;
   q3::Mxfp8View h{static_cast<const uint8_t*>(w8->elements), w8->ld_elements, static_cast<const uint8_t*>(w8->scales),
                   w8->ld_scales, w8->n, w8->k};
-  return from_hip(q3::launch_rescore(h, x, m, ldx, ids, size, y, best, static_cast<hipStream_t>(stream)));
+  return from_hip(q3::launch_rescore(h, x, m, ldx, nullptr, const_cast<int32_t*>(ids), size, y, best,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 Q3_API int64_t q3_draft_head_workspace_bytes(int64_t m, int64_t n) {
@@ -324,12 +325,11 @@ Q3_API q3_status q3_draft_head(const q3_matrix* w2, const q3_mxfp8_matrix* w8, c
   if ((st = check_device()) != Q3_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = q3::launch_head2_scores(view_of(w2), x, m, ldx, scores, w2->n, s);
-  if (e == hipSuccess)
-    e = q3::launch_shortlist(scores, m, w2->n, w2->n, size, static_cast<uint8_t*>(workspace) + align8(m * w2->n * 4),
-                             ids, nullptr, s);
+  void* cand = static_cast<uint8_t*>(workspace) + align8(m * w2->n * 4);
+  if (e == hipSuccess) e = q3::launch_shortlist(scores, m, w2->n, w2->n, size, cand, nullptr, nullptr, s);
   q3::Mxfp8View h{static_cast<const uint8_t*>(w8->elements), w8->ld_elements, static_cast<const uint8_t*>(w8->scales),
                   w8->ld_scales, w8->n, w8->k};
-  if (e == hipSuccess) e = q3::launch_rescore(h, x, m, ldx, ids, size, y8, best, s);
+  if (e == hipSuccess) e = q3::launch_rescore(h, x, m, ldx, cand, ids, size, y8, best, s);
   return from_hip(e);
 }
 

@@ -26,157 +26,261 @@ namespace {
 constexpr int kList = kShortlistMax;   // entries kept per list
 constexpr int kThreads1 = 256;         // pass-1 block size
 
-// (a, ia) ranks before (b, ib): larger score, or equal score and lower row.
-__device__ __forceinline__ bool before(float a, int ia, float b, int ib) { return a > b || (a == b && ia < ib); }
+// Entries are (key, row): key = an order-preserving 32-bit image of the score
+// (larger score, larger key; -0 folded into +0, which compares equal to it as
+// a score), ranked by key desc, then row asc.  Key 0 (below every finite
+// score's key) with row kNoRow marks an empty slot.
+__device__ __forceinline__ uint32_t score_key(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+__device__ __forceinline__ bool before(uint32_t a, int ia, uint32_t b, int ib) { return a > b || (a == b && ia < ib); }
 
-// Insert (v, id) into a sorted register list (v[0] best).  The caller scans
-// rows in increasing order, so an equal score never displaces a kept one.
-__device__ __forceinline__ void list_insert(float (&lv)[kList], int (&li)[kList], float v, int id) {
-  if (!(v > lv[kList - 1])) return;
-  lv[kList - 1] = v;
-  li[kList - 1] = id;
+constexpr int kNoRow = 0x7FFFFFFF;
+
+__device__ __forceinline__ void empty_list(uint32_t (&lk)[kList], int (&li)[kList]) {
 #pragma unroll
-  for (int j = kList - 1; j > 0; --j) {
-    if (before(lv[j], li[j], lv[j - 1], li[j - 1])) {
-      const float tv = lv[j];
-      lv[j] = lv[j - 1];
-      lv[j - 1] = tv;
-      const int ti = li[j];
-      li[j] = li[j - 1];
-      li[j - 1] = ti;
+  for (int j = 0; j < kList; ++j) {
+    lk[j] = 0u;
+    li[j] = kNoRow;
+  }
+}
+
+// Insert (k, id) into a lane's sorted list, branch-free.  The caller scans
+// rows in increasing order, so the new entry goes after every kept entry with
+// an equal or larger key (and falls off the end if there are kList of them).
+__device__ __forceinline__ void list_insert(uint32_t (&lk)[kList], int (&li)[kList], uint32_t k, int id) {
+  bool g[kList];   // g[j]: entry j stays in front of the new one
+#pragma unroll
+  for (int j = 0; j < kList; ++j) g[j] = lk[j] >= k;
+#pragma unroll
+  for (int j = kList - 1; j >= 0; --j) {
+    const bool gp = j == 0 ? true : g[j - 1];
+    const uint32_t pk = j == 0 ? 0u : lk[j - 1];
+    const int pi = j == 0 ? 0 : li[j - 1];
+    lk[j] = g[j] ? lk[j] : (gp ? k : pk);
+    li[j] = g[j] ? li[j] : (gp ? id : pi);
+  }
+}
+
+// Keep the better of (k, i) and the same pair from another lane via DPP.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ void dpp_best(uint32_t& k, int& i) {
+  const uint32_t k2 = (uint32_t)__builtin_amdgcn_update_dpp((int)k, (int)k, kCtrl, kRowMask, 0xF, false);
+  const int i2 = __builtin_amdgcn_update_dpp(i, i, kCtrl, kRowMask, 0xF, false);
+  const bool take = before(k2, i2, k, i);
+  k = take ? k2 : k;
+  i = take ? i2 : i;
+}
+
+// The wave's kList best entries over the sorted lists held by its 64 lanes,
+// best first (the same values in every lane).  Each round finds the best list
+// head with DPP exchanges (pairs, quads, half-row and row mirrors, then the
+// row broadcasts that leave the wave's best in lane 63), reads it out, and
+// the lane holding it (rows are distinct, so exactly one) drops its head.
+__device__ __forceinline__ void wave_top(uint32_t (&lk)[kList], int (&li)[kList], uint32_t (&ok)[kList],
+                                         int (&oi)[kList]) {
+#pragma unroll
+  for (int o = 0; o < kList; ++o) {
+    uint32_t k = lk[0];
+    int id = li[0];
+    dpp_best<0xB1, 0xF>(k, id);    // quad_perm [1,0,3,2]
+    dpp_best<0x4E, 0xF>(k, id);    // quad_perm [2,3,0,1]
+    dpp_best<0x141, 0xF>(k, id);   // row_half_mirror
+    dpp_best<0x140, 0xF>(k, id);   // row_mirror: every lane holds its row's best
+    dpp_best<0x142, 0xA>(k, id);   // row_bcast15 into rows 1 and 3
+    dpp_best<0x143, 0xC>(k, id);   // row_bcast31 into rows 2 and 3: lane 63 holds the best
+    const uint32_t bk = (uint32_t)__builtin_amdgcn_readlane((int)k, 63);
+    const int bi = __builtin_amdgcn_readlane(id, 63);
+    ok[o] = bk;
+    oi[o] = bi;
+    const bool mine = lk[0] == bk && li[0] == bi;
+#pragma unroll
+    for (int j = 0; j < kList - 1; ++j) {
+      lk[j] = mine ? lk[j + 1] : lk[j];
+      li[j] = mine ? li[j + 1] : li[j];
     }
+    lk[kList - 1] = mine ? 0u : lk[kList - 1];
+    li[kList - 1] = mine ? kNoRow : li[kList - 1];
   }
-}
-
-// Merge the sorted lists at LDS slots a and b into slot a (top kList kept).
-__device__ __forceinline__ void merge_lists(float* sv, int* si, int a, int b) {
-  float ov[kList];
-  int oi[kList];
-  int x = 0, y = 0;
-#pragma unroll
-  for (int o = 0; o < kList; ++o) {
-    const float va = sv[a * kList + x], vb = sv[b * kList + y];
-    const int ia = si[a * kList + x], ib = si[b * kList + y];
-    const bool takea = before(va, ia, vb, ib);
-    ov[o] = takea ? va : vb;
-    oi[o] = takea ? ia : ib;
-    x += takea ? 1 : 0;
-    y += takea ? 0 : 1;
-  }
-#pragma unroll
-  for (int o = 0; o < kList; ++o) {
-    sv[a * kList + o] = ov[o];
-    si[a * kList + o] = oi[o];
-  }
-}
-
-// Tree-merge the `count` (a power of two) lists in LDS into slot 0.
-__device__ __forceinline__ void merge_tree(float* sv, int* si, int count) {
-  for (int stride = count / 2; stride > 0; stride /= 2) {
-    __syncthreads();
-    if ((int)threadIdx.x < stride) merge_lists(sv, si, threadIdx.x, threadIdx.x + stride);
-  }
-  __syncthreads();
 }
 
 struct Cand {
-  float v;
+  uint32_t k;
   int id;
 };
 
-// Pass 1: block (c, q) keeps the top kList rows of chunk c of query q.
+// Pass 1: block (c, q) keeps the top kList rows of chunk c of query q:
+// per-lane lists, the top of each wave, then the top of the block's waves.
+constexpr int kWaves1 = kThreads1 / 64;
 __global__ __launch_bounds__(kThreads1) void shortlist_chunks(const float* __restrict__ scores, int64_t n, int64_t ld,
                                                               Cand* __restrict__ cand) {
-  __shared__ float sv[kThreads1 * kList];
-  __shared__ int si[kThreads1 * kList];
+  __shared__ uint32_t sk[kWaves1 * kList];
+  __shared__ int si[kWaves1 * kList];
   const int q = blockIdx.y, c = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t cs = (n + kShortlistChunks - 1) / kShortlistChunks;
   const int64_t r0 = (int64_t)c * cs;
   const int64_t r1 = r0 + cs < n ? r0 + cs : n;
-  float lv[kList];
+  uint32_t lk[kList];
+  int li[kList];
+  empty_list(lk, li);
+  const float* row = scores + (int64_t)q * ld;
+  // Eight loads in flight per lane before any insertion.
+  for (int64_t base = r0 + threadIdx.x; base < r1; base += 8 * kThreads1) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t r = base + (int64_t)u * kThreads1;
+      v[u] = r < r1 ? row[r] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t r = base + (int64_t)u * kThreads1;
+      if (r < r1) list_insert(lk, li, score_key(v[u]), (int)r);
+    }
+  }
+  uint32_t ok[kList];
+  int oi[kList];
+  wave_top(lk, li, ok, oi);
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < kList; ++j) {
+      sk[wave * kList + j] = ok[j];
+      si[wave * kList + j] = oi[j];
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // lane t holds entry t of the waves' lists, as a one-entry list
+    empty_list(lk, li);
+    if (lane < kWaves1 * kList) {
+      lk[0] = sk[lane];
+      li[0] = si[lane];
+    }
+    wave_top(lk, li, ok, oi);
+    Cand* out = cand + ((int64_t)q * kShortlistChunks + c) * kList;
+#pragma unroll
+    for (int j = 0; j < kList; ++j)
+      if (lane == j) out[j] = Cand{ok[j], oi[j]};
+  }
+}
+
+// Pass 2, one wave per query: lane c holds chunk c's sorted list.
+static_assert(kShortlistChunks == 64, "one chunk list per lane");
+__device__ __forceinline__ void merge_chunks(const Cand* __restrict__ in, uint32_t (&ok)[kList], int (&oi)[kList]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t lk[kList];
   int li[kList];
 #pragma unroll
   for (int j = 0; j < kList; ++j) {
-    lv[j] = -__builtin_inff();   // below every (finite) score
-    li[j] = 0x7FFFFFFF;
+    const Cand e = in[lane * kList + j];
+    lk[j] = e.k;
+    li[j] = e.id;
   }
-  const float* row = scores + (int64_t)q * ld;
-  for (int64_t r = r0 + threadIdx.x; r < r1; r += kThreads1) list_insert(lv, li, row[r], (int)r);
-#pragma unroll
-  for (int j = 0; j < kList; ++j) {
-    sv[threadIdx.x * kList + j] = lv[j];
-    si[threadIdx.x * kList + j] = li[j];
-  }
-  merge_tree(sv, si, kThreads1);
-  if (threadIdx.x < kList) {
-    Cand* out = cand + ((int64_t)q * kShortlistChunks + c) * kList;
-    out[threadIdx.x] = Cand{sv[threadIdx.x], si[threadIdx.x]};
-  }
+  wave_top(lk, li, ok, oi);
 }
 
-// Pass 2: block q merges the chunk lists of query q and writes the first `size`.
-__global__ __launch_bounds__(kShortlistChunks) void shortlist_merge(const Cand* __restrict__ cand, int32_t size,
-                                                                    int32_t* __restrict__ ids, float* __restrict__ vals) {
-  __shared__ float sv[kShortlistChunks * kList];
-  __shared__ int si[kShortlistChunks * kList];
+__global__ __launch_bounds__(64) void shortlist_merge(const Cand* __restrict__ cand, int32_t size,
+                                                      int32_t* __restrict__ ids, float* __restrict__ vals) {
   const int q = blockIdx.x;
-  const Cand* in = cand + (int64_t)q * kShortlistChunks * kList;
+  const int lane = threadIdx.x;
+  uint32_t ok[kList];
+  int oi[kList];
+  merge_chunks(cand + (int64_t)q * kShortlistChunks * kList, ok, oi);
 #pragma unroll
-  for (int j = 0; j < kList; ++j) {
-    const Cand e = in[threadIdx.x * kList + j];
-    sv[threadIdx.x * kList + j] = e.v;
-    si[threadIdx.x * kList + j] = e.id;
-  }
-  merge_tree(sv, si, kShortlistChunks);
-  if ((int)threadIdx.x < size) {
-    ids[(int64_t)q * size + threadIdx.x] = si[threadIdx.x];
-    if (vals) vals[(int64_t)q * size + threadIdx.x] = sv[threadIdx.x];
-  }
+  for (int j = 0; j < kList; ++j)
+    if (lane == j && j < size) {
+      ids[(int64_t)q * size + j] = oi[j];
+      if (vals) vals[(int64_t)q * size + j] = key_score(ok[j]);
+    }
 }
 
-// Rescore: block q scores the listed rows of query q with the MXFP8 head.
-constexpr int kRescoreWaves = 4;
+// Rescore: block q scores the listed rows of query q with the MXFP8 head, one
+// wave per listed row.  Lane l takes elements 64l .. 64l+63 of each 4096-wide
+// slice of K: four 16-byte element loads, eight 16-byte activation loads and
+// its two scale bytes, all issued before any arithmetic.  With `cand` set the
+// block first merges the query's chunk lists (pass 2 of the shortlist) and
+// writes the list to ids.
+constexpr int kRescoreWaves = kList;
 __global__ __launch_bounds__(64 * kRescoreWaves) void rescore_kernel(Mxfp8View h, const uint16_t* __restrict__ x,
-                                                                     int64_t ldx, const int32_t* __restrict__ ids,
-                                                                     int32_t size, float* __restrict__ y,
+                                                                     int64_t ldx, const Cand* __restrict__ cand,
+                                                                     int32_t* __restrict__ ids, int32_t size,
+                                                                     float* __restrict__ y,
                                                                      int32_t* __restrict__ best) {
   __shared__ float sy[kList];
+  __shared__ int sid[kList];
   const int q = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (cand) {
+    if (wave == 0) {
+      uint32_t ok[kList];
+      int oi[kList];
+      merge_chunks(cand + (int64_t)q * kShortlistChunks * kList, ok, oi);
+#pragma unroll
+      for (int j = 0; j < kList; ++j)
+        if (lane == j && j < size) {
+          sid[j] = oi[j];
+          ids[(int64_t)q * size + j] = oi[j];
+        }
+    }
+  } else if ((int)threadIdx.x < size) {
+    sid[threadIdx.x] = ids[(int64_t)q * size + threadIdx.x];
+  }
+  __syncthreads();
   const rsrc_t er = make_rsrc(h.e8, (uint32_t)(h.n * h.lde));
   const rsrc_t sr = make_rsrc(h.s8, (uint32_t)(h.n * h.lds));
   const rsrc_t xr = make_rsrc(x + (int64_t)q * ldx, (uint32_t)(h.k * 2));
-  for (int j = wave; j < size; j += kRescoreWaves) {
-    const int id = ids[(int64_t)q * size + j];
+  if (wave < size) {
+    const int id = sid[wave];
     const bool ok = id >= 0 && id < h.n;
     float acc = 0.f;
-    // Lane l takes 8 consecutive elements per 512-element slice (one quarter
-    // of a 32-element scale group).
-    for (int64_t k0 = 8 * lane; k0 < h.k; k0 += 512) {
-      const uint32_t eo = ok ? (uint32_t)(id * h.lde + k0) : kOob;
-      const u32x2 e = bload64(er, eo);
-      const uint32_t sb = bload8(sr, ok ? (uint32_t)(id * h.lds + k0 / 32) : kOob);
-      const u32x4 xv = bload128(xr, (uint32_t)(2 * k0));
-      const float sc = e8m0_to_f32(sb);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(fp8x2_to_bf16x2(e.x, sc, false), as_bf16x2(xv.x), acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(fp8x2_to_bf16x2(e.x, sc, true), as_bf16x2(xv.y), acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(fp8x2_to_bf16x2(e.y, sc, false), as_bf16x2(xv.z), acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(fp8x2_to_bf16x2(e.y, sc, true), as_bf16x2(xv.w), acc, false);
+    for (int64_t k0 = 0; k0 < h.k; k0 += 4096) {
+      const int64_t kl = k0 + 64 * lane;            // the lane's first element of this slice
+      u32x4 e[4], xv[8];
+      uint32_t sb[2];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int64_t kp = kl + 16 * p;             // 16 elements, all in or all out (k % 32 == 0)
+        e[p] = bload128(er, ok && kp < h.k ? (uint32_t)(id * h.lde + kp) : kOob);
+      }
+#pragma unroll
+      for (int p = 0; p < 8; ++p) xv[p] = bload128(xr, kl + 8 * p < h.k ? (uint32_t)(2 * (kl + 8 * p)) : kOob);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int64_t kg = kl + 32 * g;
+        sb[g] = bload8(sr, ok && kg < h.k ? (uint32_t)(id * h.lds + kg / 32) : kOob);
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float sc = e8m0_to_f32(sb[p / 2]);
+        const uint32_t wd[4] = {e[p].x, e[p].y, e[p].z, e[p].w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const u32x4 xx = xv[2 * p + d / 2];
+          const uint32_t x0 = (d & 1) ? xx.z : xx.x, x1 = (d & 1) ? xx.w : xx.y;
+          acc = __builtin_amdgcn_fdot2_f32_bf16(fp8x2_to_bf16x2(wd[d], sc, false), as_bf16x2(x0), acc, false);
+          acc = __builtin_amdgcn_fdot2_f32_bf16(fp8x2_to_bf16x2(wd[d], sc, true), as_bf16x2(x1), acc, false);
+        }
+      }
     }
 #pragma unroll
     for (int off = 32; off > 0; off /= 2) acc += __shfl_xor(acc, off, 64);
     if (lane == 0) {
-      sy[j] = acc;
-      y[(int64_t)q * size + j] = acc;
+      sy[wave] = acc;
+      y[(int64_t)q * size + wave] = acc;
     }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     int bj = 0;
     for (int j = 1; j < size; ++j)
-      if (before(sy[j], ids[(int64_t)q * size + j], sy[bj], ids[(int64_t)q * size + bj])) bj = j;
-    best[q] = ids[(int64_t)q * size + bj];
+      if (before(score_key(sy[j]), sid[j], score_key(sy[bj]), sid[bj])) bj = j;
+    best[q] = sid[bj];
   }
 }
 
@@ -187,14 +291,15 @@ hipError_t launch_shortlist(const float* scores, int64_t m, int64_t n, int64_t l
   Cand* c = static_cast<Cand*>(cand);
   hipLaunchKernelGGL(shortlist_chunks, dim3(kShortlistChunks, (unsigned)m), dim3(kThreads1), 0, s, scores, n, ld, c);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(shortlist_merge, dim3((unsigned)m), dim3(kShortlistChunks), 0, s, c, size, ids, vals);
+  if (e != hipSuccess || !ids) return e;
+  hipLaunchKernelGGL(shortlist_merge, dim3((unsigned)m), dim3(64), 0, s, c, size, ids, vals);
   return hipGetLastError();
 }
 
-hipError_t launch_rescore(const Mxfp8View& h, const uint16_t* x, int64_t m, int64_t ldx, const int32_t* ids,
-                          int32_t size, float* y, int32_t* best, hipStream_t s) {
-  hipLaunchKernelGGL(rescore_kernel, dim3((unsigned)m), dim3(64 * kRescoreWaves), 0, s, h, x, ldx, ids, size, y, best);
+hipError_t launch_rescore(const Mxfp8View& h, const uint16_t* x, int64_t m, int64_t ldx, const void* cand,
+                          int32_t* ids, int32_t size, float* y, int32_t* best, hipStream_t s) {
+  hipLaunchKernelGGL(rescore_kernel, dim3((unsigned)m), dim3(64 * kRescoreWaves), 0, s, h, x, ldx,
+                     static_cast<const Cand*>(cand), ids, size, y, best);
   return hipGetLastError();
 }
 

@@ -33,14 +33,17 @@ hipError_t launch_head2_scores(const PlaneView& w, const uint16_t* x, int64_t m,
                                hipStream_t s);
 
 // Shortlist: per query the `size` largest of n fp32 scores (ties to the lower
-// row), in two launches through `cand` (m * kShortlistChunks * size pairs).
+// row), in two launches through `cand` (m * kShortlistChunks * kShortlistMax
+// (score, row) pairs).  With ids == nullptr only the first pass runs (the
+// rescoring launch then merges the chunk lists itself).
 constexpr int kShortlistMax = 16;
 constexpr int kShortlistChunks = 64;
 hipError_t launch_shortlist(const float* scores, int64_t m, int64_t n, int64_t ld, int32_t size, void* cand,
                             int32_t* ids, float* vals, hipStream_t s);
 
 // MXFP8 rows gathered by ids: y[i][j] = x[i] . w8[ids[i][j]]; best[i] = the
-// listed row with the largest y (ties to the lower row).
+// listed row with the largest y (ties to the lower row).  With cand set (the
+// shortlist's first-pass lists), the list is merged first and written to ids.
 struct Mxfp8View {
   const uint8_t* e8;   // [n][lde] E4M3FN
   int64_t lde;
@@ -48,8 +51,8 @@ struct Mxfp8View {
   int64_t lds;
   int64_t n, k;
 };
-hipError_t launch_rescore(const Mxfp8View& h, const uint16_t* x, int64_t m, int64_t ldx, const int32_t* ids,
-                          int32_t size, float* y, int32_t* best, hipStream_t s);
+hipError_t launch_rescore(const Mxfp8View& h, const uint16_t* x, int64_t m, int64_t ldx, const void* cand,
+                          int32_t* ids, int32_t size, float* y, int32_t* best, hipStream_t s);
 
 hipError_t launch_moe_topk(const float* logits, int32_t t, int32_t e, int32_t topk, int32_t* ids,
                            hipStream_t s);

@@ -149,9 +149,15 @@ class Head:
 
 def make_head(n: int, k: int, m: int, seed: int = 0):
     """A draft head and bf16 activations x[m][k]; streams in the order codes,
-    codebook, scales, FP8 elements, FP8 scales, x."""
+    codebook, scales, FP8 elements, FP8 scales, x.  The FP8 elements are drawn
+    in row blocks (the same numbers as one draw, less memory)."""
     rs = _streams(seed, 6)
+    e8 = np.empty((n, k), dtype=np.uint8)
+    block = max(1, (1 << 25) // k)
+    for r0 in range(0, n, block):
+        r1 = min(n, r0 + block)
+        e8[r0:r1] = round_to_e4m3fn_bytes(rs[3].standard_normal((r1 - r0, k)))
     head = Head(n, k, rs[0].integers(0, 4, size=(n, k), dtype=np.uint8),
                 round_to_e4m3fn_bytes(rs[1].standard_normal((n, 4))), draw_scales(rs[2], n, k),
-                round_to_e4m3fn_bytes(rs[3].standard_normal((n, k))), draw_scales(rs[4], n, k))
+                e8, draw_scales(rs[4], n, k))
     return head, draw_x(rs[5], m, k)
