@@ -47,6 +47,18 @@ Parity status per function (what pins each one lives in tests/test_oracle.py):
                   exact Fraction brute force on tiny K
   topk_route      pinned: brute-force ranking, torch.topk on distinct logits
   grouped_linear  pinned: equals per-(token, slot) dense linear calls
+  budget_route    pinned: brute force over expert subsets (largest total mass),
+                  brute-force per-token ranking inside the set, budget = all
+                  experts reduces to topk_route, and a hand-built instance
+                  that reproduces every number of the page's toy figure
+
+Expert budget (same page, "Adaptive speculation" -- "Expert sharing"): a verify
+round gets a shared budget of experts; choices outside it are replaced by
+choices inside it.  Reading taken (the policy is not spelled out): the round
+keeps the `budget` experts with the largest total routing mass (sum over the
+round's tokens of the softmax probability of the expert; equal mass: lower
+index), and each token routes to its top-k experts inside that set by logit
+(equal logits: lower index).
 """
 from __future__ import annotations
 
@@ -359,3 +371,31 @@ def grouped_linear(planes, ids, x_bits, x_by_slot: bool, rows=None):
             y[i, j] = ye[p]
             bound[i, j] = be[p]
     return y, bound
+
+
+def routing_mass(logits: np.ndarray) -> np.ndarray:
+    """Total routing mass per expert: sum over tokens of softmax(logits[t])[e], fp64."""
+    z = np.asarray(logits, dtype=np.float64)
+    z = z - z.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p /= p.sum(axis=1, keepdims=True)
+    return p.sum(axis=0)
+
+
+def budget_route(logits: np.ndarray, topk: int, budget: int):
+    """Expert-budget routing of one verify round.
+
+    Returns (experts, ids): the kept experts, ascending (int32 [budget]), and
+    each token's top-k experts inside them, highest logit first (int32
+    [t][topk]).  Requires topk <= budget <= number of experts."""
+    t, E = logits.shape
+    if not (1 <= topk <= budget <= E):
+        raise ValueError("need 1 <= topk <= budget <= experts")
+    mass = routing_mass(logits)
+    order = sorted(range(E), key=lambda e: (-float(mass[e]), e))
+    kept = sorted(order[:budget])
+    ids = np.empty((t, topk), dtype=np.int32)
+    for i in range(t):
+        inside = sorted(kept, key=lambda e: (-float(logits[i, e]), e))
+        ids[i] = inside[:topk]
+    return np.array(kept, dtype=np.int32), ids
