@@ -153,9 +153,11 @@ def linear_point(q3, synth, n, k, m, kernel, reps=20, warmup=3, name=""):
     return pt
 
 
-def moe_point(q3, synth, reps=20, warmup=3):
+def moe_point(q3, synth, budget=None, reps=20, warmup=3):
     """Config 2: 64 experts (gate/up 2048->1536, down 768->2048), 8 drafted
-    tokens, top-8 routing; one round = router + grouped gate/up + grouped down."""
+    tokens, top-8 routing; one round = router + grouped gate/up + grouped down.
+    With a budget the router keeps the `budget` experts of largest routing mass
+    and routes each token's top-8 inside them."""
     import numpy as np
     import torch
     moe = synth.make_moe(seed=0)
@@ -183,10 +185,14 @@ def moe_point(q3, synth, reps=20, warmup=3):
     ids = torch.empty((t, topk), dtype=torch.int32, device="cuda")
     y_gu = torch.empty((t * topk, st_gu0.n), dtype=torch.float32, device="cuda")
     y_dn = torch.empty((t * topk, st_dn0.n), dtype=torch.float32, device="cuda")
+    kept = torch.empty(budget or 1, dtype=torch.int32, device="cuda")
 
     def round_all():
         for gu, dn in stacks:
-            q3.q3_moe_topk(logits, topk, ids)
+            if budget is None:
+                q3.q3_moe_topk(logits, topk, ids)
+            else:
+                q3.q3_moe_budget_topk(logits, topk, budget, ids, kept)
             q3.q3_grouped_expert_gemv(gu, x, ids, False, y_gu)
             q3.q3_grouped_expert_gemv(dn, x_dn, ids, True, y_dn)
 
@@ -196,7 +202,13 @@ def moe_point(q3, synth, reps=20, warmup=3):
     us = ms * 1e3 / len(stacks)
     union = int(np.unique(ids.cpu().numpy()).size)
     payload = union * per_expert
-    pt = dict(name="moe_verify_round", experts=E, tokens=t, topk=topk, experts_read=union,
+    # share of the round's routing mass on the experts read (plain softmax of the logits)
+    z = np.exp(moe.logits.astype(np.float64) - moe.logits.max(axis=1, keepdims=True))
+    mass = (z / z.sum(axis=1, keepdims=True)).sum(axis=0)
+    read_mass = float(mass[np.unique(ids.cpu().numpy())].sum() / mass.sum())
+    name = "moe_verify_round" if budget is None else f"moe_verify_round_budget{budget}"
+    pt = dict(name=name, experts=E, tokens=t, topk=topk, budget=budget, experts_read=union,
+              routing_mass_read=round(read_mass, 4),
               copies=len(stacks), us_per_round=round(us, 2), union_payload_bytes=payload,
               payload_GBps=round(payload / us / 1e3, 1),
               pct_of_8TBps=round(100 * payload / us / 1e3 / HBM_PEAK_GBPS, 1),
@@ -396,8 +408,9 @@ def main():
         log(points[-1])
         points.append(linear_point(q3, synth, 151936, 4096, 64, "mfma", reps=5, name="K=4096 N=151936 M=64"))
         log(points[-1])
-        points.append(moe_point(q3, synth))
-        log(points[-1])
+        for budget in (None, 16):
+            points.append(moe_point(q3, synth, budget=budget))
+            log(points[-1])
         points.append(draft_head_point(q3, synth))
         log(points[-1])
         points.append(linear_point(q3, synth, 1024, 1024, 1, chosen, name="1024x1024 M=1"))

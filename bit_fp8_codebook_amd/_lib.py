@@ -54,6 +54,7 @@ SIGNATURES = {
     "q3_moe_topk": (ctypes.c_int, [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "q3_grouped_expert_gemv": (ctypes.c_int, [ctypes.POINTER(Q3ExpertStack), c_vp, c_i64, c_i32, c_vp, c_i32,
                                               c_i32, c_vp, c_i64, c_vp]),
+    "q3_moe_budget_topk": (ctypes.c_int, [c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "q3_layout2": (ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(Q3LayoutInfo)]),
     "q3_pack2": (ctypes.c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp]),
     "q3_unpack2": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), c_vp, c_vp, c_vp]),
@@ -224,6 +225,22 @@ def q3_moe_topk(logits: torch.Tensor, topk: int, ids: torch.Tensor = None) -> to
         ids = torch.empty((t, topk), dtype=torch.int32, device=logits.device)
     _check("q3_moe_topk", lib().q3_moe_topk(logits.data_ptr(), t, E, topk, ids.data_ptr(), _stream(logits)))
     return ids
+
+
+def q3_moe_budget_topk(logits: torch.Tensor, topk: int, budget: int, ids: torch.Tensor = None,
+                       experts: torch.Tensor = None):
+    """Expert-budget routing of a verify round -> (ids int32 [t][topk], kept experts int32 [budget] ascending)."""
+    _dev(logits, "logits")
+    if logits.dtype != torch.float32 or not logits.is_contiguous():
+        raise ValueError("logits must be contiguous float32 [t][E]")
+    t, E = logits.shape
+    if ids is None:
+        ids = torch.empty((t, topk), dtype=torch.int32, device=logits.device)
+    if experts is None:
+        experts = torch.empty(budget, dtype=torch.int32, device=logits.device)
+    _check("q3_moe_budget_topk", lib().q3_moe_budget_topk(logits.data_ptr(), t, E, topk, budget, ids.data_ptr(),
+                                                          experts.data_ptr(), _stream(logits)))
+    return ids, experts
 
 
 @dataclass

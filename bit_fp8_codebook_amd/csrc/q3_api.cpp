@@ -193,6 +193,19 @@ Q3_API q3_status q3_moe_topk(const float* logits, int32_t t, int32_t num_experts
   return from_hip(q3::launch_moe_topk(logits, t, num_experts, topk, topk_ids, static_cast<hipStream_t>(stream)));
 }
 
+Q3_API q3_status q3_moe_budget_topk(const float* logits, int32_t t, int32_t num_experts, int32_t topk,
+                                    int32_t budget, int32_t* topk_ids, int32_t* experts, void* stream) {
+  if (!logits || !topk_ids) return Q3_ERR_INVALID_ARG;
+  if (t < 1 || t > 1024 || num_experts < 1 || num_experts > 1024 || topk < 1 || budget < topk ||
+      budget > num_experts)
+    return Q3_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(experts, 4)) return Q3_ERR_MISALIGNED;
+  q3_status st = check_device();
+  if (st != Q3_OK) return st;
+  return from_hip(q3::launch_moe_budget_topk(logits, t, num_experts, topk, budget, topk_ids, experts,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t* x, int64_t ldx,
                                         int32_t x_by_slot, const int32_t* topk_ids, int32_t t, int32_t topk,
                                         float* y, int64_t ldy, void* stream) {

@@ -56,6 +56,10 @@ hipError_t launch_rescore(const Mxfp8View& h, const uint16_t* x, int64_t m, int6
 
 hipError_t launch_moe_topk(const float* logits, int32_t t, int32_t e, int32_t topk, int32_t* ids,
                            hipStream_t s);
+// Expert-budget routing: the `budget` experts of largest routing mass, then each
+// token's top-k inside them; experts (nullable) gets the kept set ascending.
+hipError_t launch_moe_budget_topk(const float* logits, int32_t t, int32_t e, int32_t topk, int32_t budget,
+                                  int32_t* ids, int32_t* experts, hipStream_t s);
 
 struct ExpertView {
   PlaneView base;            // expert 0; n and groups are shared

@@ -2,10 +2,11 @@
 //
 // Hibana: Fast Agentic Inference on Unified-Memory Devices, "Adaptive
 // speculation" / "Expert sharing": a verify round must read each expert chosen
-// by at least one of its drafted tokens.  This kernel picks each token's top-k
-// experts on the device; the expert-grouped product (q3_mfma.hip) then reads
-// each picked expert once, without the list of picked experts ever coming back
-// to the host.
+// by at least one of its drafted tokens, and Hibana gives the round a shared
+// expert budget so it reads fewer.  These kernels pick each token's top-k
+// experts on the device, without or with a budget; the expert-grouped product
+// (q3_linear.hip) then reads each picked expert once, without the list of
+// picked experts ever coming back to the host.
 #include "q3_device.h"
 #include "q3_internal.h"
 
@@ -35,7 +36,87 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ lo
   if (rank < topk) ids[(int64_t)t * topk + rank] = e;
 }
 
+// Expert-budget routing, one block per token, one thread per expert.  Every
+// block first computes the round's routing mass per expert (sum over tokens
+// of the token's softmax probability of that expert): each wave takes tokens
+// and reduces their max and exp-sum over the experts with a fixed lane
+// butterfly, then each thread sums its expert's probabilities over the tokens
+// in token order, so every block gets the same masses bit for bit.  The kept
+// set is the `budget` experts of largest mass (equal mass: lower index), each
+// found by counting the experts that rank before it; the block's token then
+// ranks the kept experts by its logits the same way.  Block 0 also writes the
+// kept set in ascending order.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off /= 2) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off /= 2) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(1024) void budget_topk_kernel(const float* __restrict__ logits, int T, int E, int topk,
+                                                           int budget, int32_t* __restrict__ ids,
+                                                           int32_t* __restrict__ experts) {
+  __shared__ float mass[1024];
+  __shared__ float tok[1024];
+  __shared__ int kept[1024];
+  extern __shared__ float stats[];   // [T][2]: max, exp-sum of each token's logits
+  const int t = blockIdx.x;
+  const int e = threadIdx.x;
+  const int lane = e & 63, wave = e >> 6, waves = blockDim.x >> 6;
+  for (int u = wave; u < T; u += waves) {
+    const float* row = logits + (int64_t)u * E;
+    float mx = -__builtin_inff();
+    for (int o = lane; o < E; o += 64) mx = fmaxf(mx, row[o]);
+    mx = wave_max(mx);
+    float sm = 0.f;
+    for (int o = lane; o < E; o += 64) sm += expf(row[o] - mx);
+    sm = wave_sum(sm);
+    if (lane == 0) {
+      stats[2 * u] = mx;
+      stats[2 * u + 1] = sm;
+    }
+  }
+  __syncthreads();
+  if (e < E) {
+    float m = 0.f;
+    for (int u = 0; u < T; ++u) m += expf(logits[(int64_t)u * E + e] - stats[2 * u]) / stats[2 * u + 1];
+    mass[e] = m;
+    tok[e] = logits[(int64_t)t * E + e];
+  }
+  __syncthreads();
+  bool in = false;
+  if (e < E) {
+    int rank = 0;
+    for (int o = 0; o < E; ++o) rank += ranks_before(mass[o], o, mass[e], e) ? 1 : 0;
+    in = rank < budget;
+    kept[e] = in ? 1 : 0;
+  }
+  __syncthreads();
+  if (in) {
+    int rank = 0, below = 0;
+    for (int o = 0; o < E; ++o) {
+      if (!kept[o]) continue;
+      rank += ranks_before(tok[o], o, tok[e], e) ? 1 : 0;
+      below += o < e ? 1 : 0;
+    }
+    if (rank < topk) ids[(int64_t)t * topk + rank] = e;
+    if (t == 0 && experts) experts[below] = e;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_moe_budget_topk(const float* logits, int32_t t, int32_t e, int32_t topk, int32_t budget,
+                                  int32_t* ids, int32_t* experts, hipStream_t s) {
+  const unsigned threads = (unsigned)((e + 63) / 64 * 64);
+  hipLaunchKernelGGL(budget_topk_kernel, dim3((unsigned)t), dim3(threads), (size_t)t * 2 * sizeof(float), s, logits,
+                     (int)t, (int)e, (int)topk, (int)budget, ids, experts);
+  return hipGetLastError();
+}
 
 hipError_t launch_moe_topk(const float* logits, int32_t t, int32_t e, int32_t topk, int32_t* ids, hipStream_t s) {
   const unsigned threads = (unsigned)((e + 63) / 64 * 64);

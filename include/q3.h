@@ -160,6 +160,19 @@ Q3_API q3_status q3_gemm_small_m(const q3_matrix* w, const uint16_t* x, int64_t 
 Q3_API q3_status q3_moe_topk(const float* logits, int32_t t, int32_t num_experts, int32_t topk,
                              int32_t* topk_ids, void* stream);
 
+/* Router of a verify round with a shared expert budget ("Expert sharing": the
+ * round gets a budget of experts and choices outside it are replaced by
+ * choices inside it).  Reading of the policy: keep the `budget` experts with
+ * the largest routing mass (sum over the t tokens of softmax(logits[i])[e];
+ * equal mass: lower index), then give each token its top-k experts inside that
+ * set by logit (highest first; equal logits: lower index).  topk_ids int32
+ * [t][topk]; experts (may be NULL) int32 [budget], the kept set ascending.
+ * 1 <= topk <= budget <= num_experts <= 1024, 1 <= t <= 1024; logits finite (not
+ * checked).  Masses are fp32 sums in a fixed order (run-to-run identical).
+ * One block per token; each block recomputes the round's masses. */
+Q3_API q3_status q3_moe_budget_topk(const float* logits, int32_t t, int32_t num_experts, int32_t topk,
+                                    int32_t budget, int32_t* topk_ids, int32_t* experts, void* stream);
+
 /* Expert-grouped product of one verify round.  Only experts that appear in
  * topk_ids are read from memory, each once, and each is applied only to the
  * (token, slot) pairs routed to it:

@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
                                          "q3_gemm_small_m", "q3_moe_topk", "q3_grouped_expert_gemv",
                                          "q3_layout2", "q3_pack2", "q3_unpack2", "q3_head2_scores",
                                          "q3_shortlist_workspace_bytes", "q3_shortlist", "q3_rescore_fp8",
-                                         "q3_draft_head_workspace_bytes", "q3_draft_head"])
+                                         "q3_draft_head_workspace_bytes", "q3_draft_head", "q3_moe_budget_topk"])
 
 
 def test_library_exports_every_declared_symbol(q3lib):
@@ -135,6 +135,11 @@ def test_validation_rejects_before_any_hip_call(q3lib):
     assert q3lib.q3_pack(fake, 64, fake, 2, 16, 64, fake + 8, fake, None) == 3
     assert q3lib.q3_moe_topk(fake, 8, 64, 65, fake, None) == 2
     assert q3lib.q3_moe_topk(fake, 8, 2048, 8, fake, None) == 2
+    assert q3lib.q3_moe_budget_topk(fake, 8, 64, 8, 7, fake, None, None) == 2     # budget < topk
+    assert q3lib.q3_moe_budget_topk(fake, 8, 64, 8, 65, fake, None, None) == 2    # budget > experts
+    assert q3lib.q3_moe_budget_topk(fake, 1025, 64, 8, 16, fake, None, None) == 2  # too many tokens
+    assert q3lib.q3_moe_budget_topk(fake, 8, 64, 8, 16, fake, fake + 2, None) == 3
+    assert q3lib.q3_moe_budget_topk(None, 8, 64, 8, 16, fake, None, None) == 1
     # n = 16, k = 64: one tile of 192*4 = 768 code bytes and 64 scale bytes.
     st = _lib.Q3ExpertStack(4, 16, 64, fake, 768, fake, 64, fake, 128)
     assert q3lib.q3_grouped_expert_gemv(ctypes.byref(st), fake, 64, 2, fake, 8, 8, fake, 16, None) == 1
