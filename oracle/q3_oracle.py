@@ -47,10 +47,25 @@ Parity status per function (what pins each one lives in tests/test_oracle.py):
                   exact Fraction brute force on tiny K
   topk_route      pinned: brute-force ranking, torch.topk on distinct logits
   grouped_linear  pinned: equals per-(token, slot) dense linear calls
+  moe_mlp         pinned: closed form on constant weights (silu of a known
+                  sum, softmax of two logits), a torch float64 composition
+                  from torch-decoded weights with F.silu and a renormalised
+                  full softmax, and the bound's derivatives against autograd
   budget_route    pinned: brute force over expert subsets (largest total mass),
                   brute-force per-token ranking inside the set, budget = all
                   experts reduces to topk_route, and a hand-built instance
                   that reproduces every number of the page's toy figure
+
+Fused expert MLP of a verify round (same page, "Expert sharing", the experts
+the round reads).  Readings taken (the page gives no MLP detail): an expert's
+gate/up matrix stacks the gate rows [0, I) over the up rows [I, 2I); the
+hidden value is h = silu(g) * u with silu(z) = z / (1 + e^-z); each token's
+output is the sum over its slots of p_s * (down_expert . h), where p is the
+softmax of the token's routed logits (its top-k probabilities renormalised).
+The allowance of a fused output is 1e-3 times its first-order error bound:
+sum_s p_s sum_j |w_j| (|h_j| + |dh/dg_j| Bg_j + |dh/du_j| Bu_j), with Bg, Bu
+the sums |x w| of the gate and up products (the layer's own allowance,
+carried through the SwiGLU and the down product).
 
 Expert budget (same page, "Adaptive speculation" -- "Expert sharing"): a verify
 round gets a shared budget of experts; choices outside it are replaced by
@@ -399,3 +414,52 @@ def budget_route(logits: np.ndarray, topk: int, budget: int):
         inside = sorted(kept, key=lambda e: (-float(logits[i, e]), e))
         ids[i] = inside[:topk]
     return np.array(kept, dtype=np.int32), ids
+
+
+def silu(z):
+    """z * sigmoid(z) = z / (1 + e^-z), fp64."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def combine_weights(logits: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """p[t][s]: softmax over token t's routed logits logits[t][ids[t][s]], fp64."""
+    sel = np.take_along_axis(np.asarray(logits, dtype=np.float64), np.asarray(ids, dtype=np.int64), axis=1)
+    p = np.exp(sel - sel.max(axis=1, keepdims=True))
+    return p / p.sum(axis=1, keepdims=True)
+
+
+def moe_mlp(planes_gu, planes_dn, ids, logits, x_bits, rows=None):
+    """Fused expert MLP of one verify round: out[t][r] = sum_s p[t][s] *
+    sum_j w_dn[e][r][j] * silu(g[t][s][j]) * u[t][s][j], with g and u the gate
+    and up halves of expert e = ids[t][s] applied to x[t].
+
+    planes_gu / planes_dn: lists over experts of (code_plane, scale_plane,
+    codebook, n, k); gate/up has n = 2I, down has k = I.  Returns out[t][nr]
+    and the first-order bound of each output (module header), for the down
+    rows `rows` (default: all)."""
+    t, topk = ids.shape
+    I = planes_gu[0][3] // 2
+    n_dn = planes_dn[0][3]
+    rows = np.arange(n_dn) if rows is None else np.asarray(rows, dtype=np.int64)
+    gu, bgu = grouped_linear(planes_gu, ids, x_bits, False)          # [t][topk][2I]
+    g, u = gu[..., :I], gu[..., I:]
+    bg, bu = bgu[..., :I], bgu[..., I:]
+    sg = 1.0 / (1.0 + np.exp(-g))
+    h = g * sg * u
+    dh_dg = sg * (1.0 + g * (1.0 - sg)) * u
+    dh_du = g * sg
+    slack = np.abs(h) + np.abs(dh_dg) * bg + np.abs(dh_du) * bu
+    p = combine_weights(logits, ids)
+    out = np.zeros((t, rows.size))
+    bound = np.zeros_like(out)
+    for e in expert_union(ids):
+        cp, sp, cb, ne, ke = planes_dn[e]
+        codes, scales = unpack(cp, sp, ne, ke, rows=rows)
+        w = dequantize(codes, scales, cb[rows])                       # [nr][I]
+        for i in range(t):
+            for j in range(topk):
+                if ids[i, j] == e:
+                    out[i] += p[i, j] * (w @ h[i, j])
+                    bound[i] += p[i, j] * (np.abs(w) @ slack[i, j])
+    return out, bound
