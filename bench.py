@@ -153,11 +153,13 @@ def linear_point(q3, synth, n, k, m, kernel, reps=20, warmup=3, name=""):
     return pt
 
 
-def moe_point(q3, synth, budget=None, reps=20, warmup=3):
+def moe_point(q3, synth, budget=None, fused=False, reps=20, warmup=3):
     """Config 2: 64 experts (gate/up 2048->1536, down 768->2048), 8 drafted
     tokens, top-8 routing; one round = router + grouped gate/up + grouped down.
     With a budget the router keeps the `budget` experts of largest routing mass
-    and routes each token's top-8 inside them."""
+    and routes each token's top-8 inside them.  Fused: the round is the router
+    and the fused expert MLP (SwiGLU between the products, outputs combined by
+    routing weight into one row per token)."""
     import numpy as np
     import torch
     moe = synth.make_moe(seed=0)
@@ -186,6 +188,8 @@ def moe_point(q3, synth, budget=None, reps=20, warmup=3):
     y_gu = torch.empty((t * topk, st_gu0.n), dtype=torch.float32, device="cuda")
     y_dn = torch.empty((t * topk, st_dn0.n), dtype=torch.float32, device="cuda")
     kept = torch.empty(budget or 1, dtype=torch.int32, device="cuda")
+    ws = q3.moe_mlp_workspace(st_gu0, st_dn0, t, topk, "cuda") if fused else None
+    out = torch.empty((t, st_dn0.n), dtype=torch.float32, device="cuda")
 
     def round_all():
         for gu, dn in stacks:
@@ -193,8 +197,11 @@ def moe_point(q3, synth, budget=None, reps=20, warmup=3):
                 q3.q3_moe_topk(logits, topk, ids)
             else:
                 q3.q3_moe_budget_topk(logits, topk, budget, ids, kept)
-            q3.q3_grouped_expert_gemv(gu, x, ids, False, y_gu)
-            q3.q3_grouped_expert_gemv(dn, x_dn, ids, True, y_dn)
+            if fused:
+                q3.q3_moe_mlp(gu, dn, x, ids, logits, ws, out)
+            else:
+                q3.q3_grouped_expert_gemv(gu, x, ids, False, y_gu)
+                q3.q3_grouped_expert_gemv(dn, x_dn, ids, True, y_dn)
 
     stream = torch.cuda.Stream()
     g = capture(round_all, stream)
@@ -206,13 +213,15 @@ def moe_point(q3, synth, budget=None, reps=20, warmup=3):
     z = np.exp(moe.logits.astype(np.float64) - moe.logits.max(axis=1, keepdims=True))
     mass = (z / z.sum(axis=1, keepdims=True)).sum(axis=0)
     read_mass = float(mass[np.unique(ids.cpu().numpy())].sum() / mass.sum())
-    name = "moe_verify_round" if budget is None else f"moe_verify_round_budget{budget}"
+    name = ("moe_mlp_round" if fused else "moe_verify_round") + ("" if budget is None else f"_budget{budget}")
     pt = dict(name=name, experts=E, tokens=t, topk=topk, budget=budget, experts_read=union,
               routing_mass_read=round(read_mass, 4),
               copies=len(stacks), us_per_round=round(us, 2), union_payload_bytes=payload,
               payload_GBps=round(payload / us / 1e3, 1),
               pct_of_8TBps=round(100 * payload / us / 1e3 / HBM_PEAK_GBPS, 1),
-              tokens_per_s=round(t / (us * 1e-6), 1), kernel="mfma grouped + top-k router")
+              tokens_per_s=round(t / (us * 1e-6), 1),
+              kernel=("router + fused SwiGLU gate/up + down with combine" if fused
+                      else "mfma grouped + top-k router"))
     del stacks, g
     torch.cuda.empty_cache()
     return pt
@@ -408,9 +417,10 @@ def main():
         log(points[-1])
         points.append(linear_point(q3, synth, 151936, 4096, 64, "mfma", reps=5, name="K=4096 N=151936 M=64"))
         log(points[-1])
-        for budget in (None, 16):
-            points.append(moe_point(q3, synth, budget=budget))
-            log(points[-1])
+        for fused in (False, True):
+            for budget in (None, 16):
+                points.append(moe_point(q3, synth, budget=budget, fused=fused))
+                log(points[-1])
         points.append(draft_head_point(q3, synth))
         log(points[-1])
         points.append(linear_point(q3, synth, 1024, 1024, 1, chosen, name="1024x1024 M=1"))

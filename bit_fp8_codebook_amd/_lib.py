@@ -55,6 +55,9 @@ SIGNATURES = {
     "q3_grouped_expert_gemv": (ctypes.c_int, [ctypes.POINTER(Q3ExpertStack), c_vp, c_i64, c_i32, c_vp, c_i32,
                                               c_i32, c_vp, c_i64, c_vp]),
     "q3_moe_budget_topk": (ctypes.c_int, [c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
+    "q3_moe_mlp_workspace_bytes": (c_i64, [c_i64, c_i64, c_i32, c_i32]),
+    "q3_moe_mlp": (ctypes.c_int, [ctypes.POINTER(Q3ExpertStack), ctypes.POINTER(Q3ExpertStack), c_vp, c_i64, c_vp,
+                                  c_i32, c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
     "q3_layout2": (ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(Q3LayoutInfo)]),
     "q3_pack2": (ctypes.c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp]),
     "q3_unpack2": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), c_vp, c_vp, c_vp]),
@@ -292,6 +295,36 @@ def q3_grouped_expert_gemv(stack: ExpertStack, x: torch.Tensor, topk_ids: torch.
            lib().q3_grouped_expert_gemv(ctypes.byref(d), x.data_ptr(), _ld(x), 1 if x_by_slot else 0,
                                         topk_ids.data_ptr(), t, topk, y.data_ptr(), _ld(y), _stream(x)))
     return y
+
+
+def moe_mlp_workspace(gate_up: ExpertStack, down: ExpertStack, t: int, topk: int, device) -> torch.Tensor:
+    """Zeroed workspace for q3_moe_mlp (reusable across calls in stream order)."""
+    nbytes = lib().q3_moe_mlp_workspace_bytes(gate_up.n, down.n, t, topk)
+    if nbytes <= 0:
+        raise ValueError("unsupported fused-MLP shape")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def q3_moe_mlp(gate_up: ExpertStack, down: ExpertStack, x: torch.Tensor, topk_ids: torch.Tensor,
+               logits: torch.Tensor, workspace: torch.Tensor = None, out: torch.Tensor = None) -> torch.Tensor:
+    """Fused expert MLP of a verify round: out[t] = sum_j p[t][j] * down_e . (silu(gate_e . x[t]) * (up_e . x[t]))."""
+    _dev(x, "x"), _dev(topk_ids, "topk_ids"), _dev(logits, "logits")
+    t, topk = topk_ids.shape
+    if topk_ids.dtype != torch.int32 or not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be contiguous int32 [t][topk]")
+    if x.dim() != 2 or x.shape[1] != gate_up.k or x.stride(1) != 1 or x.shape[0] < t:
+        raise ValueError("x must be [t][k] with contiguous rows")
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1 or logits.shape[0] < t:
+        raise ValueError("logits must be fp32 [t][num_experts] with contiguous rows")
+    if workspace is None:
+        workspace = moe_mlp_workspace(gate_up, down, t, topk, x.device)
+    out = _out(out, t, down.n, x.device)
+    gd, dd = gate_up.desc(), down.desc()
+    _check("q3_moe_mlp", lib().q3_moe_mlp(ctypes.byref(gd), ctypes.byref(dd), x.data_ptr(), _ld(x),
+                                          topk_ids.data_ptr(), t, topk, logits.data_ptr(), _ld(logits),
+                                          workspace.data_ptr(), workspace.numel(), out.data_ptr(), _ld(out),
+                                          _stream(x)))
+    return out
 
 
 # ------------------------------------------------------- two-bit draft head

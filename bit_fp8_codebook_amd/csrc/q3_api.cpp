@@ -206,9 +206,9 @@ Q3_API q3_status q3_moe_budget_topk(const float* logits, int32_t t, int32_t num_
                                              static_cast<hipStream_t>(stream)));
 }
 
-Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t* x, int64_t ldx,
-                                        int32_t x_by_slot, const int32_t* topk_ids, int32_t t, int32_t topk,
-                                        float* y, int64_t ldy, void* stream) {
+namespace {
+
+q3_status check_stack(const q3_expert_stack* w) {
   if (!w) return Q3_ERR_INVALID_ARG;
   if (w->num_experts < 1 || w->num_experts > 65535) return Q3_ERR_UNSUPPORTED_SHAPE;
   q3_status st = check_planes(w->n, w->k, w->code_plane, w->scale_plane, w->codebook);
@@ -218,12 +218,10 @@ Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t
     return Q3_ERR_INVALID_ARG;
   if (w->code_expert_stride % 16 || w->scale_expert_stride % 4 || w->codebook_expert_stride % 8)
     return Q3_ERR_MISALIGNED;
-  if (x_by_slot != 0 && x_by_slot != 1) return Q3_ERR_INVALID_ARG;
-  if (!x || !topk_ids || !y) return Q3_ERR_INVALID_ARG;
-  if (t < 1 || topk < 1 || int64_t(t) * topk > 64) return Q3_ERR_UNSUPPORTED_SHAPE;
-  if (ldx < w->k || ldy < w->n) return Q3_ERR_INVALID_ARG;
-  if (ldx % 8 || !aligned(x, 16) || !aligned(y, 4) || !aligned(topk_ids, 4)) return Q3_ERR_MISALIGNED;
-  if ((st = check_device()) != Q3_OK) return st;
+  return Q3_OK;
+}
+
+q3::ExpertView view_of(const q3_expert_stack* w) {
   q3::ExpertView v;
   v.base.code = static_cast<const uint8_t*>(w->code_plane);
   v.base.scale = static_cast<const uint8_t*>(w->scale_plane);
@@ -234,7 +232,65 @@ Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t
   v.scale_stride = w->scale_expert_stride;
   v.cb_stride = w->codebook_expert_stride;
   v.num_experts = static_cast<int32_t>(w->num_experts);
-  return from_hip(q3::launch_grouped(v, x, ldx, x_by_slot, topk_ids, t, topk, y, ldy,
+  return v;
+}
+
+// Fused MLP workspace: h (bf16 [2*pairs][I]), part (fp32 [pairs][ldp]),
+// counters (uint32 per 64 down rows), each piece 256-byte aligned.
+int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
+int64_t mlp_ldp(int64_t n_dn) { return (n_dn + 3) / 4 * 4; }
+int64_t mlp_h_bytes(int64_t pairs, int64_t inter) { return align256(2 * pairs * inter * 2); }
+int64_t mlp_part_bytes(int64_t pairs, int64_t n_dn) { return align256(pairs * mlp_ldp(n_dn) * 4); }
+int64_t mlp_counter_bytes(int64_t n_dn) { return align256(4 * (int64_t)q3::moe_mlp_row_blocks(n_dn)); }
+
+}  // namespace
+
+Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t* x, int64_t ldx,
+                                        int32_t x_by_slot, const int32_t* topk_ids, int32_t t, int32_t topk,
+                                        float* y, int64_t ldy, void* stream) {
+  q3_status st = check_stack(w);
+  if (st != Q3_OK) return st;
+  if (x_by_slot != 0 && x_by_slot != 1) return Q3_ERR_INVALID_ARG;
+  if (!x || !topk_ids || !y) return Q3_ERR_INVALID_ARG;
+  if (t < 1 || topk < 1 || int64_t(t) * topk > 64) return Q3_ERR_UNSUPPORTED_SHAPE;
+  if (ldx < w->k || ldy < w->n) return Q3_ERR_INVALID_ARG;
+  if (ldx % 8 || !aligned(x, 16) || !aligned(y, 4) || !aligned(topk_ids, 4)) return Q3_ERR_MISALIGNED;
+  if ((st = check_device()) != Q3_OK) return st;
+  return from_hip(q3::launch_grouped(view_of(w), x, ldx, x_by_slot, topk_ids, t, topk, y, ldy,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+Q3_API int64_t q3_moe_mlp_workspace_bytes(int64_t n_gu, int64_t n_dn, int32_t t, int32_t topk) {
+  if (n_gu < 32 || n_gu % 64 || n_dn < 1 || t < 1 || topk < 1 || int64_t(t) * topk > 64) return 0;
+  const int64_t pairs = int64_t(t) * topk;
+  return mlp_h_bytes(pairs, n_gu / 2) + mlp_part_bytes(pairs, n_dn) + mlp_counter_bytes(n_dn);
+}
+
+Q3_API q3_status q3_moe_mlp(const q3_expert_stack* gate_up, const q3_expert_stack* down, const uint16_t* x,
+                            int64_t ldx, const int32_t* topk_ids, int32_t t, int32_t topk, const float* logits,
+                            int64_t ld_logits, void* workspace, int64_t workspace_bytes, float* out, int64_t ldo,
+                            void* stream) {
+  q3_status st = check_stack(gate_up);
+  if (st != Q3_OK) return st;
+  if ((st = check_stack(down)) != Q3_OK) return st;
+  if (gate_up->num_experts != down->num_experts) return Q3_ERR_INVALID_ARG;
+  if (gate_up->n % 64 || down->k != gate_up->n / 2) return Q3_ERR_UNSUPPORTED_SHAPE;
+  if (!x || !topk_ids || !logits || !workspace || !out) return Q3_ERR_INVALID_ARG;
+  if (t < 1 || topk < 1 || int64_t(t) * topk > 64) return Q3_ERR_UNSUPPORTED_SHAPE;
+  if (ldx < gate_up->k || ldo < down->n || ld_logits < gate_up->num_experts) return Q3_ERR_INVALID_ARG;
+  if (workspace_bytes < q3_moe_mlp_workspace_bytes(gate_up->n, down->n, t, topk)) return Q3_ERR_INVALID_ARG;
+  if (ldx % 8 || !aligned(x, 16) || !aligned(out, 4) || !aligned(topk_ids, 4) || !aligned(logits, 4) ||
+      !aligned(workspace, 256))
+    return Q3_ERR_MISALIGNED;
+  if ((st = check_device()) != Q3_OK) return st;
+  const int64_t pairs = int64_t(t) * topk;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws);
+  float* part = reinterpret_cast<float*>(ws + mlp_h_bytes(pairs, gate_up->n / 2));
+  uint32_t* counters =
+      reinterpret_cast<uint32_t*>(ws + mlp_h_bytes(pairs, gate_up->n / 2) + mlp_part_bytes(pairs, down->n));
+  return from_hip(q3::launch_moe_mlp(view_of(gate_up), view_of(down), x, ldx, topk_ids, t, topk, logits, ld_logits,
+                                     h, part, mlp_ldp(down->n), counters, out, ldo,
                                      static_cast<hipStream_t>(stream)));
 }
 

@@ -57,6 +57,17 @@ enum Mode : int {
 };
 constexpr uint32_t kRowPad = 16;          // LDS row padding against bank conflicts
 
+// Which rows and tokens a block takes.
+enum Grouping : int {
+  kDense = 0,         // every token against every row
+  kExperts = 1,       // grid row e: the (token, slot) pairs routed to expert e
+  kSwiGLU = 2,        // as kExperts on a gate/up matrix [gate I rows; up I rows]: a wave takes
+                      // gate tile q and up tile q and writes h = silu(g) * u as two bf16 terms
+  kDownCombine = 3,   // as kExperts with each pair's activation given as two bf16 rows (high
+                      // and low term); the block adds the terms, and the last block of each
+                      // row range to finish combines every token's slots by routing weight
+};
+
 struct KArgs {
   const uint8_t* code;
   int64_t code_stride;    // bytes between experts
@@ -76,6 +87,21 @@ struct KArgs {
   int sk;         // K split over the waves of a block (full-K mode)
   const int32_t* ids;
   int pairs_total, topk, x_by_slot;
+  int num_experts;
+  // kSwiGLU: tiles in the gate half; output terms h[2*pair + term][I]
+  int half_tiles;
+  uint16_t* h;
+  int64_t ldh;
+  // kDownCombine: per-pair outputs, arrival counters (one per block column, zero
+  // before and after a launch), router logits and the combined output
+  float* part;
+  int64_t ldp;
+  uint32_t* counters;
+  const float* logits;
+  int64_t ld_logits;
+  float* out;
+  int64_t ldo;
+  int t;
 };
 
 __device__ __forceinline__ bf16x8 pack_bf16x8(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
@@ -342,7 +368,7 @@ constexpr int min_waves_per_eu() {
 // NT: column tiles of 16 tokens (matrix-core mode) or tokens (vector-ALU mode).
 // kBits: 3 for the 3-bit layer, 2 for the two-bit draft head (two code words
 // per group, a 4-entry codebook per row).
-template <int NT, int R, int kW, bool kGrouped, int kMode, bool kDot, int kBits>
+template <int NT, int R, int kW, int kGrouped, int kMode, bool kDot, int kBits>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<NT, R, kDot>())))
 void linear_kernel(KArgs a) {
   constexpr int kWd = kBits == 2 ? 2 : 3;          // code words per group
@@ -352,6 +378,7 @@ void linear_kernel(KArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int pairs[64];
   __shared__ int npairs;
+  __shared__ int nexperts;   // kDownCombine: in-range experts of the round
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -368,20 +395,44 @@ void linear_kernel(KArgs a) {
   if (kGrouped) {
     expert = blockIdx.y;
     if (tid < 64) {
-      const bool match = tid < a.pairs_total && a.ids[tid] == expert;
+      const int id = tid < a.pairs_total ? a.ids[tid] : -1;
+      const bool match = id == expert;
       const unsigned long long mask = __ballot(match);
       if (match) pairs[__popcll(mask & ((1ull << tid) - 1ull))] = tid;
       if (tid == 0) npairs = __popcll(mask);
+      if constexpr (kGrouped == kDownCombine) {
+        // The blocks of one row range that will arrive: one per distinct in-range expert.
+        bool first = id >= 0 && id < a.num_experts;
+        for (int o = 0; o < 64; ++o) {
+          const int other = __shfl(id, o, 64);
+          if (o < tid && other == id) first = false;
+        }
+        const unsigned long long fm = __ballot(first);
+        if (tid == 0) nexperts = __popcll(fm);
+      }
     }
     __syncthreads();
     if (npairs == 0) return;   // not picked this round: no weight byte is read
   }
-  const int total_tokens = kGrouped ? __builtin_amdgcn_readfirstlane(npairs) : a.m;
+  const int total_tokens =
+      kGrouped == kDownCombine ? 2 * __builtin_amdgcn_readfirstlane(npairs)
+                             : (kGrouped ? __builtin_amdgcn_readfirstlane(npairs) : a.m);
 
   const int G = a.G;
   const uint32_t gp = (uint32_t)((G + 3) & ~3);
   const int64_t tiles = (a.n + 15) / 16;
   const int64_t tile0 = ((int64_t)blockIdx.x * rb + rg) * R;   // first row tile of this wave
+  // Row tiles of this wave: R consecutive tiles, or gate tile q and up tile q.
+  int64_t tix[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if constexpr (kGrouped == kSwiGLU) {
+      const int64_t q = (int64_t)blockIdx.x * rb + rg;
+      tix[r] = q < a.half_tiles ? q + r * a.half_tiles : tiles;
+    } else {
+      tix[r] = tile0 + r;
+    }
+  }
 
   Planes p;
   p.code = make_rsrc(a.code + (int64_t)expert * a.code_stride, (uint32_t)(tiles * 64 * kWd * gp));
@@ -394,7 +445,7 @@ void linear_kernel(KArgs a) {
   RowTile rt[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t T = tile0 + r;
+    const int64_t T = tix[r];
     const bool tile_ok = T < tiles;
     rt[r].vcode = tile_ok ? (uint32_t)T * (64u * kWd * gp) + 16u * lane : kOob;
     rt[r].vscale = tile_ok ? (uint32_t)T * (16u * gp) + 4u * lane : kOob;
@@ -411,6 +462,7 @@ void linear_kernel(KArgs a) {
     const int cnt = total_tokens - slice < kSlice ? total_tokens - slice : kSlice;
     // Token slot j of this slice -> its x row and y row.
     auto xrow = [&](int j) -> int {
+      if (kGrouped == kDownCombine) return 2 * pairs[(slice + j) >> 1] + ((slice + j) & 1);
       if (kGrouped) return a.x_by_slot ? pairs[slice + j] : pairs[slice + j] / a.topk;
       return slice + j;
     };
@@ -431,7 +483,7 @@ void linear_kernel(KArgs a) {
       if (sl == 0) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const int64_t row = (tile0 + r) * 16 + i;
+          const int64_t row = tix[r] * 16 + i;
           if constexpr (kBits == 2) {
             rt[r].cbl = bload32(cbr, row < a.n ? (uint32_t)row * 4u : kOob);
             rt[r].cbh = 0u;
@@ -606,11 +658,65 @@ void linear_kernel(KArgs a) {
         if (kb == 0) {
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            const int64_t row = (tile0 + r) * 16 + i;
+            const int64_t row = tix[r] * 16 + i;
             if (row < a.n) {
 #pragma unroll
               for (int m = 0; m < NT; ++m)
                 if (m < cnt) a.y[(int64_t)yrow(m) * a.ldy + row] = dacc[r][m];
+            }
+          }
+        }
+      } else if constexpr (kGrouped == kSwiGLU) {
+        // D layout: lane l holds rows 4*(l/16)+v of the tile for token l%16; the
+        // gate and up tiles share it, so h is elementwise.  h goes out as a high
+        // bf16 term and the bf16 rounding of the remainder (exact in fp32).
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          const int j = 16 * c + i;
+          if (j < cnt && tix[0] < a.half_tiles) {
+            const int pair = pairs[slice + j];
+            uint32_t hi[2], lo[2];
+#pragma unroll
+            for (int v = 0; v < 4; v += 2) {
+              float hv[2];
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const float g = acc[0][c][v + e], u = acc[1][c][v + e];
+                hv[e] = g / (1.0f + expf(-g)) * u;
+              }
+              const bf16x2 h2 = {static_cast<__bf16>(hv[0]), static_cast<__bf16>(hv[1])};
+              const bf16x2 l2 = {static_cast<__bf16>(hv[0] - static_cast<float>(h2[0])),
+                                 static_cast<__bf16>(hv[1] - static_cast<float>(h2[1]))};
+              hi[v / 2] = __builtin_bit_cast(uint32_t, h2);
+              lo[v / 2] = __builtin_bit_cast(uint32_t, l2);
+            }
+            const int64_t col = tix[0] * 16 + 4 * kb;
+            uint16_t* hr = a.h + (int64_t)(2 * pair) * a.ldh + col;
+            *reinterpret_cast<u32x2*>(hr) = u32x2{hi[0], hi[1]};
+            *reinterpret_cast<u32x2*>(hr + a.ldh) = u32x2{lo[0], lo[1]};
+          }
+        }
+      } else if constexpr (kGrouped == kDownCombine) {
+        // Token columns 2p and 2p+1 are the two terms of pair p: add the
+        // neighbouring column, then the even lanes store the pair's outputs.
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          const int j = 16 * c + i;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            f32x4 v = acc[r][c];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], 1, 64);
+            const int64_t row0 = tix[r] * 16 + 4 * kb;
+            if (j < cnt && (i & 1) == 0) {
+              float* pr = a.part + (int64_t)pairs[(slice + j) >> 1] * a.ldp;
+              if (row0 + 3 < a.n) {
+                *reinterpret_cast<f32x4*>(pr + row0) = v;
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (row0 + e < a.n) pr[row0 + e] = v[e];
+              }
             }
           }
         }
@@ -623,7 +729,7 @@ void linear_kernel(KArgs a) {
             float* yr = a.y + (int64_t)yrow(j) * a.ldy;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-              const int64_t row0 = (tile0 + r) * 16 + 4 * kb;
+              const int64_t row0 = tix[r] * 16 + 4 * kb;
               if (a.vec_y && row0 + 3 < a.n) {
                 *reinterpret_cast<f32x4*>(yr + row0) = acc[r][c];
               } else {
@@ -637,6 +743,61 @@ void linear_kernel(KArgs a) {
       }
     }
     __syncthreads();   // LDS is rewritten by the next slice
+  }
+
+  if constexpr (kGrouped == kDownCombine) {
+    // Arrival: every thread's outputs are made visible at device scope, then
+    // one thread counts the block in.  The block that completes the count for
+    // this row range sums each token's slots in slot order (deterministic,
+    // whatever the arrival order) and clears the counter for the next launch.
+    // Nothing waits, so no block depends on another being resident.
+    __shared__ int last;
+    __shared__ float pw[64];
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned prev =
+          __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      last = prev + 1u == (unsigned)nexperts;
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    // Routing weights: softmax over each token's routed (in-range) logits.
+    if (tid < a.pairs_total) {
+      const int tk = tid / a.topk;
+      const int* row_ids = a.ids + tk * a.topk;
+      const float* lg = a.logits + (int64_t)tk * a.ld_logits;
+      float mx = -__builtin_inff();
+      for (int q = 0; q < a.topk; ++q) {
+        const int e = row_ids[q];
+        if (e >= 0 && e < a.num_experts) mx = fmaxf(mx, lg[e]);
+      }
+      float den = 0.f;
+      for (int q = 0; q < a.topk; ++q) {
+        const int e = row_ids[q];
+        if (e >= 0 && e < a.num_experts) den += expf(lg[e] - mx);
+      }
+      const int e = a.ids[tid];
+      pw[tid] = e >= 0 && e < a.num_experts ? expf(lg[e] - mx) / den : 0.f;
+    }
+    __syncthreads();
+    constexpr int kRows = 64 * 1;   // rows per block column: kW waves x R tiles x 16
+    static_assert(R == 1 && kW == 4, "the down pass takes one 16-row tile per wave, four waves");
+    const int64_t row_base = (int64_t)blockIdx.x * kRows;
+    for (int idx = tid; idx < a.t * kRows; idx += kThreads) {
+      const int tk = idx / kRows;
+      const int64_t row = row_base + (idx - tk * kRows);
+      if (row < a.n) {
+        float sum = 0.f;
+        for (int q = 0; q < a.topk; ++q) {
+          const int pi = tk * a.topk + q;
+          if (pw[pi] != 0.f) sum += pw[pi] * a.part[(int64_t)pi * a.ldp + row];
+        }
+        a.out[(int64_t)tk * a.ldo + row] = sum;
+      }
+    }
+    if (tid == 0) __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -799,7 +960,7 @@ size_t reduce_bytes(int vals, int r, int w) { return (size_t)w * r * vals * 64 *
 
 // Dynamic LDS above 64 KB must be allowed per kernel; raise each kernel's limit
 // once to the largest size this file ever requests.
-template <int NT, int R, int kW, bool kGrouped, int kMode, bool kDot, int kBits>
+template <int NT, int R, int kW, int kGrouped, int kMode, bool kDot, int kBits>
 hipError_t allow_lds(size_t bytes) {
   static std::atomic<size_t> allowed{64 * 1024};   // per kernel instantiation
   if (bytes <= allowed.load(std::memory_order_acquire)) return hipSuccess;
@@ -814,7 +975,7 @@ hipError_t allow_lds(size_t bytes) {
   return e;
 }
 
-template <int NT, int R, int kW, bool kGrouped, int kMode, bool kDot, int kBits>
+template <int NT, int R, int kW, int kGrouped, int kMode, bool kDot, int kBits>
 hipError_t launch_one(const KArgs& a, size_t shm, unsigned grid_y, hipStream_t s) {
   const int rb = kW / (kMode != kStream ? a.sk : 1);
   const int64_t tiles = (a.n + 15) / 16;
@@ -873,20 +1034,25 @@ Shape pick_shape(int64_t n, int groups, bool full_k, int tokens, bool dot) {
 #endif
 }
 
-template <int NT, int R, bool kGrouped, bool kDot, int kBits>
+template <int NT, int R, int kGrouped, bool kDot, int kBits>
 hipError_t launch_r(KArgs a, int w, int mode, size_t shm, unsigned grid_y, hipStream_t s) {
-  switch (mode) {
-    case kShared:
-      if (w == 8) return launch_one<NT, R, 8, kGrouped, kShared, kDot, kBits>(a, shm, grid_y, s);
-      return launch_one<NT, R, 4, kGrouped, kShared, kDot, kBits>(a, shm, grid_y, s);
-    default:
-      if (w == 8) return launch_one<NT, R, 8, kGrouped, kStream, kDot, kBits>(a, shm, grid_y, s);
-      return launch_one<NT, R, 4, kGrouped, kStream, kDot, kBits>(a, shm, grid_y, s);
+  if constexpr (kGrouped != kDense) {   // expert passes: four waves per block
+    if (mode == kShared) return launch_one<NT, R, 4, kGrouped, kShared, kDot, kBits>(a, shm, grid_y, s);
+    return launch_one<NT, R, 4, kGrouped, kStream, kDot, kBits>(a, shm, grid_y, s);
+  } else {
+    switch (mode) {
+      case kShared:
+        if (w == 8) return launch_one<NT, R, 8, kGrouped, kShared, kDot, kBits>(a, shm, grid_y, s);
+        return launch_one<NT, R, 4, kGrouped, kShared, kDot, kBits>(a, shm, grid_y, s);
+      default:
+        if (w == 8) return launch_one<NT, R, 8, kGrouped, kStream, kDot, kBits>(a, shm, grid_y, s);
+        return launch_one<NT, R, 4, kGrouped, kStream, kDot, kBits>(a, shm, grid_y, s);
+    }
   }
 }
 
 // tokens_in_slice: tokens the LDS staging holds at once.
-template <int NT, bool kGrouped, bool kDot, int kBits = 3>
+template <int NT, int kGrouped, bool kDot, int kBits = 3>
 hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t s) {
   constexpr int kSlice = kDot ? NT : 16 * NT;
   const size_t fk = full_k_bytes(tokens_in_slice, a.G);
@@ -894,7 +1060,8 @@ hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t
 #if defined(Q3_FORCE_R) && defined(Q3_FORCE_W) && defined(Q3_FORCE_SK)
   const Shape sh = pick_shape(a.n, a.G, full_k, tokens_in_slice, kDot);
 #else
-  const Shape sh = kGrouped ? Shape{1, 4, 1} : pick_shape(a.n, a.G, full_k, tokens_in_slice, kDot);
+  const Shape sh = kGrouped ? Shape{kGrouped == kSwiGLU ? 2 : 1, 4, 1}
+                            : pick_shape(a.n, a.G, full_k, tokens_in_slice, kDot);
 #endif
   a.sk = full_k ? sh.sk : 1;
   const int steps = (((a.G + 3) & ~3) + 15) / 16;
@@ -913,7 +1080,9 @@ hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t
     const size_t red = reduce_bytes(kDot ? NT : 4 * NT, sh.r, sh.w);
     if (shm < red) shm = red;
   }
-  if constexpr (kGrouped || kDot) {
+  if constexpr (kGrouped == kSwiGLU) {
+    return launch_r<NT, 2, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, s);
+  } else if constexpr (kGrouped || kDot) {
     return launch_r<NT, 1, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, s);
   } else {
     switch (sh.r) {
@@ -947,10 +1116,10 @@ hipError_t launch_gemm_small_m(const PlaneView& w, const uint16_t* x, int64_t m,
   a.m = (int)m;
   a.x_rows = m;
   a.vec_y = ((uintptr_t)y % 16 == 0) && (ldy % 4 == 0);
-  if (m <= 16) return launch_cfg<1, false, false>(a, (int)m, 1, s);
-  if (m <= 32) return launch_cfg<2, false, false>(a, (int)m, 1, s);
-  if (m <= 48) return launch_cfg<3, false, false>(a, (int)m, 1, s);
-  return launch_cfg<4, false, false>(a, (int)m, 1, s);
+  if (m <= 16) return launch_cfg<1, kDense, false>(a, (int)m, 1, s);
+  if (m <= 32) return launch_cfg<2, kDense, false>(a, (int)m, 1, s);
+  if (m <= 48) return launch_cfg<3, kDense, false>(a, (int)m, 1, s);
+  return launch_cfg<4, kDense, false>(a, (int)m, 1, s);
 }
 
 hipError_t launch_head2_scores(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
@@ -964,7 +1133,7 @@ hipError_t launch_head2_scores(const PlaneView& w, const uint16_t* x, int64_t m,
   a.m = (int)m;
   a.x_rows = m;
   a.vec_y = ((uintptr_t)y % 16 == 0) && (ldy % 4 == 0);
-  return launch_cfg<1, false, false, 2>(a, (int)m, 1, s);
+  return launch_cfg<1, kDense, false, 2>(a, (int)m, 1, s);
 }
 
 hipError_t launch_gemv(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
@@ -978,14 +1147,14 @@ hipError_t launch_gemv(const PlaneView& w, const uint16_t* x, int64_t m, int64_t
   a.m = (int)m;
   a.x_rows = m;
   switch (m) {
-    case 1: return launch_cfg<1, false, true>(a, 1, 1, s);
-    case 2: return launch_cfg<2, false, true>(a, 2, 1, s);
-    case 3: return launch_cfg<3, false, true>(a, 3, 1, s);
-    case 4: return launch_cfg<4, false, true>(a, 4, 1, s);
-    case 5: return launch_cfg<5, false, true>(a, 5, 1, s);
-    case 6: return launch_cfg<6, false, true>(a, 6, 1, s);
-    case 7: return launch_cfg<7, false, true>(a, 7, 1, s);
-    case 8: return launch_cfg<8, false, true>(a, 8, 1, s);
+    case 1: return launch_cfg<1, kDense, true>(a, 1, 1, s);
+    case 2: return launch_cfg<2, kDense, true>(a, 2, 1, s);
+    case 3: return launch_cfg<3, kDense, true>(a, 3, 1, s);
+    case 4: return launch_cfg<4, kDense, true>(a, 4, 1, s);
+    case 5: return launch_cfg<5, kDense, true>(a, 5, 1, s);
+    case 6: return launch_cfg<6, kDense, true>(a, 6, 1, s);
+    case 7: return launch_cfg<7, kDense, true>(a, 7, 1, s);
+    case 8: return launch_cfg<8, kDense, true>(a, 8, 1, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1008,7 +1177,53 @@ hipError_t launch_grouped(const ExpertView& w, const uint16_t* x, int64_t ldx, i
   a.vec_y = ((uintptr_t)y % 16 == 0) && (ldy % 4 == 0);
   a.x_rows = x_by_slot ? (int64_t)t * topk : t;
   const int slice = a.pairs_total < 16 ? a.pairs_total : 16;
-  return launch_cfg<1, true, false>(a, slice, (unsigned)w.num_experts, s);
+  return launch_cfg<1, kExperts, false>(a, slice, (unsigned)w.num_experts, s);
+}
+
+int moe_mlp_row_blocks(int64_t n_dn) { return (int)((n_dn + 63) / 64); }
+
+hipError_t launch_moe_mlp(const ExpertView& gu, const ExpertView& dn, const uint16_t* x, int64_t ldx,
+                          const int32_t* ids, int32_t t, int32_t topk, const float* logits, int64_t ld_logits,
+                          uint16_t* h, float* part, int64_t ldp, uint32_t* counters, float* out, int64_t ldo,
+                          hipStream_t s) {
+  const int pairs = t * topk;
+  const int64_t inter = gu.base.n / 2;
+  KArgs a = base_args(gu.base);
+  a.code_stride = gu.code_stride;
+  a.scale_stride = gu.scale_stride;
+  a.cb_stride = gu.cb_stride;
+  a.x = x;
+  a.ldx = ldx;
+  a.x_rows = t;
+  a.ids = ids;
+  a.pairs_total = pairs;
+  a.topk = topk;
+  a.num_experts = gu.num_experts;
+  a.half_tiles = (int)(inter / 16);
+  a.h = h;
+  a.ldh = inter;
+  hipError_t e = launch_cfg<1, kSwiGLU, false>(a, pairs < 16 ? pairs : 16, (unsigned)gu.num_experts, s);
+  if (e != hipSuccess) return e;
+  KArgs b = base_args(dn.base);
+  b.code_stride = dn.code_stride;
+  b.scale_stride = dn.scale_stride;
+  b.cb_stride = dn.cb_stride;
+  b.x = h;
+  b.ldx = inter;
+  b.x_rows = 2 * (int64_t)pairs;
+  b.ids = ids;
+  b.pairs_total = pairs;
+  b.topk = topk;
+  b.num_experts = dn.num_experts;
+  b.part = part;
+  b.ldp = ldp;
+  b.counters = counters;
+  b.logits = logits;
+  b.ld_logits = ld_logits;
+  b.out = out;
+  b.ldo = ldo;
+  b.t = t;
+  return launch_cfg<1, kDownCombine, false>(b, 2 * pairs < 16 ? 2 * pairs : 16, (unsigned)dn.num_experts, s);
 }
 
 }  // namespace q3

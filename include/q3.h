@@ -186,6 +186,35 @@ Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t
                                         int32_t x_by_slot, const int32_t* topk_ids, int32_t t,
                                         int32_t topk, float* y, int64_t ldy, void* stream);
 
+/* Fused expert MLP of one verify round (Hibana page, "Adaptive speculation",
+ * "Expert sharing": the experts a round reads, each run as its MLP on the
+ * tokens routed to it).  Readings of the page, which gives no MLP detail:
+ *   gate_up: per expert [gate rows 0..I-1; up rows I..2I-1] x K_in (n = 2I);
+ *   down:    per expert H x I (k = I);
+ *   h[i][j]  = silu(gate . x[i]) * (up . x[i]), silu(z) = z / (1 + e^-z), for
+ *              expert e = topk_ids[i][j]; carried into the down product as two
+ *              bf16 terms (|h - hi - lo| <= 2^-17 |h|), not rounded to bf16;
+ *   out[i][:] = sum_j p[i][j] * (down_e . h[i][j]), p[i] = softmax over token
+ *              i's routed logits logits[i][topk_ids[i][j]] (its top-k
+ *              probabilities renormalised to sum 1).
+ * x bf16 [t][ldx]; logits fp32 [t][ld_logits] (the router's, e.g. the input of
+ * q3_moe_topk or q3_moe_budget_topk); out fp32 [t][ldo].  Ids outside
+ * [0, num_experts) are skipped (weight 0, excluded from the softmax); a token
+ * with none in range gets 0, and a round with none in range writes nothing.
+ * Two launches, no host synchronisation; only experts that appear in
+ * topk_ids are read, each once per matrix.
+ * Shapes: gate_up.n % 64 == 0, down.k == gate_up.n / 2, same num_experts,
+ * 1 <= t*topk <= 64.
+ * workspace: device memory of at least q3_moe_mlp_workspace_bytes(...) bytes,
+ * 256-byte aligned, all zero before its first use; every call leaves its
+ * counters zero again, so one workspace serves any number of calls in stream
+ * order.  Calls that overlap in time must not share a workspace. */
+Q3_API int64_t q3_moe_mlp_workspace_bytes(int64_t n_gu, int64_t n_dn, int32_t t, int32_t topk);
+Q3_API q3_status q3_moe_mlp(const q3_expert_stack* gate_up, const q3_expert_stack* down, const uint16_t* x,
+                            int64_t ldx, const int32_t* topk_ids, int32_t t, int32_t topk, const float* logits,
+                            int64_t ld_logits, void* workspace, int64_t workspace_bytes, float* out, int64_t ldo,
+                            void* stream);
+
 /* ---- Two-bit draft head ------------------------------------------------------
  * (Hibana page, "Model surgery" / "Two-bit draft head": the drafter's output
  * head scores every vocabulary token; a 2-bit copy of it shortlists candidates

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
                                          "q3_gemm_small_m", "q3_moe_topk", "q3_grouped_expert_gemv",
                                          "q3_layout2", "q3_pack2", "q3_unpack2", "q3_head2_scores",
                                          "q3_shortlist_workspace_bytes", "q3_shortlist", "q3_rescore_fp8",
-                                         "q3_draft_head_workspace_bytes", "q3_draft_head", "q3_moe_budget_topk"])
+                                         "q3_draft_head_workspace_bytes", "q3_draft_head", "q3_moe_budget_topk",
+                                         "q3_moe_mlp_workspace_bytes", "q3_moe_mlp"])
 
 
 def test_library_exports_every_declared_symbol(q3lib):
@@ -72,6 +73,12 @@ def test_workspace_sizes(q3lib):
     # draft head: fp32 scores [m][n] (rounded up to 8 bytes), then the shortlist scratch
     assert q3lib.q3_draft_head_workspace_bytes(1, 151936) == 151936 * 4 + 64 * 16 * 8
     assert q3lib.q3_draft_head_workspace_bytes(3, 5) == 64 + 3 * 64 * 16 * 8
+    # fused MLP: h (bf16, two terms per pair, I = n_gu / 2), per-pair fp32 outputs
+    # (rows padded to 4), one counter per 64 down rows; each piece 256-aligned
+    assert q3lib.q3_moe_mlp_workspace_bytes(1536, 2048, 8, 8) == 2 * 64 * 768 * 2 + 64 * 2048 * 4 + 256
+    assert q3lib.q3_moe_mlp_workspace_bytes(64, 30, 1, 1) == 256 + 256 + 256
+    assert q3lib.q3_moe_mlp_workspace_bytes(1536, 2048, 9, 8) == 0      # more than 64 pairs
+    assert q3lib.q3_moe_mlp_workspace_bytes(1504, 2048, 8, 8) == 0      # I not a multiple of 32
 
 
 def test_head_validation_rejects_before_any_hip_call(q3lib):
@@ -148,3 +155,17 @@ def test_validation_rejects_before_any_hip_call(q3lib):
     assert q3lib.q3_grouped_expert_gemv(ctypes.byref(st), fake, 64, 0, fake, 8, 8, fake, 16, None) == 1
     st.code_expert_stride = 776                                                     # not 16-aligned
     assert q3lib.q3_grouped_expert_gemv(ctypes.byref(st), fake, 64, 0, fake, 8, 8, fake, 16, None) == 3
+    # fused MLP: gate/up n = 64 (I = 32), k = 64; down n = 16, k = 32
+    gu = _lib.Q3ExpertStack(4, 64, 64, fake, 3072, fake, 256, fake, 512)
+    dn = _lib.Q3ExpertStack(4, 16, 32, fake, 768, fake, 64, fake, 128)
+    ws = q3lib.q3_moe_mlp_workspace_bytes(64, 16, 2, 2)
+    mlp = lambda g, d, t=2, topk=2, logits=fake, wsp=fake, wsb=ws: q3lib.q3_moe_mlp(
+        ctypes.byref(g), ctypes.byref(d), fake, 64, fake, t, topk, logits, 4, wsp, wsb, fake, 16, None)
+    assert mlp(gu, dn, logits=None) == 1
+    assert mlp(gu, dn, t=33) == 2                                                   # 66 pairs
+    assert mlp(gu, dn, wsb=ws - 1) == 1                                             # workspace too small
+    assert mlp(gu, dn, wsp=fake + 16) == 3                                          # workspace not 256-aligned
+    dn.k = 64
+    assert mlp(gu, dn) == 2                                                         # down k != I
+    dn.k, dn.num_experts = 32, 3
+    assert mlp(gu, dn) == 1                                                         # expert counts differ

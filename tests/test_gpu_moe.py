@@ -193,3 +193,143 @@ def test_budget_round_feeds_grouped_products(q3):
     ref, b = oracle.grouped_linear(planes(moe.experts_gu), ref_ids, moe.x, False)
     assert_close(y, ref.reshape(y.shape), b.reshape(y.shape), "budget gate/up")
     assert oracle.expert_union(ref_ids).size <= 6
+
+
+# Fused expert MLP (gate/up with SwiGLU, down with the routing-weight combine)
+# against the oracle's fp64 composition, within 1e-3 of each output's
+# first-order bound.  Random-sign rounds check every path; rounds on positive
+# codebooks and activations, where the bound is within a small factor of the
+# output itself, make that tolerance a sharp one; negative gate rows put the
+# SwiGLU on both sides of zero.
+def _mlp_planes(layers):
+    return [(*oracle.pack(L.codes, L.scales), L.codebook, L.n, L.k) for L in layers]
+
+
+def _sign_fixed(moe, gate_negative=False):
+    """Positive codebooks and activations; optionally negative gate rows on even experts."""
+    moe.x = moe.x & np.uint16(0x7FFF)
+    for e, L in enumerate(moe.experts_gu):
+        L.codebook = L.codebook & np.uint8(0x7F)
+        if gate_negative and e % 2 == 0:
+            L.codebook[: L.n // 2] |= np.uint8(0x80)
+    for L in moe.experts_dn:
+        L.codebook = L.codebook & np.uint8(0x7F)
+    return moe
+
+
+def _run_mlp(q3, moe, ids, rows=None, ws=None, logits=None):
+    logits = moe.logits if logits is None else logits
+    st_gu, st_dn = stack_experts(q3, moe.experts_gu), stack_experts(q3, moe.experts_dn)
+    out = q3.q3_moe_mlp(st_gu, st_dn, dev(moe.x), dev(ids), dev(logits), ws).cpu().numpy()
+    ref, bound = oracle.moe_mlp(_mlp_planes(moe.experts_gu), _mlp_planes(moe.experts_dn), ids, logits, moe.x,
+                                rows=rows)
+    if rows is not None:
+        out = out[:, rows]
+    return out, ref, bound
+
+
+@pytest.mark.parametrize("E,k_gu,n_gu,n_dn,t,topk,sign", [
+    (6, 64, 64, 40, 3, 2, "random"),          # one block column, ragged down rows
+    (16, 256, 192, 130, 8, 4, "random"),      # I = 96: a half-empty gate/up block; 3 down columns
+    (16, 256, 192, 130, 8, 4, "positive"),
+    (8, 512, 128, 200, 5, 3, "gate_negative"),
+    (4, 96, 64, 64, 1, 1, "positive"),        # one pair
+    (12, 128, 256, 96, 16, 4, "positive"),    # 64 pairs
+])
+def test_moe_mlp_matches_oracle(q3, E, k_gu, n_gu, n_dn, t, topk, sign):
+    moe = synth.make_moe(num_experts=E, k_gu=k_gu, n_gu=n_gu, k_dn=n_gu // 2, n_dn=n_dn, tokens=t, topk=topk,
+                         seed=E + t + n_dn)
+    if sign != "random":
+        _sign_fixed(moe, gate_negative=sign == "gate_negative")
+    ids = oracle.topk_route(moe.logits, topk)
+    out, ref, bound = _run_mlp(q3, moe, ids)
+    ratio = assert_close(out, ref, bound, f"moe mlp {sign}")
+    if sign == "positive":
+        assert np.all(bound <= 4 * np.abs(ref))   # the tolerance is within 0.4% of each output
+    assert ratio < 1e-5
+
+
+def test_moe_mlp_many_pairs_on_one_expert(q3):
+    """64 tokens on one expert: four 16-token slices in gate/up, eight in down."""
+    moe = _sign_fixed(synth.make_moe(num_experts=4, k_gu=128, n_gu=64, k_dn=32, n_dn=72, tokens=64, topk=1,
+                                     seed=8))
+    moe.logits[:, 2] += 10.0
+    ids = oracle.topk_route(moe.logits, 1)
+    assert np.all(ids == 2)
+    out, ref, bound = _run_mlp(q3, moe, ids)
+    assert_close(out, ref, bound, "one expert, 64 tokens")
+
+
+def test_moe_mlp_config2_full_size(q3):
+    """64 experts, gate/up 2048 -> 2 x 768, down 768 -> 2048, 8 drafted tokens x
+    top-8, plain and budgeted routes; sampled output rows (all of h is computed)."""
+    moe = synth.make_moe(seed=0)
+    rows = np.sort(np.concatenate([np.random.default_rng(4).choice(2048, 46, replace=False), [0, 2047]]))
+    for ids in (oracle.topk_route(moe.logits, 8), oracle.budget_route(moe.logits, 8, 16)[1]):
+        out, ref, bound = _run_mlp(q3, moe, ids, rows=rows)
+        assert_close(out, ref, bound, "config 2 fused MLP")
+
+
+def test_moe_mlp_workspace_reuse_and_determinism(q3):
+    """The counters are left zero: one workspace serves consecutive rounds with
+    different routes; repeated rounds are bitwise identical."""
+    moe = synth.make_moe(num_experts=16, k_gu=256, n_gu=192, k_dn=96, n_dn=130, tokens=8, topk=4, seed=21)
+    st_gu, st_dn = stack_experts(q3, moe.experts_gu), stack_experts(q3, moe.experts_dn)
+    ws = q3.moe_mlp_workspace(st_gu, st_dn, 8, 4, "cuda")
+    pl_gu, pl_dn = _mlp_planes(moe.experts_gu), _mlp_planes(moe.experts_dn)
+    x, logits = dev(moe.x), dev(moe.logits)
+    first = None
+    for rnd, budget in enumerate((None, 6, None, 4)):
+        ids = oracle.topk_route(moe.logits, 4) if budget is None else oracle.budget_route(moe.logits, 4, budget)[1]
+        out = q3.q3_moe_mlp(st_gu, st_dn, x, dev(ids), logits, ws).cpu().numpy()
+        ref, bound = oracle.moe_mlp(pl_gu, pl_dn, ids, moe.logits, moe.x)
+        assert_close(out, ref, bound, f"round {rnd}")
+        if budget is None:
+            if first is None:
+                first = out
+            else:
+                assert np.array_equal(out, first)
+        counters = ws[-256:].cpu().numpy()
+        assert not counters.any()
+
+
+def test_moe_mlp_skips_out_of_range_ids(q3):
+    moe = synth.make_moe(num_experts=6, k_gu=64, n_gu=64, k_dn=32, n_dn=40, tokens=3, topk=2, seed=13)
+    ids = oracle.topk_route(moe.logits, 2)
+    bad = ids.copy()
+    bad[0, 1] = -1                  # token 0 keeps only its first expert (weight 1)
+    bad[2, :] = 6                   # token 2 has none in range: its output is 0
+    st_gu, st_dn = stack_experts(q3, moe.experts_gu), stack_experts(q3, moe.experts_dn)
+    out = q3.q3_moe_mlp(st_gu, st_dn, dev(moe.x), dev(bad), dev(moe.logits)).cpu().numpy()
+    pl_gu, pl_dn = _mlp_planes(moe.experts_gu), _mlp_planes(moe.experts_dn)
+    r0, b0 = oracle.moe_mlp(pl_gu, pl_dn, ids[:1, :1], moe.logits[:1], moe.x[:1])
+    r1, b1 = oracle.moe_mlp(pl_gu, pl_dn, ids[1:2], moe.logits[1:2], moe.x[1:2])
+    assert_close(out[:1], r0, b0, "token 0, one slot")
+    assert_close(out[1:2], r1, b1, "token 1")
+    assert not out[2].any()
+
+
+def test_moe_mlp_graph_replays(q3):
+    """Captured in a graph, every replay (with eager work between) equals the eager result."""
+    moe = synth.make_moe(num_experts=16, k_gu=256, n_gu=192, k_dn=96, n_dn=130, tokens=8, topk=4, seed=22)
+    st_gu, st_dn = stack_experts(q3, moe.experts_gu), stack_experts(q3, moe.experts_dn)
+    ws = q3.moe_mlp_workspace(st_gu, st_dn, 8, 4, "cuda")
+    x, ids, logits = dev(moe.x), dev(oracle.topk_route(moe.logits, 4)), dev(moe.logits)
+    eager = q3.q3_moe_mlp(st_gu, st_dn, x, ids, logits, ws).cpu().numpy()
+    out = torch.zeros((8, 130), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        q3.q3_moe_mlp(st_gu, st_dn, x, ids, logits, ws, out)
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            q3.q3_moe_mlp(st_gu, st_dn, x, ids, logits, ws, out)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager)
+        q3.q3_moe_mlp(st_gu, st_dn, x, ids, logits, ws)      # eager work between replays
+        torch.cuda.synchronize()
