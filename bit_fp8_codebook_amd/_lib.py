@@ -298,11 +298,11 @@ def q3_grouped_expert_gemv(stack: ExpertStack, x: torch.Tensor, topk_ids: torch.
 
 
 def moe_mlp_workspace(gate_up: ExpertStack, down: ExpertStack, t: int, topk: int, device) -> torch.Tensor:
-    """Zeroed workspace for q3_moe_mlp (reusable across calls in stream order)."""
+    """Workspace for q3_moe_mlp (reusable across calls in stream order)."""
     nbytes = lib().q3_moe_mlp_workspace_bytes(gate_up.n, down.n, t, topk)
     if nbytes <= 0:
         raise ValueError("unsupported fused-MLP shape")
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 def q3_moe_mlp(gate_up: ExpertStack, down: ExpertStack, x: torch.Tensor, topk_ids: torch.Tensor,

@@ -235,13 +235,12 @@ q3::ExpertView view_of(const q3_expert_stack* w) {
   return v;
 }
 
-// Fused MLP workspace: h (bf16 [2*pairs][I]), part (fp32 [pairs][ldp]),
-// counters (uint32 per 64 down rows), each piece 256-byte aligned.
+// Fused MLP workspace: h (bf16 [2*pairs][I]) and part (fp32 [pairs][ldp]),
+// each 256-byte aligned.
 int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 int64_t mlp_ldp(int64_t n_dn) { return (n_dn + 3) / 4 * 4; }
 int64_t mlp_h_bytes(int64_t pairs, int64_t inter) { return align256(2 * pairs * inter * 2); }
 int64_t mlp_part_bytes(int64_t pairs, int64_t n_dn) { return align256(pairs * mlp_ldp(n_dn) * 4); }
-int64_t mlp_counter_bytes(int64_t n_dn) { return align256(4 * (int64_t)q3::moe_mlp_row_blocks(n_dn)); }
 
 }  // namespace
 
@@ -263,7 +262,7 @@ Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t
 Q3_API int64_t q3_moe_mlp_workspace_bytes(int64_t n_gu, int64_t n_dn, int32_t t, int32_t topk) {
   if (n_gu < 32 || n_gu % 64 || n_dn < 1 || t < 1 || topk < 1 || int64_t(t) * topk > 64) return 0;
   const int64_t pairs = int64_t(t) * topk;
-  return mlp_h_bytes(pairs, n_gu / 2) + mlp_part_bytes(pairs, n_dn) + mlp_counter_bytes(n_dn);
+  return mlp_h_bytes(pairs, n_gu / 2) + mlp_part_bytes(pairs, n_dn);
 }
 
 Q3_API q3_status q3_moe_mlp(const q3_expert_stack* gate_up, const q3_expert_stack* down, const uint16_t* x,
@@ -287,11 +286,8 @@ Q3_API q3_status q3_moe_mlp(const q3_expert_stack* gate_up, const q3_expert_stac
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint16_t* h = reinterpret_cast<uint16_t*>(ws);
   float* part = reinterpret_cast<float*>(ws + mlp_h_bytes(pairs, gate_up->n / 2));
-  uint32_t* counters =
-      reinterpret_cast<uint32_t*>(ws + mlp_h_bytes(pairs, gate_up->n / 2) + mlp_part_bytes(pairs, down->n));
   return from_hip(q3::launch_moe_mlp(view_of(gate_up), view_of(down), x, ldx, topk_ids, t, topk, logits, ld_logits,
-                                     h, part, mlp_ldp(down->n), counters, out, ldo,
-                                     static_cast<hipStream_t>(stream)));
+                                     h, part, mlp_ldp(down->n), out, ldo, static_cast<hipStream_t>(stream)));
 }
 
 Q3_API q3_status q3_layout2(int64_t n, int64_t k, q3_layout_info* out) {

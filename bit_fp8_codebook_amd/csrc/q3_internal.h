@@ -70,14 +70,17 @@ struct ExpertView {
 hipError_t launch_grouped(const ExpertView& w, const uint16_t* x, int64_t ldx, int32_t x_by_slot,
                           const int32_t* ids, int32_t t, int32_t topk, float* y, int64_t ldy, hipStream_t s);
 
-// Fused expert MLP of a verify round, two launches: gate/up with SwiGLU into
-// h (bf16 [2*pairs][I], high and low term per pair), then down with the
-// routing-weight combine through part (fp32 [pairs][ldp]) and counters
-// (moe_mlp_row_blocks(n_dn) words, zero before and after).
-int moe_mlp_row_blocks(int64_t n_dn);
+// Routing-weight combine: out[i][r] = sum_j p[i][j] * part[i*topk + j][r], p[i]
+// the softmax of token i's routed (in-range) logits; slots in slot order.
+hipError_t launch_moe_combine(const float* part, int64_t ldp, const int32_t* ids, int32_t t, int32_t topk,
+                              int32_t num_experts, const float* logits, int64_t ld_logits, int64_t n, float* out,
+                              int64_t ldo, hipStream_t s);
+
+// Fused expert MLP of a verify round, three launches: gate/up with SwiGLU into
+// h (bf16 [2*pairs][I], high and low term per pair), down into part (fp32
+// [pairs][ldp]), then the combine.
 hipError_t launch_moe_mlp(const ExpertView& gu, const ExpertView& dn, const uint16_t* x, int64_t ldx,
                           const int32_t* ids, int32_t t, int32_t topk, const float* logits, int64_t ld_logits,
-                          uint16_t* h, float* part, int64_t ldp, uint32_t* counters, float* out, int64_t ldo,
-                          hipStream_t s);
+                          uint16_t* h, float* part, int64_t ldp, float* out, int64_t ldo, hipStream_t s);
 
 }  // namespace q3

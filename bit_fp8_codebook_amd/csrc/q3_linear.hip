@@ -63,9 +63,9 @@ enum Grouping : int {
   kExperts = 1,       // grid row e: the (token, slot) pairs routed to expert e
   kSwiGLU = 2,        // as kExperts on a gate/up matrix [gate I rows; up I rows]: a wave takes
                       // gate tile q and up tile q and writes h = silu(g) * u as two bf16 terms
-  kDownCombine = 3,   // as kExperts with each pair's activation given as two bf16 rows (high
-                      // and low term); the block adds the terms, and the last block of each
-                      // row range to finish combines every token's slots by routing weight
+  kDownTerms = 3,     // as kExperts with each pair's activation given as two bf16 rows (high
+                      // and low term): the block adds the two products and stores one output
+                      // row per pair
 };
 
 struct KArgs {
@@ -92,16 +92,9 @@ struct KArgs {
   int half_tiles;
   uint16_t* h;
   int64_t ldh;
-  // kDownCombine: per-pair outputs, arrival counters (one per block column, zero
-  // before and after a launch), router logits and the combined output
+  // kDownTerms: per-pair outputs
   float* part;
   int64_t ldp;
-  uint32_t* counters;
-  const float* logits;
-  int64_t ld_logits;
-  float* out;
-  int64_t ldo;
-  int t;
 };
 
 __device__ __forceinline__ bf16x8 pack_bf16x8(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
@@ -378,7 +371,6 @@ void linear_kernel(KArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int pairs[64];
   __shared__ int npairs;
-  __shared__ int nexperts;   // kDownCombine: in-range experts of the round
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -400,22 +392,12 @@ void linear_kernel(KArgs a) {
       const unsigned long long mask = __ballot(match);
       if (match) pairs[__popcll(mask & ((1ull << tid) - 1ull))] = tid;
       if (tid == 0) npairs = __popcll(mask);
-      if constexpr (kGrouped == kDownCombine) {
-        // The blocks of one row range that will arrive: one per distinct in-range expert.
-        bool first = id >= 0 && id < a.num_experts;
-        for (int o = 0; o < 64; ++o) {
-          const int other = __shfl(id, o, 64);
-          if (o < tid && other == id) first = false;
-        }
-        const unsigned long long fm = __ballot(first);
-        if (tid == 0) nexperts = __popcll(fm);
-      }
     }
     __syncthreads();
     if (npairs == 0) return;   // not picked this round: no weight byte is read
   }
   const int total_tokens =
-      kGrouped == kDownCombine ? 2 * __builtin_amdgcn_readfirstlane(npairs)
+      kGrouped == kDownTerms ? 2 * __builtin_amdgcn_readfirstlane(npairs)
                              : (kGrouped ? __builtin_amdgcn_readfirstlane(npairs) : a.m);
 
   const int G = a.G;
@@ -462,7 +444,7 @@ void linear_kernel(KArgs a) {
     const int cnt = total_tokens - slice < kSlice ? total_tokens - slice : kSlice;
     // Token slot j of this slice -> its x row and y row.
     auto xrow = [&](int j) -> int {
-      if (kGrouped == kDownCombine) return 2 * pairs[(slice + j) >> 1] + ((slice + j) & 1);
+      if (kGrouped == kDownTerms) return 2 * pairs[(slice + j) >> 1] + ((slice + j) & 1);
       if (kGrouped) return a.x_by_slot ? pairs[slice + j] : pairs[slice + j] / a.topk;
       return slice + j;
     };
@@ -696,7 +678,7 @@ void linear_kernel(KArgs a) {
             *reinterpret_cast<u32x2*>(hr + a.ldh) = u32x2{lo[0], lo[1]};
           }
         }
-      } else if constexpr (kGrouped == kDownCombine) {
+      } else if constexpr (kGrouped == kDownTerms) {
         // Token columns 2p and 2p+1 are the two terms of pair p: add the
         // neighbouring column, then the even lanes store the pair's outputs.
 #pragma unroll
@@ -743,61 +725,6 @@ void linear_kernel(KArgs a) {
       }
     }
     __syncthreads();   // LDS is rewritten by the next slice
-  }
-
-  if constexpr (kGrouped == kDownCombine) {
-    // Arrival: every thread's outputs are made visible at device scope, then
-    // one thread counts the block in.  The block that completes the count for
-    // this row range sums each token's slots in slot order (deterministic,
-    // whatever the arrival order) and clears the counter for the next launch.
-    // Nothing waits, so no block depends on another being resident.
-    __shared__ int last;
-    __shared__ float pw[64];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned prev =
-          __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      last = prev + 1u == (unsigned)nexperts;
-    }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    // Routing weights: softmax over each token's routed (in-range) logits.
-    if (tid < a.pairs_total) {
-      const int tk = tid / a.topk;
-      const int* row_ids = a.ids + tk * a.topk;
-      const float* lg = a.logits + (int64_t)tk * a.ld_logits;
-      float mx = -__builtin_inff();
-      for (int q = 0; q < a.topk; ++q) {
-        const int e = row_ids[q];
-        if (e >= 0 && e < a.num_experts) mx = fmaxf(mx, lg[e]);
-      }
-      float den = 0.f;
-      for (int q = 0; q < a.topk; ++q) {
-        const int e = row_ids[q];
-        if (e >= 0 && e < a.num_experts) den += expf(lg[e] - mx);
-      }
-      const int e = a.ids[tid];
-      pw[tid] = e >= 0 && e < a.num_experts ? expf(lg[e] - mx) / den : 0.f;
-    }
-    __syncthreads();
-    constexpr int kRows = 64 * 1;   // rows per block column: kW waves x R tiles x 16
-    static_assert(R == 1 && kW == 4, "the down pass takes one 16-row tile per wave, four waves");
-    const int64_t row_base = (int64_t)blockIdx.x * kRows;
-    for (int idx = tid; idx < a.t * kRows; idx += kThreads) {
-      const int tk = idx / kRows;
-      const int64_t row = row_base + (idx - tk * kRows);
-      if (row < a.n) {
-        float sum = 0.f;
-        for (int q = 0; q < a.topk; ++q) {
-          const int pi = tk * a.topk + q;
-          if (pw[pi] != 0.f) sum += pw[pi] * a.part[(int64_t)pi * a.ldp + row];
-        }
-        a.out[(int64_t)tk * a.ldo + row] = sum;
-      }
-    }
-    if (tid == 0) __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1034,11 +961,29 @@ Shape pick_shape(int64_t n, int groups, bool full_k, int tokens, bool dot) {
 #endif
 }
 
+// Block shape of the expert passes: one 16-row tile (two for the SwiGLU pass)
+// per wave, four waves, the whole K per wave.
+#ifdef Q3_EXPERT_SK
+constexpr int kExpertSplitK = Q3_EXPERT_SK;
+#else
+constexpr int kExpertSplitK = 1;
+#endif
+#ifdef Q3_EXPERT_W
+constexpr int kExpertWaves = Q3_EXPERT_W;
+#else
+constexpr int kExpertWaves = 4;
+#endif
+#ifdef Q3_EXPERT_STREAM
+constexpr bool kExpertStream = true;
+#else
+constexpr bool kExpertStream = false;
+#endif
+
 template <int NT, int R, int kGrouped, bool kDot, int kBits>
 hipError_t launch_r(KArgs a, int w, int mode, size_t shm, unsigned grid_y, hipStream_t s) {
-  if constexpr (kGrouped != kDense) {   // expert passes: four waves per block
-    if (mode == kShared) return launch_one<NT, R, 4, kGrouped, kShared, kDot, kBits>(a, shm, grid_y, s);
-    return launch_one<NT, R, 4, kGrouped, kStream, kDot, kBits>(a, shm, grid_y, s);
+  if constexpr (kGrouped != kDense) {   // expert passes: one block shape
+    if (mode == kShared) return launch_one<NT, R, kExpertWaves, kGrouped, kShared, kDot, kBits>(a, shm, grid_y, s);
+    return launch_one<NT, R, kExpertWaves, kGrouped, kStream, kDot, kBits>(a, shm, grid_y, s);
   } else {
     switch (mode) {
       case kShared:
@@ -1051,18 +996,15 @@ hipError_t launch_r(KArgs a, int w, int mode, size_t shm, unsigned grid_y, hipSt
   }
 }
 
+
 // tokens_in_slice: tokens the LDS staging holds at once.
 template <int NT, int kGrouped, bool kDot, int kBits = 3>
 hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t s) {
   constexpr int kSlice = kDot ? NT : 16 * NT;
   const size_t fk = full_k_bytes(tokens_in_slice, a.G);
-  const bool full_k = fk <= (size_t)kFullKBudget;
-#if defined(Q3_FORCE_R) && defined(Q3_FORCE_W) && defined(Q3_FORCE_SK)
-  const Shape sh = pick_shape(a.n, a.G, full_k, tokens_in_slice, kDot);
-#else
-  const Shape sh = kGrouped ? Shape{kGrouped == kSwiGLU ? 2 : 1, 4, 1}
+  const bool full_k = fk <= (size_t)kFullKBudget && !(kGrouped && kExpertStream);
+  const Shape sh = kGrouped ? Shape{kGrouped == kSwiGLU ? 2 : 1, kExpertWaves, kExpertSplitK}
                             : pick_shape(a.n, a.G, full_k, tokens_in_slice, kDot);
-#endif
   a.sk = full_k ? sh.sk : 1;
   const int steps = (((a.G + 3) & ~3) + 15) / 16;
   while (a.sk > 1 && a.sk > steps) a.sk /= 2;   // every wave gets at least one step
@@ -1180,12 +1122,9 @@ hipError_t launch_grouped(const ExpertView& w, const uint16_t* x, int64_t ldx, i
   return launch_cfg<1, kExperts, false>(a, slice, (unsigned)w.num_experts, s);
 }
 
-int moe_mlp_row_blocks(int64_t n_dn) { return (int)((n_dn + 63) / 64); }
-
 hipError_t launch_moe_mlp(const ExpertView& gu, const ExpertView& dn, const uint16_t* x, int64_t ldx,
                           const int32_t* ids, int32_t t, int32_t topk, const float* logits, int64_t ld_logits,
-                          uint16_t* h, float* part, int64_t ldp, uint32_t* counters, float* out, int64_t ldo,
-                          hipStream_t s) {
+                          uint16_t* h, float* part, int64_t ldp, float* out, int64_t ldo, hipStream_t s) {
   const int pairs = t * topk;
   const int64_t inter = gu.base.n / 2;
   KArgs a = base_args(gu.base);
@@ -1217,13 +1156,9 @@ hipError_t launch_moe_mlp(const ExpertView& gu, const ExpertView& dn, const uint
   b.num_experts = dn.num_experts;
   b.part = part;
   b.ldp = ldp;
-  b.counters = counters;
-  b.logits = logits;
-  b.ld_logits = ld_logits;
-  b.out = out;
-  b.ldo = ldo;
-  b.t = t;
-  return launch_cfg<1, kDownCombine, false>(b, 2 * pairs < 16 ? 2 * pairs : 16, (unsigned)dn.num_experts, s);
+  e = launch_cfg<1, kDownTerms, false>(b, 2 * pairs < 16 ? 2 * pairs : 16, (unsigned)dn.num_experts, s);
+  if (e != hipSuccess) return e;
+  return launch_moe_combine(part, ldp, ids, t, topk, dn.num_experts, logits, ld_logits, dn.base.n, out, ldo, s);
 }
 
 }  // namespace q3

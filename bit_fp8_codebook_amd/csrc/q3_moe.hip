@@ -124,4 +124,45 @@ hipError_t launch_moe_topk(const float* logits, int32_t t, int32_t e, int32_t to
   return hipGetLastError();
 }
 
+namespace {
+
+// One block per (token, 256 output rows): the token's routing weights go to
+// LDS, then each thread sums its row over the token's slots in slot order.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, int64_t ldp,
+                                                      const int32_t* __restrict__ ids, int topk, int E,
+                                                      const float* __restrict__ logits, int64_t ld_logits,
+                                                      int64_t n, float* __restrict__ out, int64_t ldo) {
+  __shared__ float pw[64];
+  const int tk = blockIdx.y;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int lane = tid;
+    const int e = lane < topk ? ids[tk * topk + lane] : -1;
+    const bool in = e >= 0 && e < E;
+    const float l = in ? logits[(int64_t)tk * ld_logits + e] : -__builtin_inff();
+    const float mx = wave_max(l);
+    const float z = in ? expf(l - mx) : 0.f;
+    const float den = wave_sum(z);
+    pw[lane] = in ? z / den : 0.f;
+  }
+  __syncthreads();
+  const int64_t row = (int64_t)blockIdx.x * 256 + tid;
+  if (row >= n) return;
+  float sum = 0.f;
+  for (int q = 0; q < topk; ++q)
+    if (pw[q] != 0.f) sum += pw[q] * part[(int64_t)(tk * topk + q) * ldp + row];
+  out[(int64_t)tk * ldo + row] = sum;
+}
+
+}  // namespace
+
+hipError_t launch_moe_combine(const float* part, int64_t ldp, const int32_t* ids, int32_t t, int32_t topk,
+                              int32_t num_experts, const float* logits, int64_t ld_logits, int64_t n, float* out,
+                              int64_t ldo, hipStream_t s) {
+  const dim3 grid((unsigned)((n + 255) / 256), (unsigned)t);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, part, ldp, ids, (int)topk, (int)num_experts, logits,
+                     ld_logits, n, out, ldo);
+  return hipGetLastError();
+}
+
 }  // namespace q3

@@ -201,14 +201,14 @@ Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t
  * q3_moe_topk or q3_moe_budget_topk); out fp32 [t][ldo].  Ids outside
  * [0, num_experts) are skipped (weight 0, excluded from the softmax); a token
  * with none in range gets 0, and a round with none in range writes nothing.
- * Two launches, no host synchronisation; only experts that appear in
- * topk_ids are read, each once per matrix.
+ * Three launches (gate/up with the SwiGLU, down, combine), no host
+ * synchronisation; only experts that appear in topk_ids are read, each once
+ * per matrix.  Deterministic: the combine adds slots in slot order.
  * Shapes: gate_up.n % 64 == 0, down.k == gate_up.n / 2, same num_experts,
  * 1 <= t*topk <= 64.
  * workspace: device memory of at least q3_moe_mlp_workspace_bytes(...) bytes,
- * 256-byte aligned, all zero before its first use; every call leaves its
- * counters zero again, so one workspace serves any number of calls in stream
- * order.  Calls that overlap in time must not share a workspace. */
+ * 256-byte aligned, any contents (it holds h and the per-pair outputs); calls
+ * that overlap in time must not share a workspace. */
 Q3_API int64_t q3_moe_mlp_workspace_bytes(int64_t n_gu, int64_t n_dn, int32_t t, int32_t topk);
 Q3_API q3_status q3_moe_mlp(const q3_expert_stack* gate_up, const q3_expert_stack* down, const uint16_t* x,
                             int64_t ldx, const int32_t* topk_ids, int32_t t, int32_t topk, const float* logits,

@@ -73,10 +73,10 @@ def test_workspace_sizes(q3lib):
     # draft head: fp32 scores [m][n] (rounded up to 8 bytes), then the shortlist scratch
     assert q3lib.q3_draft_head_workspace_bytes(1, 151936) == 151936 * 4 + 64 * 16 * 8
     assert q3lib.q3_draft_head_workspace_bytes(3, 5) == 64 + 3 * 64 * 16 * 8
-    # fused MLP: h (bf16, two terms per pair, I = n_gu / 2), per-pair fp32 outputs
-    # (rows padded to 4), one counter per 64 down rows; each piece 256-aligned
-    assert q3lib.q3_moe_mlp_workspace_bytes(1536, 2048, 8, 8) == 2 * 64 * 768 * 2 + 64 * 2048 * 4 + 256
-    assert q3lib.q3_moe_mlp_workspace_bytes(64, 30, 1, 1) == 256 + 256 + 256
+    # fused MLP: h (bf16, two terms per pair, I = n_gu / 2) and per-pair fp32
+    # outputs (rows padded to 4), each piece 256-aligned
+    assert q3lib.q3_moe_mlp_workspace_bytes(1536, 2048, 8, 8) == 2 * 64 * 768 * 2 + 64 * 2048 * 4
+    assert q3lib.q3_moe_mlp_workspace_bytes(64, 30, 1, 1) == 256 + 256
     assert q3lib.q3_moe_mlp_workspace_bytes(1536, 2048, 9, 8) == 0      # more than 64 pairs
     assert q3lib.q3_moe_mlp_workspace_bytes(1504, 2048, 8, 8) == 0      # I not a multiple of 32
 

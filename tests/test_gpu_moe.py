@@ -271,11 +271,12 @@ def test_moe_mlp_config2_full_size(q3):
 
 
 def test_moe_mlp_workspace_reuse_and_determinism(q3):
-    """The counters are left zero: one workspace serves consecutive rounds with
+    """One workspace (filled with garbage first) serves consecutive rounds with
     different routes; repeated rounds are bitwise identical."""
     moe = synth.make_moe(num_experts=16, k_gu=256, n_gu=192, k_dn=96, n_dn=130, tokens=8, topk=4, seed=21)
     st_gu, st_dn = stack_experts(q3, moe.experts_gu), stack_experts(q3, moe.experts_dn)
     ws = q3.moe_mlp_workspace(st_gu, st_dn, 8, 4, "cuda")
+    ws.fill_(0xFF)                  # NaN patterns everywhere
     pl_gu, pl_dn = _mlp_planes(moe.experts_gu), _mlp_planes(moe.experts_dn)
     x, logits = dev(moe.x), dev(moe.logits)
     first = None
@@ -289,8 +290,6 @@ def test_moe_mlp_workspace_reuse_and_determinism(q3):
                 first = out
             else:
                 assert np.array_equal(out, first)
-        counters = ws[-256:].cpu().numpy()
-        assert not counters.any()
 
 
 def test_moe_mlp_skips_out_of_range_ids(q3):
