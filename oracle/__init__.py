@@ -9,3 +9,4 @@ from .q3_oracle import (E4M3FN_TABLE, bf16_decode, dequantize, e4m3fn_decode, e8
                         combine_weights, moe_mlp, silu)
 from .q2_head import (decide, dequantize2, layout2, linear2, mxfp8_dequantize, pack2, pack_group2,  # noqa: F401
                       rescore, shortlist, unpack2, unpack_group2, word_offset2)
+from .q3_quant import choose_scales, codebook_values, quantize, snap  # noqa: F401,E402

@@ -161,3 +161,15 @@ def make_head(n: int, k: int, m: int, seed: int = 0):
                 round_to_e4m3fn_bytes(rs[1].standard_normal((n, 4))), draw_scales(rs[2], n, k),
                 e8, draw_scales(rs[4], n, k))
     return head, draw_x(rs[5], m, k)
+
+
+def make_quant(n: int, k: int, seed: int = 0):
+    """Weights to quantize and their per-row codebooks: w float32 [n][k] drawn
+    N(0,1) * 2^u with u an integer per group of 32, uniform in [-12, 3] (so
+    the groups' scales spread), and E4M3FN codebooks [n][8] drawn as for a
+    layer.  Streams in the order codebook, group exponents, weights."""
+    rs = _streams(seed, 3)
+    codebook = draw_codebook(rs[0], n)
+    u = rs[1].integers(-12, 4, size=(n, k // 32))
+    w = rs[2].standard_normal((n, k)) * np.repeat(np.ldexp(1.0, u), 32, axis=1)
+    return w.astype(np.float32), codebook
