@@ -227,6 +227,38 @@ def moe_point(q3, synth, budget=None, fused=False, reps=20, warmup=3):
     return pt
 
 
+def quantize_point(q3, synth, n=28672, k=8192, reps=10, warmup=2):
+    """Quantizer on the K=8192 N=28672 matrix: fp32 weights (N(0,1) times a
+    power of two per group, drawn on the GPU from a fixed seed) and E4M3FN
+    codebooks -> codes and scale bytes, one launch.  Algorithmic bytes: 4 per
+    weight read, 1 + 1/32 written, 8 per row of codebook."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    w = torch.randn((n, k), generator=gen, device="cuda", dtype=torch.float32)
+    u = torch.randint(-12, 4, (n, k // 32), generator=gen, device="cuda").to(torch.float32)
+    w *= torch.exp2(u).repeat_interleave(32, dim=1)
+    del u
+    cb = (torch.randn((n, 8), generator=gen, device="cuda")).to(torch.float8_e4m3fn).view(torch.uint8)
+    codes = torch.empty((n, k), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((n, k // 32), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            q3.q3_quantize(w, cb, codes, scales)
+        stream.synchronize()
+        with Timer(stream) as t:
+            for _ in range(reps):
+                q3.q3_quantize(w, cb, codes, scales)
+    us = t.ms * 1e3 / reps
+    alg = n * k * 4 + n * k + n * k // 32 + n * 8
+    pt = dict(name=f"quantize K={k} N={n} (fp32 -> codes + scales)", n=n, k=k, us_per_launch=round(us, 1),
+              algorithmic_bytes=alg, GBps=round(alg / us / 1e3, 1),
+              pct_of_8TBps=round(100 * alg / us / 1e3 / HBM_PEAK_GBPS, 1), kernel="quantize_kernel")
+    del w, codes, scales, cb
+    torch.cuda.empty_cache()
+    return pt
+
+
 def draft_head_point(q3, synth, n=151936, k=4096, m=1, size=16, reps=10, warmup=2):
     """Two-bit draft head on a vocabulary-sized head: 2-bit scores of every row,
     shortlist of 16, MXFP8 rescoring of the 16 and the decision (four launches),
@@ -422,6 +454,8 @@ def main():
                 points.append(moe_point(q3, synth, budget=budget, fused=fused))
                 log(points[-1])
         points.append(draft_head_point(q3, synth))
+        log(points[-1])
+        points.append(quantize_point(q3, synth))
         log(points[-1])
         points.append(linear_point(q3, synth, 1024, 1024, 1, chosen, name="1024x1024 M=1"))
         log(points[-1])

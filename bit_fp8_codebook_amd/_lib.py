@@ -54,6 +54,7 @@ SIGNATURES = {
     "q3_moe_topk": (ctypes.c_int, [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "q3_grouped_expert_gemv": (ctypes.c_int, [ctypes.POINTER(Q3ExpertStack), c_vp, c_i64, c_i32, c_vp, c_i32,
                                               c_i32, c_vp, c_i64, c_vp]),
+    "q3_quantize": (ctypes.c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
     "q3_moe_budget_topk": (ctypes.c_int, [c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "q3_moe_mlp_workspace_bytes": (c_i64, [c_i64, c_i64, c_i32, c_i32]),
     "q3_moe_mlp": (ctypes.c_int, [ctypes.POINTER(Q3ExpertStack), ctypes.POINTER(Q3ExpertStack), c_vp, c_i64, c_vp,
@@ -195,6 +196,23 @@ def _out(y, m, n, device):
     if y.dtype != torch.float32 or y.stride(1) != 1:
         raise ValueError("y must be float32 with contiguous rows")
     return y
+
+
+def q3_quantize(w: torch.Tensor, codebook: torch.Tensor, codes: torch.Tensor = None, scales: torch.Tensor = None):
+    """fp32 weights [n][k] and E4M3FN codebooks [n][8] -> (codes uint8 [n][k], scales uint8 [n][k/32])."""
+    _dev(w, "w"), _dev(codebook, "codebook")
+    if w.dtype != torch.float32 or w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be float32 [n][k] with contiguous rows")
+    n, k = w.shape
+    if codebook.dtype != torch.uint8 or tuple(codebook.shape) != (n, 8) or not codebook.is_contiguous():
+        raise ValueError("codebook must be contiguous uint8 [n][8]")
+    if codes is None:
+        codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((n, k // 32), dtype=torch.uint8, device=w.device)
+    _check("q3_quantize", lib().q3_quantize(w.data_ptr(), _ld(w), codebook.data_ptr(), n, k, codes.data_ptr(),
+                                            _ld(codes), scales.data_ptr(), _ld(scales), _stream(w)))
+    return codes, scales
 
 
 def q3_gemv(w: PackedMatrix, x: torch.Tensor, y: torch.Tensor = None) -> torch.Tensor:

@@ -164,6 +164,18 @@ Q3_API q3_status q3_unpack(const q3_matrix* w, uint8_t* codes_out, uint8_t* scal
   return from_hip(q3::launch_unpack(view_of(w), codes_out, scale_out, static_cast<hipStream_t>(stream), 3));
 }
 
+Q3_API q3_status q3_quantize(const float* w, int64_t ldw, const uint8_t* codebook, int64_t n, int64_t k,
+                             uint8_t* codes, int64_t ldc, uint8_t* scale_bytes, int64_t lds, void* stream) {
+  q3_status st = check_shape(n, k);
+  if (st != Q3_OK) return st;
+  if (n > 0 && (!w || !codebook || !codes || !scale_bytes)) return Q3_ERR_INVALID_ARG;
+  if (ldw < k || ldc < k || lds < k / kGroup) return Q3_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || ldw % 4 || !aligned(codebook, 8) || !aligned(codes, 8) || ldc % 8) return Q3_ERR_MISALIGNED;
+  if ((st = check_device()) != Q3_OK) return st;
+  return from_hip(q3::launch_quantize(w, ldw, codebook, n, k, codes, ldc, scale_bytes, lds,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 Q3_API q3_status q3_gemv(const q3_matrix* w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
                          void* stream) {
   q3_status st = check_matrix(w);

@@ -20,6 +20,10 @@ hipError_t launch_pack(const uint8_t* codes, int64_t ldc, const uint8_t* scales,
                        int64_t k, uint8_t* code_plane, uint8_t* scale_plane, hipStream_t s, int bits);
 hipError_t launch_unpack(const PlaneView& w, uint8_t* codes, uint8_t* scales, hipStream_t s, int bits);
 
+// Quantizer: per-group scale and nearest code under the row's codebook.
+hipError_t launch_quantize(const float* w, int64_t ldw, const uint8_t* cb, int64_t n, int64_t k, uint8_t* codes,
+                           int64_t ldc, uint8_t* scales, int64_t lds, hipStream_t s);
+
 // VALU path, 1 <= m <= 8.
 hipError_t launch_gemv(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
                        hipStream_t s);

@@ -123,6 +123,24 @@ Q3_API const char* q3_status_string(q3_status s);
  * n >= 0.  Host only. */
 Q3_API q3_status q3_layout(int64_t n, int64_t k, q3_layout_info* out);
 
+/* Quantize fp32 weights under given per-row codebooks (the step before
+ * q3_pack; "Model surgery" brings a model's weights to this format, the rule
+ * is this library's reading):
+ *   scale_bytes[r][g] = the smallest s in 0..254 with
+ *       max_{k in group g} |w[r][k]| <= max_j |E4M3(codebook[r][j])| * 2^(s-127)
+ *     (254 when none fits, i.e. an all-zero codebook; 0 for an all-zero group);
+ *   codes[r][k] = argmin_j |w[r][k] - E4M3(codebook[r][j]) * 2^(s-127)|, equal
+ *     distances (and repeated entries) to the lower index j.
+ * Exact (bit-identical to exact rational arithmetic).
+ *   w           [n][ldw] fp32, finite, |w| <= 2^64 (not checked); 16-byte
+ *               aligned, ldw % 4 == 0, ldw >= k
+ *   codebook    [n][8] E4M3FN bytes without NaN entries (not checked), 8-byte aligned
+ *   codes       [n][ldc] uint8 out, 8-byte aligned, ldc % 8 == 0, ldc >= k
+ *   scale_bytes [n][lds] uint8 out, lds >= k/32
+ * k > 0, k % 32 == 0.  One launch; codebook fitting is not part of it. */
+Q3_API q3_status q3_quantize(const float* w, int64_t ldw, const uint8_t* codebook, int64_t n, int64_t k,
+                             uint8_t* codes, int64_t ldc, uint8_t* scale_bytes, int64_t lds, void* stream);
+
 /* Pack unpacked codes and scales into the planes ("Three-bit weights": a
  * 3-bit index per weight, one 8-bit scale per group of 32).
  *   codes       [n][ldc] uint8, entries 0..7 (higher bits ignored), ldc >= k

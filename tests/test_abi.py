@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
                                          "q3_layout2", "q3_pack2", "q3_unpack2", "q3_head2_scores",
                                          "q3_shortlist_workspace_bytes", "q3_shortlist", "q3_rescore_fp8",
                                          "q3_draft_head_workspace_bytes", "q3_draft_head", "q3_moe_budget_topk",
-                                         "q3_moe_mlp_workspace_bytes", "q3_moe_mlp"])
+                                         "q3_moe_mlp_workspace_bytes", "q3_moe_mlp", "q3_quantize"])
 
 
 def test_library_exports_every_declared_symbol(q3lib):
@@ -155,6 +155,16 @@ def test_validation_rejects_before_any_hip_call(q3lib):
     assert q3lib.q3_grouped_expert_gemv(ctypes.byref(st), fake, 64, 0, fake, 8, 8, fake, 16, None) == 1
     st.code_expert_stride = 776                                                     # not 16-aligned
     assert q3lib.q3_grouped_expert_gemv(ctypes.byref(st), fake, 64, 0, fake, 8, 8, fake, 16, None) == 3
+    # quantizer
+    assert q3lib.q3_quantize(fake, 64, fake, 4, 48, fake, 64, fake, 2, None) == 2       # k % 32 != 0
+    assert q3lib.q3_quantize(fake, 60, fake, 4, 64, fake, 64, fake, 2, None) == 1       # ldw < k
+    assert q3lib.q3_quantize(fake, 64, fake, 4, 64, fake, 64, fake, 1, None) == 1       # lds < k/32
+    assert q3lib.q3_quantize(fake + 4, 64, fake, 4, 64, fake, 64, fake, 2, None) == 3   # w not 16-aligned
+    assert q3lib.q3_quantize(fake, 66, fake, 4, 64, fake, 64, fake, 2, None) == 3       # ldw % 4
+    assert q3lib.q3_quantize(fake, 64, fake + 4, 4, 64, fake, 64, fake, 2, None) == 3   # codebook not 8-aligned
+    assert q3lib.q3_quantize(fake, 64, fake, 4, 64, fake + 4, 64, fake, 2, None) == 3   # codes not 8-aligned
+    assert q3lib.q3_quantize(fake, 64, fake, 4, 64, fake, 68, fake, 2, None) == 3       # ldc % 8
+    assert q3lib.q3_quantize(None, 64, fake, 4, 64, fake, 64, fake, 2, None) == 1
     # fused MLP: gate/up n = 64 (I = 32), k = 64; down n = 16, k = 32
     gu = _lib.Q3ExpertStack(4, 64, 64, fake, 3072, fake, 256, fake, 512)
     dn = _lib.Q3ExpertStack(4, 16, 32, fake, 768, fake, 64, fake, 128)
