@@ -334,9 +334,13 @@ def read_traffic(dot: bool):
         return family, None
     if t.get("source_hash") != source_hash():
         return family, None
-    cands = [(v.get("dispatches", 0), k, v) for k, v in t.get("kernels", {}).items()
-             if k.startswith("linear_kernel<1, ") and k.endswith(("true, 3>" if dot else "false, 3>"))
-             and ", false, " in k]
+    def dense_m1(k):
+        if not (k.startswith("linear_kernel<") and k.endswith(">")):
+            return False
+        args = [a.strip() for a in k[len("linear_kernel<"):-1].split(",")]
+        return (len(args) == 7 and args[0] == "1" and args[3] in ("0", "false")
+                and args[5] == ("true" if dot else "false") and args[6] == "3")
+    cands = [(v.get("dispatches", 0), k, v) for k, v in t.get("kernels", {}).items() if dense_m1(k)]
     if not cands:
         return family, None
     _, name, v = max(cands)

@@ -29,7 +29,8 @@ def per_kernel(path, counter):
 
 
 def short(name):
-    for key in ("linear_kernel<", "wide_kernel<", "pack_kernel", "unpack_kernel", "topk_kernel", "copyBuffer"):
+    for key in ("linear_kernel<", "wide_kernel<", "pack_kernel", "unpack_kernel", "budget_topk_kernel", "topk_kernel",
+                "combine_kernel", "quantize_kernel", "shortlist_chunks", "rescore_kernel", "copyBuffer"):
         if key in name:
             i = name.index(key)
             return name[i:name.index(">", i) + 1] if key.endswith("<") and ">" in name[i:] else key
