@@ -134,7 +134,12 @@ def linear_point(q3, synth, n, k, m, kernel, reps=20, warmup=3, name=""):
     ws = [w0] + [w0.clone() for _ in range(ncopy - 1)]
     xd = to_dev(x)
     y = torch.empty((m, n), dtype=torch.float32, device="cuda")
-    fn = q3.q3_gemv if kernel == "gemv" else q3.q3_gemm_small_m
+    if kernel == "mfma_ws":
+        # one caller-owned workspace serves every launch (they run in order on one stream)
+        wsb = torch.empty(max(16, q3.q3_gemm_small_m_workspace_bytes(n, k, m)), dtype=torch.uint8, device="cuda")
+        fn = lambda w_, x_, y_: q3.q3_gemm_small_m_ws(w_, x_, y_, wsb)  # noqa: E731
+    else:
+        fn = q3.q3_gemv if kernel == "gemv" else q3.q3_gemm_small_m
     stream = torch.cuda.Stream()
     g = capture(lambda: [fn(w, xd, y) for w in ws], stream)
     ms = time_graph(g, stream, reps, warmup)
@@ -147,7 +152,9 @@ def linear_point(q3, synth, n, k, m, kernel, reps=20, warmup=3, name=""):
               algorithmic_GBps=round(algorithmic_bytes(n, k, m) / us / 1e3, 1),
               tokens_per_s=round(m / (us * 1e-6), 1),
               mfma_pct_of_bf16_peak=round(100 * flops / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 2)
-              if kernel == "mfma" else None)
+              if kernel != "gemv" else None)
+    if kernel == "mfma_ws":
+        pt["k_splits"] = max(1, q3.q3_gemm_small_m_workspace_bytes(n, k, m) // (4 * m * n))
     del ws, w0, g
     torch.cuda.empty_cache()
     return pt
@@ -453,6 +460,12 @@ def main():
         log(points[-1])
         points.append(linear_point(q3, synth, 151936, 4096, 64, "mfma", reps=5, name="K=4096 N=151936 M=64"))
         log(points[-1])
+        # Verify batches on matrices with few row tiles: one pass, and K split
+        # over blocks through a workspace (q3_gemm_small_m_ws).
+        for nn, kk, mm in ((4096, 4096, 16), (4096, 4096, 64), (8192, 28672, 16)):
+            for kn in ("mfma", "mfma_ws"):
+                points.append(linear_point(q3, synth, nn, kk, mm, kn, name=f"K={kk} N={nn} M={mm}"))
+                log(points[-1])
         for fused in (False, True):
             for budget in (None, 16):
                 points.append(moe_point(q3, synth, budget=budget, fused=fused))

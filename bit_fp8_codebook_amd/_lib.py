@@ -51,6 +51,9 @@ SIGNATURES = {
     "q3_unpack": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), c_vp, c_vp, c_vp]),
     "q3_gemv": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), c_vp, c_i64, c_i64, c_vp, c_i64, c_vp]),
     "q3_gemm_small_m": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), c_vp, c_i64, c_i64, c_vp, c_i64, c_vp]),
+    "q3_gemm_small_m_workspace_bytes": (c_i64, [c_i64, c_i64, c_i64]),
+    "q3_gemm_small_m_ws": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64,
+                                          c_vp]),
     "q3_moe_topk": (ctypes.c_int, [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "q3_grouped_expert_gemv": (ctypes.c_int, [ctypes.POINTER(Q3ExpertStack), c_vp, c_i64, c_i32, c_vp, c_i32,
                                               c_i32, c_vp, c_i64, c_vp]),
@@ -234,6 +237,29 @@ def q3_gemm_small_m(w: PackedMatrix, x: torch.Tensor, y: torch.Tensor = None) ->
     d = w.desc()
     _check("q3_gemm_small_m", lib().q3_gemm_small_m(ctypes.byref(d), x.data_ptr(), m, _ld(x), y.data_ptr(),
                                                     _ld(y), _stream(x)))
+    return y
+
+
+def q3_gemm_small_m_workspace_bytes(n: int, k: int, m: int) -> int:
+    return lib().q3_gemm_small_m_workspace_bytes(n, k, m)
+
+
+def q3_gemm_small_m_ws(w: PackedMatrix, x: torch.Tensor, y: torch.Tensor = None,
+                       workspace: torch.Tensor = None) -> torch.Tensor:
+    """q3_gemm_small_m with a workspace (uint8 device tensor); when none is
+    given, one of q3_gemm_small_m_workspace_bytes bytes is allocated here."""
+    x = _tokens(x, w.k)
+    m = x.shape[0]
+    y = _out(y, m, w.n, x.device)
+    if workspace is None:
+        nbytes = q3_gemm_small_m_workspace_bytes(w.n, w.k, m)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    else:
+        _dev(workspace, "workspace")
+    d = w.desc()
+    _check("q3_gemm_small_m_ws", lib().q3_gemm_small_m_ws(ctypes.byref(d), x.data_ptr(), m, _ld(x), y.data_ptr(),
+                                                          _ld(y), workspace.data_ptr(), workspace.numel(),
+                                                          _stream(x)))
     return y
 
 

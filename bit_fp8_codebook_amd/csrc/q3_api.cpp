@@ -191,7 +191,24 @@ Q3_API q3_status q3_gemm_small_m(const q3_matrix* w, const uint16_t* x, int64_t 
   if (st != Q3_OK) return st;
   if ((st = check_tokens(w->k, w->n, x, m, ldx, y, ldy, 64)) != Q3_OK) return st;
   if ((st = check_device()) != Q3_OK) return st;
-  return from_hip(q3::launch_gemm_small_m(view_of(w), x, m, ldx, y, ldy, static_cast<hipStream_t>(stream)));
+  return from_hip(
+      q3::launch_gemm_small_m(view_of(w), x, m, ldx, y, ldy, nullptr, 0, static_cast<hipStream_t>(stream)));
+}
+
+Q3_API int64_t q3_gemm_small_m_workspace_bytes(int64_t n, int64_t k, int64_t m) {
+  if (n < 1 || k < 32 || k % 32 || m < 1 || m > 64) return 0;
+  return q3::gemm_small_m_workspace_bytes(n, k, m);
+}
+
+Q3_API q3_status q3_gemm_small_m_ws(const q3_matrix* w, const uint16_t* x, int64_t m, int64_t ldx, float* y,
+                                    int64_t ldy, void* workspace, int64_t workspace_bytes, void* stream) {
+  q3_status st = check_matrix(w);
+  if (st != Q3_OK) return st;
+  if ((st = check_tokens(w->k, w->n, x, m, ldx, y, ldy, 64)) != Q3_OK) return st;
+  if (workspace && !aligned(workspace, 16)) return Q3_ERR_MISALIGNED;
+  if ((st = check_device()) != Q3_OK) return st;
+  return from_hip(q3::launch_gemm_small_m(view_of(w), x, m, ldx, y, ldy, workspace, workspace ? workspace_bytes : 0,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 Q3_API q3_status q3_moe_topk(const float* logits, int32_t t, int32_t num_experts, int32_t topk,

@@ -28,9 +28,12 @@ hipError_t launch_quantize(const float* w, int64_t ldw, const uint8_t* cb, int64
 hipError_t launch_gemv(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
                        hipStream_t s);
 
-// MFMA path, 1 <= m <= 64.
+// MFMA path, 1 <= m <= 64.  ws (nullable, 16-byte aligned) of at least
+// gemm_small_m_workspace_bytes(n, k, m) bytes lets streamed activations split
+// K over blocks; without it every block covers the whole K.
+int64_t gemm_small_m_workspace_bytes(int64_t n, int64_t k, int64_t m);
 hipError_t launch_gemm_small_m(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y,
-                               int64_t ldy, hipStream_t s);
+                               int64_t ldy, void* ws, int64_t ws_bytes, hipStream_t s);
 
 // Two-bit draft head: scores of every row for 1 <= m <= 16 queries (matrix cores).
 hipError_t launch_head2_scores(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,

@@ -82,6 +82,7 @@ struct KArgs {
   int64_t x_rows;   // rows of x that may be read
   float* y;
   int64_t ldy;
+  int64_t split_stride;   // streamed modes split over blockIdx.z: split z writes y + z * split_stride
   int m;          // dense: number of tokens
   int vec_y;      // y rows 16-byte aligned: four consecutive outputs go out as one store
   int sk;         // K split over the waves of a block (full-K mode)
@@ -433,8 +434,13 @@ void linear_kernel(KArgs a) {
     rt[r].vscale = tile_ok ? (uint32_t)T * (16u * gp) + 4u * lane : kOob;
   }
 
-  const int s0 = kMode != kStream ? (ks * p.steps) / sk : 0;
-  const int s1 = kMode != kStream ? ((ks + 1) * p.steps) / sk : p.steps;
+  // Full-K mode splits K over the waves of a block; stream mode over the
+  // blocks of a grid column (blockIdx.z), each split writing its own partial
+  // output plane.
+  const int zs = blockIdx.z, nzs = gridDim.z;
+  const int s0 = kMode != kStream ? (ks * p.steps) / sk : (zs * p.steps) / nzs;
+  const int s1 = kMode != kStream ? ((ks + 1) * p.steps) / sk : ((zs + 1) * p.steps) / nzs;
+  float* const ybase = a.y + (int64_t)zs * a.split_stride;
 
   StepData<R, kWd> A, B;
   const rsrc_t xr_rsrc = make_rsrc(a.x, (uint32_t)((a.x_rows - 1) * a.ldx * 2 + (int64_t)G * 64));
@@ -562,7 +568,7 @@ void linear_kernel(KArgs a) {
           const int idx = tid + q * kThreads;
           const int j = idx >> 6, c16 = idx & 63;
           const int k0 = s * 512 + c16 * 8;
-          const bool ok = idx < nchunk && j < cnt && s < p.steps && k0 < G * 32;
+          const bool ok = idx < nchunk && j < cnt && s < s1 && k0 < G * 32;
           r[q] = bload128(xr_rsrc, ok ? (uint32_t)xrow(j) * ldx_bytes + 2u * k0 : kOob);
         }
       };
@@ -575,12 +581,12 @@ void linear_kernel(KArgs a) {
         }
       };
       u32x4 xr[kChunks];
-      fetch(0, xr);
+      fetch(s0, xr);
       begin_slice(slice);
       if (tid < 64) *reinterpret_cast<u32x4*>(lds + zero_base + 16u * tid) = u32x4{0u, 0u, 0u, 0u};
       put(0, xr);
       __syncthreads();
-      for (int s = 0; s < s1; s += 2) {
+      for (int s = s0; s < s1; s += 2) {
         load_step(p, rt, last_ok, s + 1, s1, B);
         fetch(s + 1, xr);
         __builtin_amdgcn_sched_barrier(0);
@@ -644,7 +650,7 @@ void linear_kernel(KArgs a) {
             if (row < a.n) {
 #pragma unroll
               for (int m = 0; m < NT; ++m)
-                if (m < cnt) a.y[(int64_t)yrow(m) * a.ldy + row] = dacc[r][m];
+                if (m < cnt) ybase[(int64_t)yrow(m) * a.ldy + row] = dacc[r][m];
             }
           }
         }
@@ -708,7 +714,7 @@ void linear_kernel(KArgs a) {
         for (int c = 0; c < NT; ++c) {
           const int j = 16 * c + i;
           if (j < cnt) {
-            float* yr = a.y + (int64_t)yrow(j) * a.ldy;
+            float* yr = ybase + (int64_t)yrow(j) * a.ldy;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
               const int64_t row0 = tix[r] * 16 + 4 * kb;
@@ -737,11 +743,6 @@ void linear_kernel(KArgs a) {
 // bytes land at 16*l), weights through two register sets, and the step's
 // matrix-core work is software-pipelined against the dequantisation.  Step
 // advances ride in scalar offsets, so the loop does no vector address work.
-#ifdef Q3_WIDE_ROWS
-constexpr int kWideRows = Q3_WIDE_ROWS;
-#else
-constexpr int kWideRows = 5;
-#endif
 #ifdef Q3_WIDE_MIN_NT
 constexpr int kWideMinNT = Q3_WIDE_MIN_NT;
 #else
@@ -749,10 +750,10 @@ constexpr int kWideMinNT = 2;
 #endif
 constexpr int kWideWaves = 4;
 
-template <int NT>
+template <int NT, int R>
 __global__ __launch_bounds__(64 * kWideWaves) __attribute__((amdgpu_waves_per_eu(1)))
 void wide_kernel(KArgs a) {
-  constexpr int R = kWideRows, kW = kWideWaves, kSlice = 16 * NT;
+  constexpr int kW = kWideWaves, kSlice = 16 * NT;
   constexpr uint32_t rstride = 1024u + kRowPad;
   constexpr uint32_t buf_bytes = (uint32_t)kSlice * rstride;
   constexpr uint32_t zero_base = 2u * buf_bytes;
@@ -770,6 +771,10 @@ void wide_kernel(KArgs a) {
   p.scale = make_rsrc(a.scale, (uint32_t)(tiles * 16 * gp));
   p.full_steps = p.steps = (int)(gp / 16);
   p.q_last = 4;
+  // Steps [s_begin, s_end) of this K split (blockIdx.z) and its output plane.
+  const int s_begin = (int)(blockIdx.z * p.steps / gridDim.z);
+  const int s_end = (int)((blockIdx.z + 1) * p.steps / gridDim.z);
+  float* const ybase = a.y + (int64_t)blockIdx.z * a.split_stride;
   const rsrc_t cbr = make_rsrc(a.cb, (uint32_t)(a.n * 8));
   RowTile rt[R];
 #pragma unroll
@@ -809,8 +814,8 @@ void wide_kernel(KArgs a) {
     // of range (zeros, no memory traffic) and are never used.
     constexpr int kLoads = 4 * R + kSlice / kW;
     auto loads_of = [&](StepData<R>& dst, uint32_t buf, int sn) {
-      const bool live = sn < p.steps;
-      const uint32_t sc = (uint32_t)(live ? sn : p.steps - 1);
+      const bool live = sn < s_end;
+      const uint32_t sc = (uint32_t)(live ? sn : s_end - 1);
       return [&, buf, live, sc](auto q) {
         constexpr int Q = decltype(q)::value;
         if constexpr (Q < 3 * R) {
@@ -834,13 +839,13 @@ void wide_kernel(KArgs a) {
     // halves doubles the accumulators' register footprint).
     StepData<R> A, B;
     {
-      auto first = loads_of(A, 0u, 0);
+      auto first = loads_of(A, 0u, s_begin);
       issue_range<0, kLoads>(first);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    int s = 0;
-    for (; s + 1 < p.steps; s += 2) {
+    int s = s_begin;
+    for (; s + 1 < s_end; s += 2) {
       mfma_step_pipe<NT, R, kLoads>(A, rt, xb0, lds, acc, loads_of(B, buf_bytes, s + 1));
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0);
@@ -850,14 +855,14 @@ void wide_kernel(KArgs a) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    if (s < p.steps) mfma_step_pipe<NT, R, 0>(A, rt, xb0, lds, acc, [](auto) {});
+    if (s < s_end) mfma_step_pipe<NT, R, 0>(A, rt, xb0, lds, acc, [](auto) {});
 
     // D layout: lane l holds rows 4*(l/16)+v (v = 0..3) of the tile for token l%16.
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
       const int j = 16 * c + i;
       if (j < cnt) {
-        float* yr = a.y + (int64_t)(slice + j) * a.ldy;
+        float* yr = ybase + (int64_t)(slice + j) * a.ldy;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int64_t row0 = (tile0 + r) * 16 + 4 * kb;
@@ -903,32 +908,57 @@ hipError_t allow_lds(size_t bytes) {
 }
 
 template <int NT, int R, int kW, int kGrouped, int kMode, bool kDot, int kBits>
-hipError_t launch_one(const KArgs& a, size_t shm, unsigned grid_y, hipStream_t s) {
+hipError_t launch_one(const KArgs& a, size_t shm, unsigned grid_y, unsigned grid_z, hipStream_t s) {
   const int rb = kW / (kMode != kStream ? a.sk : 1);
   const int64_t tiles = (a.n + 15) / 16;
   const int64_t groups = (tiles + R - 1) / R;   // row groups of R tiles
-  const dim3 grid((unsigned)((groups + rb - 1) / rb), grid_y);
+  const dim3 grid((unsigned)((groups + rb - 1) / rb), grid_y, grid_z);
   hipError_t e = allow_lds<NT, R, kW, kGrouped, kMode, kDot, kBits>(shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((linear_kernel<NT, R, kW, kGrouped, kMode, kDot, kBits>), grid, dim3(64 * kW), shm, s, a);
   return hipGetLastError();
 }
 
-template <int NT>
-hipError_t launch_wide(const KArgs& a, hipStream_t s) {
-  constexpr int kRowsPerBlock = kWideRows * kWideWaves;
+template <int NT, int R>
+hipError_t launch_wide(const KArgs& a, unsigned splits, hipStream_t s) {
+  constexpr int kRowsPerBlock = R * kWideWaves;
   const size_t shm = stream_bytes(16 * NT);
   static std::atomic<bool> allowed{false};
   if (!allowed.load(std::memory_order_acquire)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(wide_kernel<NT>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(wide_kernel<NT, R>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     if (e != hipSuccess) return e;
     allowed.store(true, std::memory_order_release);
   }
   const int64_t tiles = (a.n + 15) / 16;
-  const dim3 grid((unsigned)((tiles + kRowsPerBlock - 1) / kRowsPerBlock));
-  hipLaunchKernelGGL((wide_kernel<NT>), grid, dim3(64 * kWideWaves), shm, s, a);
+  const dim3 grid((unsigned)((tiles + kRowsPerBlock - 1) / kRowsPerBlock), 1, splits);
+  hipLaunchKernelGGL((wide_kernel<NT, R>), grid, dim3(64 * kWideWaves), shm, s, a);
   return hipGetLastError();
+}
+
+// Sum of the K splits' partial planes in split order: y[r][c] = sum_z
+// part[z][r][c] (part rows of n floats, planes m*n apart).  Four columns per
+// thread.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* part, int splits, int64_t m, int64_t n,
+                                                           float* y, int64_t ldy, int vec) {
+  const int64_t nq = (n + 3) / 4;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= m * nq) return;
+  const int64_t r = e / nq, c = 4 * (e - r * nq);
+  const int64_t plane = m * n;
+  const float* src = part + r * n + c;
+  float* dst = y + r * ldy + c;
+  if (vec && c + 3 < n) {
+    f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+    for (int z = 1; z < splits; ++z) acc += *reinterpret_cast<const f32x4*>(src + z * plane);
+    *reinterpret_cast<f32x4*>(dst) = acc;
+  } else {
+    for (int v = 0; v < 4 && c + v < n; ++v) {
+      float acc = src[v];
+      for (int z = 1; z < splits; ++z) acc += src[z * plane + v];
+      dst[v] = acc;
+    }
+  }
 }
 
 // Launch shape: R row tiles per wave, W waves per block, K split sk (full-K
@@ -980,26 +1010,30 @@ constexpr bool kExpertStream = false;
 #endif
 
 template <int NT, int R, int kGrouped, bool kDot, int kBits>
-hipError_t launch_r(KArgs a, int w, int mode, size_t shm, unsigned grid_y, hipStream_t s) {
+hipError_t launch_r(KArgs a, int w, int mode, size_t shm, unsigned grid_y, unsigned splits, hipStream_t s) {
   if constexpr (kGrouped != kDense) {   // expert passes: one block shape
-    if (mode == kShared) return launch_one<NT, R, kExpertWaves, kGrouped, kShared, kDot, kBits>(a, shm, grid_y, s);
-    return launch_one<NT, R, kExpertWaves, kGrouped, kStream, kDot, kBits>(a, shm, grid_y, s);
+    if (mode == kShared) return launch_one<NT, R, kExpertWaves, kGrouped, kShared, kDot, kBits>(a, shm, grid_y, 1, s);
+    return launch_one<NT, R, kExpertWaves, kGrouped, kStream, kDot, kBits>(a, shm, grid_y, 1, s);
   } else {
     switch (mode) {
       case kShared:
-        if (w == 8) return launch_one<NT, R, 8, kGrouped, kShared, kDot, kBits>(a, shm, grid_y, s);
-        return launch_one<NT, R, 4, kGrouped, kShared, kDot, kBits>(a, shm, grid_y, s);
+        if (w == 8) return launch_one<NT, R, 8, kGrouped, kShared, kDot, kBits>(a, shm, grid_y, 1, s);
+        return launch_one<NT, R, 4, kGrouped, kShared, kDot, kBits>(a, shm, grid_y, 1, s);
       default:
-        if (w == 8) return launch_one<NT, R, 8, kGrouped, kStream, kDot, kBits>(a, shm, grid_y, s);
-        return launch_one<NT, R, 4, kGrouped, kStream, kDot, kBits>(a, shm, grid_y, s);
+        if (w == 8) return launch_one<NT, R, 8, kGrouped, kStream, kDot, kBits>(a, shm, grid_y, splits, s);
+        return launch_one<NT, R, 4, kGrouped, kStream, kDot, kBits>(a, shm, grid_y, splits, s);
     }
   }
 }
 
 
-// tokens_in_slice: tokens the LDS staging holds at once.
+// tokens_in_slice: tokens the LDS staging holds at once.  wide_rows and
+// splits (dense matrix-core products of streamed activations only): row tiles
+// per wave of the wide kernel (5 or 2) and K splits over blocks, each writing
+// the partial plane a.y + z * a.split_stride.
 template <int NT, int kGrouped, bool kDot, int kBits = 3>
-hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t s) {
+hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t s, int wide_rows = 5,
+                      unsigned splits = 1) {
   constexpr int kSlice = kDot ? NT : 16 * NT;
   const size_t fk = full_k_bytes(tokens_in_slice, a.G);
   const bool full_k = fk <= (size_t)kFullKBudget && !(kGrouped && kExpertStream);
@@ -1014,22 +1048,24 @@ hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t
   // Two or more column tiles of streamed activations on whole steps: the wide
   // kernel (one wave per SIMD, many row tiles, activations loaded into LDS).
   if constexpr (!kGrouped && !kDot && kBits == 3 && NT >= kWideMinNT) {
-    if (mode == kStream && a.G % 16 == 0) return launch_wide<NT>(a, s);
+    if (mode == kStream && a.G % 16 == 0)
+      return wide_rows == 2 ? launch_wide<NT, 2>(a, splits, s) : launch_wide<NT, 5>(a, splits, s);
   }
 #endif
+  if (mode == kShared) splits = 1;
   size_t shm = mode == kShared ? fk : stream_bytes(kSlice);
   if (mode != kStream && a.sk > 1) {
     const size_t red = reduce_bytes(kDot ? NT : 4 * NT, sh.r, sh.w);
     if (shm < red) shm = red;
   }
   if constexpr (kGrouped == kSwiGLU) {
-    return launch_r<NT, 2, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, s);
+    return launch_r<NT, 2, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, 1, s);
   } else if constexpr (kGrouped || kDot) {
-    return launch_r<NT, 1, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, s);
+    return launch_r<NT, 1, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, splits, s);
   } else {
     switch (sh.r) {
-      case 1: return launch_r<NT, 1, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, s);
-      case 2: return launch_r<NT, 2, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, s);
+      case 1: return launch_r<NT, 1, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, splits, s);
+      case 2: return launch_r<NT, 2, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, splits, s);
       default: return hipErrorInvalidValue;
     }
   }
@@ -1045,10 +1081,61 @@ KArgs base_args(const PlaneView& w) {
   return a;
 }
 
+// Launch plan of a dense matrix-core product (1..64 tokens).  Activations that
+// fit in LDS whole are staged once per block and K is split over the waves of
+// a block.  Streamed activations put whole row groups in a block: on a matrix
+// with few of them the grid would leave most of the chip idle, so K is split
+// over the blocks of a grid column as well (partial planes in a workspace,
+// then a fixed-order sum), and the wide kernel takes two row tiles per wave
+// instead of five.  Splits stop at 128 blocks (wide) or 192 (8-wave stream
+// blocks) and at two steps per split: measured on MI355X, more splits cost
+// more in partial planes and per-block start-up than they gain (N = 8192,
+// K = 28672, 16 tokens: 65.7 us in one pass, 28.7 us in 4 splits; a grid of
+// 224 blocks or more is faster unsplit).
+#ifndef Q3_SPLIT_TARGET_WIDE
+#define Q3_SPLIT_TARGET_WIDE 128
+#endif
+#ifndef Q3_SPLIT_TARGET_STREAM
+#define Q3_SPLIT_TARGET_STREAM 192
+#endif
+#ifndef Q3_SPLIT_MIN_STEPS
+#define Q3_SPLIT_MIN_STEPS 2
+#endif
+struct SmallMPlan {
+  int wide_rows;   // row tiles per wave of the wide kernel
+  int splits;      // K splits over blocks
+};
+
+SmallMPlan plan_small_m(int64_t n, int groups, int64_t m) {
+  SmallMPlan pl{5, 1};
+  if (n <= 0) return pl;
+  const int nt = (int)((m + 15) / 16);
+  if (full_k_bytes((int)m, groups) <= (size_t)kFullKBudget) return pl;   // staged whole: no split
+  const int64_t tiles = (n + 15) / 16;
+  const int steps = (((groups + 3) & ~3) + 15) / 16;
+  int64_t blocks, target;
+  if (nt >= kWideMinNT && groups % 16 == 0) {
+    if ((tiles + 19) / 20 < 384) pl.wide_rows = 2;
+    blocks = (tiles + 4 * pl.wide_rows - 1) / (4 * pl.wide_rows);
+    target = Q3_SPLIT_TARGET_WIDE;
+  } else {
+    const Shape sh = pick_shape(n, groups, false, (int)m, false);
+    blocks = (tiles + (int64_t)sh.r * sh.w - 1) / ((int64_t)sh.r * sh.w);
+    target = Q3_SPLIT_TARGET_STREAM;
+  }
+  while (pl.splits < 16 && blocks * pl.splits < target && steps >= 2 * pl.splits * Q3_SPLIT_MIN_STEPS) pl.splits *= 2;
+  return pl;
+}
+
 }  // namespace
 
+int64_t gemm_small_m_workspace_bytes(int64_t n, int64_t k, int64_t m) {
+  const SmallMPlan pl = plan_small_m(n, (int)(k / 32), m);
+  return pl.splits > 1 ? (int64_t)pl.splits * m * n * 4 : 0;
+}
+
 hipError_t launch_gemm_small_m(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y,
-                               int64_t ldy, hipStream_t s) {
+                               int64_t ldy, void* ws, int64_t ws_bytes, hipStream_t s) {
   if (w.n == 0) return hipSuccess;
   KArgs a = base_args(w);
   a.x = x;
@@ -1058,10 +1145,26 @@ hipError_t launch_gemm_small_m(const PlaneView& w, const uint16_t* x, int64_t m,
   a.m = (int)m;
   a.x_rows = m;
   a.vec_y = ((uintptr_t)y % 16 == 0) && (ldy % 4 == 0);
-  if (m <= 16) return launch_cfg<1, kDense, false>(a, (int)m, 1, s);
-  if (m <= 32) return launch_cfg<2, kDense, false>(a, (int)m, 1, s);
-  if (m <= 48) return launch_cfg<3, kDense, false>(a, (int)m, 1, s);
-  return launch_cfg<4, kDense, false>(a, (int)m, 1, s);
+  SmallMPlan pl = plan_small_m(w.n, w.groups, m);
+  const int64_t need = pl.splits > 1 ? (int64_t)pl.splits * m * w.n * 4 : 0;
+  if (pl.splits > 1 && (ws == nullptr || ws_bytes < need)) pl.splits = 1;   // no workspace: one pass
+  if (pl.splits > 1) {
+    a.y = static_cast<float*>(ws);
+    a.ldy = w.n;
+    a.split_stride = m * w.n;
+    a.vec_y = ((uintptr_t)ws % 16 == 0) && (w.n % 4 == 0);
+  }
+  hipError_t e;
+  if (m <= 16) e = launch_cfg<1, kDense, false>(a, (int)m, 1, s, pl.wide_rows, pl.splits);
+  else if (m <= 32) e = launch_cfg<2, kDense, false>(a, (int)m, 1, s, pl.wide_rows, pl.splits);
+  else if (m <= 48) e = launch_cfg<3, kDense, false>(a, (int)m, 1, s, pl.wide_rows, pl.splits);
+  else e = launch_cfg<4, kDense, false>(a, (int)m, 1, s, pl.wide_rows, pl.splits);
+  if (e != hipSuccess || pl.splits == 1) return e;
+  const int64_t threads = m * ((w.n + 3) / 4);
+  const int vec = ((uintptr_t)ws % 16 == 0) && (w.n % 4 == 0) && ((uintptr_t)y % 16 == 0) && (ldy % 4 == 0);
+  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const float*>(ws), pl.splits, m, w.n, y, ldy, vec);
+  return hipGetLastError();
 }
 
 hipError_t launch_head2_scores(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,

@@ -169,6 +169,22 @@ Q3_API q3_status q3_gemv(const q3_matrix* w, const uint16_t* x, int64_t m, int64
 Q3_API q3_status q3_gemm_small_m(const q3_matrix* w, const uint16_t* x, int64_t m, int64_t ldx,
                                  float* y, int64_t ldy, void* stream);
 
+/* Device workspace bytes q3_gemm_small_m_ws can use for an n x k matrix and m
+ * tokens (host only, no device call); 0 when the product runs in one pass. */
+Q3_API int64_t q3_gemm_small_m_workspace_bytes(int64_t n, int64_t k, int64_t m);
+
+/* q3_gemm_small_m with a caller-owned workspace.  When the activations are too
+ * large to be staged in LDS whole (m * k above about 48K elements) and the
+ * matrix has few 16-row tiles, K is split over blocks: each split writes an
+ * fp32 partial plane into the workspace and a second launch adds the planes
+ * in split order, so results are run-to-run identical.  workspace: device
+ * memory, 16-byte aligned, of at least q3_gemm_small_m_workspace_bytes(n, k, m)
+ * bytes; NULL or a smaller workspace_bytes gives the one-pass product (never an
+ * error).  Calls that overlap in time must not share a workspace.  Same
+ * arguments, result tolerance and errors as q3_gemm_small_m otherwise. */
+Q3_API q3_status q3_gemm_small_m_ws(const q3_matrix* w, const uint16_t* x, int64_t m, int64_t ldx, float* y,
+                                    int64_t ldy, void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Router of an MoE verify round (Hibana page, "Adaptive speculation",
  * "Expert sharing": a verify round reads the weights of each expert chosen by
  * at least one of its drafted tokens).  logits fp32 [t][num_experts] (row pitch num_experts) ->

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
                                          "q3_layout2", "q3_pack2", "q3_unpack2", "q3_head2_scores",
                                          "q3_shortlist_workspace_bytes", "q3_shortlist", "q3_rescore_fp8",
                                          "q3_draft_head_workspace_bytes", "q3_draft_head", "q3_moe_budget_topk",
-                                         "q3_moe_mlp_workspace_bytes", "q3_moe_mlp", "q3_quantize"])
+                                         "q3_moe_mlp_workspace_bytes", "q3_moe_mlp", "q3_quantize",
+                                         "q3_gemm_small_m_workspace_bytes", "q3_gemm_small_m_ws"])
 
 
 def test_library_exports_every_declared_symbol(q3lib):
@@ -79,6 +80,37 @@ def test_workspace_sizes(q3lib):
     assert q3lib.q3_moe_mlp_workspace_bytes(64, 30, 1, 1) == 256 + 256
     assert q3lib.q3_moe_mlp_workspace_bytes(1536, 2048, 9, 8) == 0      # more than 64 pairs
     assert q3lib.q3_moe_mlp_workspace_bytes(1504, 2048, 8, 8) == 0      # I not a multiple of 32
+
+
+def test_gemm_small_m_workspace_sizes(q3lib):
+    ws = q3lib.q3_gemm_small_m_workspace_bytes
+    # activations staged in LDS whole (m * k up to about 48K elements): one pass, no workspace
+    assert ws(4096, 4096, 8) == 0
+    assert ws(96, 1024, 16) == 0
+    # a wide grid needs no K split: the 28672 x 8192 verify batch and the vocabulary projection
+    assert ws(28672, 8192, 16) == 0
+    assert ws(151936, 4096, 64) == 0
+    # few row tiles and streamed activations: fp32 partial planes, splits * m * n floats
+    assert ws(4096, 4096, 16) == 4 * 16 * 4096 * 4
+    assert ws(4096, 4096, 64) == 4 * 64 * 4096 * 4
+    assert ws(8192, 28672, 16) == 4 * 16 * 8192 * 4
+    assert ws(8192, 28672, 64) == 2 * 64 * 8192 * 4
+    # invalid shapes report no workspace
+    assert ws(4096, 4096, 65) == 0
+    assert ws(4096, 4100, 16) == 0
+    assert ws(0, 4096, 16) == 0
+
+
+def test_gemm_small_m_ws_validation(q3lib):
+    from bit_fp8_codebook_amd import _lib
+    fake = 0x1000
+    w = _lib.Q3Matrix(4096, 4096, fake, fake, fake)
+    f = q3lib.q3_gemm_small_m_ws
+    assert f(ctypes.byref(w), fake, 65, 4096, fake, 4096, fake, 1 << 20, None) == 2      # m > 64
+    assert f(ctypes.byref(w), fake, 0, 4096, fake, 4096, fake, 1 << 20, None) == 2
+    assert f(ctypes.byref(w), fake, 16, 4096, fake, 4096, fake + 4, 1 << 20, None) == 3  # workspace 16-aligned
+    assert f(ctypes.byref(w), fake, 16, 4000, fake, 4096, fake, 1 << 20, None) == 1      # ldx < k
+    assert f(None, fake, 16, 4096, fake, 4096, fake, 1 << 20, None) == 1
 
 
 def test_head_validation_rejects_before_any_hip_call(q3lib):
