@@ -88,6 +88,7 @@ struct KArgs {
   int sk;         // K split over the waves of a block (full-K mode)
   const int32_t* ids;
   int pairs_total, topk, x_by_slot;
+  int slice_cap;   // expert passes in full-K mode: token rows the LDS staging holds (<= 16, even)
   int num_experts;
   // kSwiGLU: tiles in the gate half; output terms h[2*pair + term][I]
   int half_tiles;
@@ -446,8 +447,12 @@ void linear_kernel(KArgs a) {
   const rsrc_t xr_rsrc = make_rsrc(a.x, (uint32_t)((a.x_rows - 1) * a.ldx * 2 + (int64_t)G * 64));
   const uint32_t ldx_bytes = (uint32_t)(a.ldx * 2);
 
-  for (int slice = 0; slice < total_tokens; slice += kSlice) {
-    const int cnt = total_tokens - slice < kSlice ? total_tokens - slice : kSlice;
+  // Tokens per slice: the matrix-core width, or for the expert passes in
+  // full-K mode the rows their LDS was sized for (an expert meets each token at
+  // most once per round, so one slice normally covers it).
+  const int cap = kGrouped && kMode == kShared ? a.slice_cap : kSlice;
+  for (int slice = 0; slice < total_tokens; slice += cap) {
+    const int cnt = total_tokens - slice < cap ? total_tokens - slice : cap;
     // Token slot j of this slice -> its x row and y row.
     auto xrow = [&](int j) -> int {
       if (kGrouped == kDownTerms) return 2 * pairs[(slice + j) >> 1] + ((slice + j) & 1);
@@ -1071,6 +1076,17 @@ hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t
   }
 }
 
+// Token rows an expert block stages at once: with distinct experts per token
+// (top-k routing) an expert has at most t pairs, so t rows (times the terms per
+// pair) cover it; more pairs (repeated ids) take further slices.  Even and at
+// most 16 (one matrix-core column tile).
+int expert_slice(int t, int pairs, int terms) {
+  int c = (t < pairs ? t : pairs) * terms;
+  c = c < 16 ? c : 16;
+  c = c < 2 ? 2 : c;
+  return c + (c & 1);
+}
+
 KArgs base_args(const PlaneView& w) {
   KArgs a{};
   a.code = w.code;
@@ -1221,8 +1237,8 @@ hipError_t launch_grouped(const ExpertView& w, const uint16_t* x, int64_t ldx, i
   a.x_by_slot = x_by_slot;
   a.vec_y = ((uintptr_t)y % 16 == 0) && (ldy % 4 == 0);
   a.x_rows = x_by_slot ? (int64_t)t * topk : t;
-  const int slice = a.pairs_total < 16 ? a.pairs_total : 16;
-  return launch_cfg<1, kExperts, false>(a, slice, (unsigned)w.num_experts, s);
+  a.slice_cap = expert_slice(t, a.pairs_total, 1);
+  return launch_cfg<1, kExperts, false>(a, a.slice_cap, (unsigned)w.num_experts, s);
 }
 
 hipError_t launch_moe_mlp(const ExpertView& gu, const ExpertView& dn, const uint16_t* x, int64_t ldx,
@@ -1244,7 +1260,8 @@ hipError_t launch_moe_mlp(const ExpertView& gu, const ExpertView& dn, const uint
   a.half_tiles = (int)(inter / 16);
   a.h = h;
   a.ldh = inter;
-  hipError_t e = launch_cfg<1, kSwiGLU, false>(a, pairs < 16 ? pairs : 16, (unsigned)gu.num_experts, s);
+  a.slice_cap = expert_slice(t, pairs, 1);
+  hipError_t e = launch_cfg<1, kSwiGLU, false>(a, a.slice_cap, (unsigned)gu.num_experts, s);
   if (e != hipSuccess) return e;
   KArgs b = base_args(dn.base);
   b.code_stride = dn.code_stride;
@@ -1259,7 +1276,8 @@ hipError_t launch_moe_mlp(const ExpertView& gu, const ExpertView& dn, const uint
   b.num_experts = dn.num_experts;
   b.part = part;
   b.ldp = ldp;
-  e = launch_cfg<1, kDownTerms, false>(b, 2 * pairs < 16 ? 2 * pairs : 16, (unsigned)dn.num_experts, s);
+  b.slice_cap = expert_slice(t, pairs, 2);
+  e = launch_cfg<1, kDownTerms, false>(b, b.slice_cap, (unsigned)dn.num_experts, s);
   if (e != hipSuccess) return e;
   return launch_moe_combine(part, ldp, ids, t, topk, dn.num_experts, logits, ld_logits, dn.base.n, out, ldo, s);
 }
