@@ -73,6 +73,25 @@ def test_grouped_one_token_many_experts(q3):
     run_round(q3, moe, 12)
 
 
+def test_grouped_repeated_ids_take_several_slices(q3):
+    # An id repeated inside a token's list gives an expert more (token, slot)
+    # pairs than there are tokens, beyond the rows its block stages at once:
+    # the block takes several slices.
+    moe = synth.make_moe(num_experts=6, k_gu=256, n_gu=128, k_dn=64, n_dn=130, tokens=2, topk=8, seed=9)
+    ids = np.array([[3, 3, 3, 3, 5, 5, 5, 5], [3, 3, 3, 3, 3, 3, 3, 3]], dtype=np.int32)
+    st_gu = stack_experts(q3, moe.experts_gu)
+    st_dn = stack_experts(q3, moe.experts_dn)
+    y_gu = q3.q3_grouped_expert_gemv(st_gu, dev(moe.x), dev(ids), False).cpu().numpy()
+    x_dn = np.ascontiguousarray(moe.x_dn[:, :8]).reshape(16, -1)
+    y_dn = q3.q3_grouped_expert_gemv(st_dn, dev(x_dn), dev(ids), True).cpu().numpy()
+    ref_gu, b_gu = oracle.grouped_linear(planes(moe.experts_gu), ids, moe.x, False)
+    ref_dn, b_dn = oracle.grouped_linear(planes(moe.experts_dn), ids, moe.x_dn[:, :8], True)
+    assert_close(y_gu, ref_gu.reshape(16, -1), b_gu.reshape(16, -1), "gate/up, repeated ids")
+    assert_close(y_dn, ref_dn.reshape(16, -1), b_dn.reshape(16, -1), "down, repeated ids")
+    out, ref, bound = _run_mlp(q3, moe, ids)
+    assert_close(out, ref, bound, "fused MLP, repeated ids")
+
+
 def test_grouped_config2_full_size(q3):
     """64 experts, gate/up 2048->1536, down 768->2048, 8 drafted tokens x top-8."""
     moe = synth.make_moe(seed=0)
