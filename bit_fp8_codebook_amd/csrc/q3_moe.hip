@@ -45,7 +45,11 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ lo
 // set is the `budget` experts of largest mass (equal mass: lower index), each
 // found by counting the experts that rank before it; the block's token then
 // ranks the kept experts by its logits the same way.  Block 0 also writes the
-// kept set in ascending order.
+// kept set in ascending order.  When the round's logits fit (T*E floats up to
+// kStageFloats), the block first copies them all to LDS with every load issued
+// before the first use, so the per-token passes cost one memory latency in all
+// instead of one per token; the arithmetic and its order are the same either
+// way.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off /= 2) v = fmaxf(v, __shfl_xor(v, off, 64));
@@ -57,18 +61,41 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+constexpr int kStageFloats = 8192;
+
 __global__ __launch_bounds__(1024) void budget_topk_kernel(const float* __restrict__ logits, int T, int E, int topk,
                                                            int budget, int32_t* __restrict__ ids,
-                                                           int32_t* __restrict__ experts) {
+                                                           int32_t* __restrict__ experts, int staged) {
   __shared__ float mass[1024];
   __shared__ float tok[1024];
   __shared__ int kept[1024];
-  extern __shared__ float stats[];   // [T][2]: max, exp-sum of each token's logits
+  extern __shared__ float dyn[];   // [T][2] max and exp-sum of each token's logits; then [T][E] logits if staged
+  float* const stats = dyn;
   const int t = blockIdx.x;
   const int e = threadIdx.x;
   const int lane = e & 63, wave = e >> 6, waves = blockDim.x >> 6;
+  const float* src = logits;
+  if (staged) {
+    float* const lg = dyn + 2 * T;
+    const int total = T * E;
+    for (int base = e; base < total; base += 4 * (int)blockDim.x) {
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = base + q * (int)blockDim.x;
+        v[q] = i < total ? logits[i] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = base + q * (int)blockDim.x;
+        if (i < total) lg[i] = v[q];
+      }
+    }
+    __syncthreads();
+    src = lg;
+  }
   for (int u = wave; u < T; u += waves) {
-    const float* row = logits + (int64_t)u * E;
+    const float* row = src + (int64_t)u * E;
     float mx = -__builtin_inff();
     for (int o = lane; o < E; o += 64) mx = fmaxf(mx, row[o]);
     mx = wave_max(mx);
@@ -83,9 +110,9 @@ __global__ __launch_bounds__(1024) void budget_topk_kernel(const float* __restri
   __syncthreads();
   if (e < E) {
     float m = 0.f;
-    for (int u = 0; u < T; ++u) m += expf(logits[(int64_t)u * E + e] - stats[2 * u]) / stats[2 * u + 1];
+    for (int u = 0; u < T; ++u) m += expf(src[(int64_t)u * E + e] - stats[2 * u]) / stats[2 * u + 1];
     mass[e] = m;
-    tok[e] = logits[(int64_t)t * E + e];
+    tok[e] = src[(int64_t)t * E + e];
   }
   __syncthreads();
   bool in = false;
@@ -112,9 +139,13 @@ __global__ __launch_bounds__(1024) void budget_topk_kernel(const float* __restri
 
 hipError_t launch_moe_budget_topk(const float* logits, int32_t t, int32_t e, int32_t topk, int32_t budget,
                                   int32_t* ids, int32_t* experts, hipStream_t s) {
-  const unsigned threads = (unsigned)((e + 63) / 64 * 64);
-  hipLaunchKernelGGL(budget_topk_kernel, dim3((unsigned)t), dim3(threads), (size_t)t * 2 * sizeof(float), s, logits,
-                     (int)t, (int)e, (int)topk, (int)budget, ids, experts);
+  // One thread per expert, at least four waves (the per-token passes are spread over the waves).
+  unsigned threads = (unsigned)((e + 63) / 64 * 64);
+  threads = threads < 256u ? 256u : threads;
+  const int staged = (int64_t)t * e <= kStageFloats;
+  const size_t shm = ((size_t)t * 2 + (staged ? (size_t)t * e : 0)) * sizeof(float);
+  hipLaunchKernelGGL(budget_topk_kernel, dim3((unsigned)t), dim3(threads), shm, s, logits, (int)t, (int)e, (int)topk,
+                     (int)budget, ids, experts, staged);
   return hipGetLastError();
 }
 
