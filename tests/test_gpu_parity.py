@@ -182,9 +182,9 @@ def test_config4_full_size_sampled_rows(q3):
 
 @pytest.mark.parametrize("n,k,m", [(90000, 1024, 64), (90000, 1536, 40), (90000, 2048, 33)])
 def test_many_row_groups_sampled_rows(q3, n, k, m):
-    # More row groups than a launch has blocks: blocks walk several groups;
-    # with an even step count a group's first step is loaded during the
-    # previous group's last one.
+    # The wide kernel on a tall matrix with 2, 3 and 4 steps of 512 k (the odd
+    # count ends on the step after its paired loop), several blocks per CU and
+    # a last row group that is only partly inside the matrix.
     layer, x = synth.make_linear(n, k, m, seed=k + m)
     w = pack_layer(q3, layer)
     y = q3.q3_gemm_small_m(w, dev(x)).cpu().numpy()
