@@ -1102,8 +1102,8 @@ KArgs base_args(const PlaneView& w) {
 // a block.  Streamed activations put whole row groups in a block: on a matrix
 // with few of them the grid would leave most of the chip idle, so K is split
 // over the blocks of a grid column as well (partial planes in a workspace,
-// then a fixed-order sum), and the wide kernel takes two row tiles per wave
-// instead of five.  Splits stop at 128 blocks (wide) or 192 (8-wave stream
+// then a fixed-order sum), and the wide kernel may take two row tiles per
+// wave instead of five.  Splits stop at 128 blocks (wide) or 192 (8-wave stream
 // blocks) and at two steps per split: measured on MI355X, more splits cost
 // more in partial planes and per-block start-up than they gain (N = 8192,
 // K = 28672, 16 tokens: 65.7 us in one pass, 28.7 us in 4 splits; a grid of
@@ -1131,7 +1131,13 @@ SmallMPlan plan_small_m(int64_t n, int groups, int64_t m) {
   const int steps = (((groups + 3) & ~3) + 15) / 16;
   int64_t blocks, target;
   if (nt >= kWideMinNT && groups % 16 == 0) {
-    if ((tiles + 19) / 20 < 384) pl.wide_rows = 2;
+    // Rounds of 256 blocks (one block per CU: the activation buffers take
+    // 134 KB of LDS) times the block's time: a five-tile block costs about
+    // 1.8x a two-tile one (measured at 64 tokens: 9 and 12.5 us per round
+    // and row tile), so five row tiles win only where they do not add a
+    // nearly empty round (N = 65536: 46 vs 50 us; N = 98304: 89 vs 74 us).
+    const int64_t rounds5 = ((tiles + 19) / 20 + 255) / 256, rounds2 = ((tiles + 7) / 8 + 255) / 256;
+    if (rounds2 * 50 < rounds5 * 90) pl.wide_rows = 2;
     blocks = (tiles + 4 * pl.wide_rows - 1) / (4 * pl.wide_rows);
     target = Q3_SPLIT_TARGET_WIDE;
   } else {
