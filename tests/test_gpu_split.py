@@ -125,3 +125,19 @@ def test_split_graph_replays(q3):
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy().view(np.uint32), eager.view(np.uint32)), f"replay {rep}"
+
+
+@pytest.mark.parametrize("n,k,m,split", [(65536, 2048, 40, False), (65536, 2048, 20, False),
+                                         (33600, 4096, 64, True), (33600, 4096, 40, True)])
+def test_wide_five_row_tiles_sampled_rows(q3, n, k, m, split):
+    """The wide kernel with five row tiles per wave at 2..4 column tiles, on its
+    own and with K split over blocks (a matrix whose five-tile grid has fewer
+    than 128 blocks but would gain nothing from two-tile blocks)."""
+    assert (splits_of(q3, n, k, m) > 1) == split
+    layer, x = synth.make_linear(n, k, m, seed=n + m)
+    w = pack_layer(q3, layer)
+    y = (q3.q3_gemm_small_m_ws(w, dev(x)) if split else q3.q3_gemm_small_m(w, dev(x))).cpu().numpy()
+    rng = np.random.default_rng(m)
+    rows = np.sort(np.concatenate([rng.choice(n, 120, replace=False), [0, 15, 16, 319, 320, n - 1]]))
+    y_ref, bound = oracle_linear(layer, x, rows=rows)
+    assert_close(y[:, rows], y_ref, bound, f"n={n} k={k} m={m}")
