@@ -968,9 +968,12 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* part, in
 
 // Launch shape: R row tiles per wave, W waves per block, K split sk (full-K
 // only).  Measured on MI355X over the decode shapes: tall matrices stream best
-// with fewer, longer-lived waves that each own two row tiles (a 4096 x 4096
-// launch already fills the chip with one row tile per wave and a 4-way K
-// split); activations that do not fit in LDS stream through 8-wave blocks.
+// with one row tile per wave in 8-wave blocks on the matrix cores (K=8192
+// N=28672: 19.5 -> 18.9 us, K=4096 N=151936: 44.5 -> 43.2 us against two row
+// tiles per wave in 4-wave blocks) and in 4-wave blocks on the vector ALUs (a
+// 4096 x 4096 launch already fills the chip with one row tile per wave and a
+// 4-way K split); activations that do not fit in LDS stream through 8-wave
+// blocks.
 struct Shape {
   int r, w, sk;
 };
@@ -986,7 +989,7 @@ Shape pick_shape(int64_t n, int groups, bool full_k, int tokens, bool dot) {
   return Shape{Q3_FORCE_R, Q3_FORCE_W, full_k ? Q3_FORCE_SK : 1};
 #else
   if (!full_k) return Shape{!dot && tokens > 32 && tiles >= 4096 ? 2 : 1, 8, 1};
-  if (tiles >= 1024) return Shape{dot ? 1 : 2, 4, 1};
+  if (tiles >= 1024) return dot ? Shape{1, 4, 1} : Shape{1, 8, 1};
   // Small matrices: split K over the block's waves up to about 1024 waves
   // (2048 when each wave has several tokens to multiply).
   const int64_t target = tokens > 4 ? 2048 : 1024;
