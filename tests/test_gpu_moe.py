@@ -351,3 +351,35 @@ def test_moe_mlp_graph_replays(q3):
         assert np.array_equal(out.cpu().numpy(), eager)
         q3.q3_moe_mlp(st_gu, st_dn, x, ids, logits, ws)      # eager work between replays
         torch.cuda.synchronize()
+
+
+def _random_rounds(count=10, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        E = int(rng.integers(2, 49))
+        topk = int(rng.integers(1, min(E, 8) + 1))
+        t = int(rng.integers(1, 64 // topk + 1))
+        n_gu = 64 * int(rng.integers(1, 9))                 # I = n_gu / 2, a multiple of 32
+        k_gu = 32 * int(rng.integers(1, 65))
+        n_dn = int(rng.integers(1, 400))
+        budget = int(rng.integers(topk, E + 1)) if rng.random() < 0.5 else None
+        out.append((E, topk, t, n_gu, k_gu, n_dn, budget))
+    return out
+
+
+@pytest.mark.parametrize("E,topk,t,n_gu,k_gu,n_dn,budget", _random_rounds())
+def test_moe_mlp_random_rounds(q3, E, topk, t, n_gu, k_gu, n_dn, budget):
+    """Seeded random rounds of the fused expert MLP (expert count, tokens,
+    top-k, ragged down rows, optional expert budget): routes from the device
+    router, outputs within the oracle's first-order bound."""
+    moe = synth.make_moe(num_experts=E, k_gu=k_gu, n_gu=n_gu, k_dn=n_gu // 2, n_dn=n_dn, tokens=t, topk=topk,
+                         seed=E * 100 + t)
+    lg = dev(moe.logits)
+    if budget is None:
+        ids = q3.q3_moe_topk(lg, topk).cpu().numpy()
+        assert np.array_equal(ids, oracle.topk_route(moe.logits, topk))
+    else:
+        ids = q3.q3_moe_budget_topk(lg, topk, budget)[0].cpu().numpy()
+    out, ref, bound = _run_mlp(q3, moe, ids)
+    assert_close(out, ref, bound, f"random round E={E} topk={topk} t={t} budget={budget}")
