@@ -137,7 +137,11 @@ Q3_API q3_status q3_layout(int64_t n, int64_t k, q3_layout_info* out);
  *   codebook    [n][8] E4M3FN bytes without NaN entries (not checked), 8-byte aligned
  *   codes       [n][ldc] uint8 out, 8-byte aligned, ldc % 8 == 0, ldc >= k
  *   scale_bytes [n][lds] uint8 out, lds >= k/32
- * k > 0, k % 32 == 0.  One launch; codebook fitting is not part of it. */
+ * k > 0, k % 32 == 0.  One launch; codebook fitting is not part of it.
+ * A group whose largest magnitude is below max|codebook| * 2^-111 (an all-zero
+ * group included) or above max|codebook| * 2^113 gets a scale byte outside
+ * [16, 240], the range in which the products below dequantise exactly; their
+ * outputs for rows with such groups are then not covered by the 1e-3 bound. */
 Q3_API q3_status q3_quantize(const float* w, int64_t ldw, const uint8_t* codebook, int64_t n, int64_t k,
                              uint8_t* codes, int64_t ldc, uint8_t* scale_bytes, int64_t lds, void* stream);
 
