@@ -48,7 +48,14 @@
 namespace q3 {
 namespace {
 
-constexpr int kFullKBudget = 96 * 1024;   // LDS bytes for full-K activation staging
+// LDS bytes for full-K activation staging: up to 136 KB, one block per CU
+// (measured on MI355X: 4096 x 4096 at 16 tokens 12.1 us streamed, 7.1 us
+// staged whole in 8-wave blocks with K split over the waves).
+#ifdef Q3_FULLK_KB
+constexpr int kFullKBudget = Q3_FULLK_KB * 1024;
+#else
+constexpr int kFullKBudget = 136 * 1024;
+#endif
 
 // How a block holds the activations.
 enum Mode : int {

@@ -178,7 +178,7 @@ Q3_API q3_status q3_gemm_small_m(const q3_matrix* w, const uint16_t* x, int64_t 
 Q3_API int64_t q3_gemm_small_m_workspace_bytes(int64_t n, int64_t k, int64_t m);
 
 /* q3_gemm_small_m with a caller-owned workspace.  When the activations are too
- * large to be staged in LDS whole (m * k above about 48K elements) and the
+ * large to be staged in LDS whole (m * k above about 68K elements) and the
  * matrix has few 16-row tiles, K is split over blocks: each split writes an
  * fp32 partial plane into the workspace and a second launch adds the planes
  * in split order, so results are run-to-run identical.  workspace: device

@@ -27,12 +27,13 @@ def splits_of(q3, n, k, m):
     return b // (4 * m * n) if b else 1
 
 
-# (n, k, m): 4096 x 4096 verify batches (wide kernel with two row tiles per
-# wave for m > 16, the 8-wave stream kernel for m <= 16), a ragged matrix whose
-# groups per row are not a multiple of 16 (stream kernel with 3 column tiles),
-# a small ragged one, and a K that leaves a partial last step.
-FULL = [(4096, 4096, 12), (4096, 4096, 16), (4096, 4096, 33), (4096, 4096, 64), (1000, 4128, 40),
-        (520, 3104, 17), (300, 3104, 16)]
+# (n, k, m): verify batches on 4096 rows (the 8-wave stream kernel for m <= 16
+# at K = 8192, the wide kernel with two row tiles per wave for m > 16), a
+# ragged matrix whose groups per row are not a multiple of 16 (stream kernel
+# with 3 column tiles), a small ragged one, and a K that leaves a partial last
+# step.
+FULL = [(4096, 8192, 12), (4096, 8192, 16), (4096, 4096, 33), (4096, 4096, 64), (1000, 4128, 40),
+        (520, 6176, 17), (300, 6176, 16)]
 
 
 @pytest.mark.parametrize("n,k,m", FULL)
@@ -73,7 +74,7 @@ def test_split_deterministic_and_workspace_contents_irrelevant(q3):
 
 
 def test_small_workspace_falls_back_to_one_pass(q3):
-    n, k, m = 4096, 4096, 16
+    n, k, m = 4096, 8192, 16
     layer, x = synth.make_linear(n, k, m, seed=12)
     w = pack_layer(q3, layer)
     xd = dev(x)
