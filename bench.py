@@ -337,10 +337,27 @@ def cpu_baseline(synth, budget_s=12.0):
             break
     per = el / reps
     payload = 4096 * 4096 * 13 // 32
+    # The same oracle with BLAS held to one thread, on a shorter bounded sample.
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            reps1, t1 = 0, time.perf_counter()
+            while True:
+                oracle.linear(cp, sp, layer.codebook, 4096, 4096, x)
+                reps1 += 1
+                el1 = time.perf_counter() - t1
+                if el1 >= budget_s / 2 or reps1 >= 50:
+                    break
+        single = dict(value=round(payload / (el1 / reps1) / 1e9, 4), unit="GB/s", cores=1,
+                      seconds_per_layer=round(el1 / reps1, 3), passes=reps1)
+    except ImportError:
+        pass
     return dict(value=round(payload / per / 1e9, 4), unit="GB/s", cores=int(min(threads, cores)),
                 kind="oracle", seconds_per_layer=round(per, 3), host_cores=cores,
                 sample=f"{reps} oracle passes over one 4096x4096 layer at M=1 "
-                       "(unpack from packed planes, fp64 dequant and product)")
+                       "(unpack from packed planes, fp64 dequant and product)",
+                single_thread=single)
 
 
 def read_traffic(dot: bool):
