@@ -356,7 +356,8 @@ def cpu_baseline(synth, budget_s=12.0):
     return dict(value=round(payload / per / 1e9, 4), unit="GB/s", cores=int(min(threads, cores)),
                 kind="oracle", seconds_per_layer=round(per, 3), host_cores=cores,
                 sample=f"{reps} oracle passes over one 4096x4096 layer at M=1 "
-                       "(unpack from packed planes, fp64 dequant and product)",
+                       "(unpack from packed planes, fp64 dequant and product; BLAS may use every "
+                       "core, the numpy unpacking and dequantisation run on one)",
                 single_thread=single)
 
 
