@@ -7,16 +7,19 @@
 // q3_linear.hip.  Here:
 //   * shortlist: per query the `size` (<= 16) largest scores, larger first,
 //     equal scores to the lower row.  Pass 1 runs kShortlistChunks blocks per
-//     query, each keeping the top 16 of its slice of rows (per-thread sorted
-//     lists, then a pairwise merge tree in LDS); pass 2 merges the chunks'
-//     lists with the same tree.  The order (score desc, row asc) is total, so
-//     the result is unique and run-to-run identical.
+//     query, each keeping the top 16 of its slice of rows: per-thread sorted
+//     lists, then 16 rounds that each take the best head over a wave's lists
+//     (DPP maximum of the key, then minimum of the row among equal keys),
+//     first within each wave, then over the waves' lists; pass 2 merges the
+//     chunks' lists the same way.  The order (score desc, row asc) is total,
+//     so the result is unique and run-to-run identical.
 //   * rescore: per query one block; each wave takes listed rows, streams the
 //     row's MXFP8 elements (E4M3FN, one E8M0 scale per 32) and the query's
 //     bf16 activations, widens the elements exactly to bf16 with the scale
 //     folded into the conversion, and accumulates v_dot2 products in fp32; a
 //     fixed-order lane reduction gives the score.  The block then picks the
-//     listed row with the largest score (ties to the lower row).
+//     listed row with the largest score (ties to the lower row) by the same
+//     wave-wide maximum and minimum.
 #include "q3_device.h"
 #include "q3_internal.h"
 
@@ -24,7 +27,7 @@ namespace q3 {
 namespace {
 
 constexpr int kList = kShortlistMax;   // entries kept per list
-constexpr int kThreads1 = 256;         // pass-1 block size
+constexpr int kThreads1 = 1024;        // pass-1 block size
 
 // Entries are (key, row): key = an order-preserving 32-bit image of the score
 // (larger score, larger key; -0 folded into +0, which compares equal to it as
@@ -37,7 +40,6 @@ __device__ __forceinline__ uint32_t score_key(float v) {
 __device__ __forceinline__ float key_score(uint32_t k) {
   return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
-__device__ __forceinline__ bool before(uint32_t a, int ia, uint32_t b, int ib) { return a > b || (a == b && ia < ib); }
 
 constexpr int kNoRow = 0x7FFFFFFF;
 
@@ -66,45 +68,54 @@ __device__ __forceinline__ void list_insert(uint32_t (&lk)[kList], int (&li)[kLi
   }
 }
 
-// Keep the better of (k, i) and the same pair from another lane via DPP.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ void dpp_best(uint32_t& k, int& i) {
-  const uint32_t k2 = (uint32_t)__builtin_amdgcn_update_dpp((int)k, (int)k, kCtrl, kRowMask, 0xF, false);
-  const int i2 = __builtin_amdgcn_update_dpp(i, i, kCtrl, kRowMask, 0xF, false);
-  const bool take = before(k2, i2, k, i);
-  k = take ? k2 : k;
-  i = take ? i2 : i;
+// Wave-wide maximum (minimum) of an unsigned value: DPP exchanges within
+// quads, half-rows and rows, then the row broadcasts that leave the wave's
+// result in lane 63, which is read out (the same value in every lane).  Lanes
+// a broadcast does not write see the identity (0 for the maximum, all ones
+// for the minimum), so no copy of the value is needed for them.
+template <bool kMax>
+__device__ __forceinline__ uint32_t wave_extreme(uint32_t v) {
+  constexpr int kId = kMax ? 0 : -1;
+  auto pick = [](uint32_t a, int b) {
+    const uint32_t u = (uint32_t)b;
+    return kMax ? (a > u ? a : u) : (a < u ? a : u);
+  };
+  v = pick(v, __builtin_amdgcn_update_dpp(kId, (int)v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+  v = pick(v, __builtin_amdgcn_update_dpp(kId, (int)v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+  v = pick(v, __builtin_amdgcn_update_dpp(kId, (int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v = pick(v, __builtin_amdgcn_update_dpp(kId, (int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+  v = pick(v, __builtin_amdgcn_update_dpp(kId, (int)v, 0x142, 0xA, 0xF, false));   // row_bcast15
+  v = pick(v, __builtin_amdgcn_update_dpp(kId, (int)v, 0x143, 0xC, 0xF, false));   // row_bcast31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// The wave's kList best entries over the sorted lists held by its 64 lanes,
-// best first (the same values in every lane).  Each round finds the best list
-// head with DPP exchanges (pairs, quads, half-row and row mirrors, then the
-// row broadcasts that leave the wave's best in lane 63), reads it out, and
-// the lane holding it (rows are distinct, so exactly one) drops its head.
-__device__ __forceinline__ void wave_top(uint32_t (&lk)[kList], int (&li)[kList], uint32_t (&ok)[kList],
-                                         int (&oi)[kList]) {
+// The wave's kList best entries over the sorted lists (L entries each) held
+// by its 64 lanes, best first (the same values in every lane).  Each round
+// takes the largest head key over the wave, then the lowest row among the
+// heads with that key (read from the one lane holding the key when there is
+// only one, the common case); that is the best head (rows of real entries
+// are distinct), and the lane holding it drops its head.  Several lanes can
+// hold the empty entry (0, kNoRow) at once; they all drop it, and every
+// later round then yields the same empty entry again.
+template <int L>
+__device__ __forceinline__ void wave_top(uint32_t (&lk)[L], int (&li)[L], uint32_t (&ok)[kList], int (&oi)[kList]) {
 #pragma unroll
   for (int o = 0; o < kList; ++o) {
-    uint32_t k = lk[0];
-    int id = li[0];
-    dpp_best<0xB1, 0xF>(k, id);    // quad_perm [1,0,3,2]
-    dpp_best<0x4E, 0xF>(k, id);    // quad_perm [2,3,0,1]
-    dpp_best<0x141, 0xF>(k, id);   // row_half_mirror
-    dpp_best<0x140, 0xF>(k, id);   // row_mirror: every lane holds its row's best
-    dpp_best<0x142, 0xA>(k, id);   // row_bcast15 into rows 1 and 3
-    dpp_best<0x143, 0xC>(k, id);   // row_bcast31 into rows 2 and 3: lane 63 holds the best
-    const uint32_t bk = (uint32_t)__builtin_amdgcn_readlane((int)k, 63);
-    const int bi = __builtin_amdgcn_readlane(id, 63);
+    const uint32_t bk = wave_extreme<true>(lk[0]);
+    const uint64_t hold = __ballot(lk[0] == bk);
+    const int bi = __builtin_popcountll(hold) == 1
+                       ? __builtin_amdgcn_readlane(li[0], (int)__builtin_ctzll(hold))
+                       : (int)wave_extreme<false>(lk[0] == bk ? (uint32_t)li[0] : (uint32_t)kNoRow);
     ok[o] = bk;
     oi[o] = bi;
     const bool mine = lk[0] == bk && li[0] == bi;
 #pragma unroll
-    for (int j = 0; j < kList - 1; ++j) {
+    for (int j = 0; j < L - 1; ++j) {
       lk[j] = mine ? lk[j + 1] : lk[j];
       li[j] = mine ? li[j + 1] : li[j];
     }
-    lk[kList - 1] = mine ? 0u : lk[kList - 1];
-    li[kList - 1] = mine ? kNoRow : li[kList - 1];
+    lk[L - 1] = mine ? 0u : lk[L - 1];
+    li[L - 1] = mine ? kNoRow : li[L - 1];
   }
 }
 
@@ -115,7 +126,10 @@ struct Cand {
 
 // Pass 1: block (c, q) keeps the top kList rows of chunk c of query q:
 // per-lane lists, the top of each wave, then the top of the block's waves.
+// A lane's rows of the chunk (two or three for a 151936-row head) are loaded
+// in one batch of up to kBatch1 before any insertion.
 constexpr int kWaves1 = kThreads1 / 64;
+constexpr int kBatch1 = 16;
 __global__ __launch_bounds__(kThreads1) void shortlist_chunks(const float* __restrict__ scores, int64_t n, int64_t ld,
                                                               Cand* __restrict__ cand) {
   __shared__ uint32_t sk[kWaves1 * kList];
@@ -129,16 +143,15 @@ __global__ __launch_bounds__(kThreads1) void shortlist_chunks(const float* __res
   int li[kList];
   empty_list(lk, li);
   const float* row = scores + (int64_t)q * ld;
-  // Eight loads in flight per lane before any insertion.
-  for (int64_t base = r0 + threadIdx.x; base < r1; base += 8 * kThreads1) {
-    float v[8];
+  for (int64_t base = r0 + threadIdx.x; base < r1; base += kBatch1 * kThreads1) {
+    float v[kBatch1];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kBatch1; ++u) {
       const int64_t r = base + (int64_t)u * kThreads1;
       v[u] = r < r1 ? row[r] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kBatch1; ++u) {
       const int64_t r = base + (int64_t)u * kThreads1;
       if (r < r1) list_insert(lk, li, score_key(v[u]), (int)r);
     }
@@ -155,13 +168,17 @@ __global__ __launch_bounds__(kThreads1) void shortlist_chunks(const float* __res
   }
   __syncthreads();
   if (wave == 0) {
-    // lane t holds entry t of the waves' lists, as a one-entry list
-    empty_list(lk, li);
-    if (lane < kWaves1 * kList) {
-      lk[0] = sk[lane];
-      li[0] = si[lane];
+    // Lane t holds entries 4(t%4) .. 4(t%4)+3 of wave t/4's list: a sorted
+    // four-entry list per lane, the 16 waves' lists between them.
+    static_assert(kWaves1 * kList == 4 * 64, "four entries per lane");
+    uint32_t k4[4];
+    int i4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      k4[j] = sk[4 * lane + j];
+      i4[j] = si[4 * lane + j];
     }
-    wave_top(lk, li, ok, oi);
+    wave_top(k4, i4, ok, oi);
     Cand* out = cand + ((int64_t)q * kShortlistChunks + c) * kList;
 #pragma unroll
     for (int j = 0; j < kList; ++j)
@@ -276,11 +293,15 @@ __global__ __launch_bounds__(64 * kRescoreWaves) void rescore_kernel(Mxfp8View h
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int bj = 0;
-    for (int j = 1; j < size; ++j)
-      if (before(score_key(sy[j]), sid[j], score_key(sy[bj]), sid[bj])) bj = j;
-    best[q] = sid[bj];
+  if (wave == 0) {
+    // The listed row with the largest score, equal scores to the lower id
+    // (signed: ids are the caller's when no list is given), across lanes.
+    const bool live = lane < size;
+    const uint32_t k = live ? score_key(sy[lane]) : 0u;
+    const uint32_t id = live ? (uint32_t)sid[lane] ^ 0x80000000u : 0xFFFFFFFFu;
+    const uint32_t bk = wave_extreme<true>(k);
+    const uint32_t bi = wave_extreme<false>(live && k == bk ? id : 0xFFFFFFFFu);
+    if (lane == 0) best[q] = (int)(bi ^ 0x80000000u);
   }
 }
 
