@@ -43,9 +43,10 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 
 constexpr int kNoRow = 0x7FFFFFFF;
 
-__device__ __forceinline__ void empty_list(uint32_t (&lk)[kList], int (&li)[kList]) {
+template <int L>
+__device__ __forceinline__ void empty_list(uint32_t (&lk)[L], int (&li)[L]) {
 #pragma unroll
-  for (int j = 0; j < kList; ++j) {
+  for (int j = 0; j < L; ++j) {
     lk[j] = 0u;
     li[j] = kNoRow;
   }
@@ -53,13 +54,14 @@ __device__ __forceinline__ void empty_list(uint32_t (&lk)[kList], int (&li)[kLis
 
 // Insert (k, id) into a lane's sorted list, branch-free.  The caller scans
 // rows in increasing order, so the new entry goes after every kept entry with
-// an equal or larger key (and falls off the end if there are kList of them).
-__device__ __forceinline__ void list_insert(uint32_t (&lk)[kList], int (&li)[kList], uint32_t k, int id) {
-  bool g[kList];   // g[j]: entry j stays in front of the new one
+// an equal or larger key (and falls off the end if there are L of them).
+template <int L>
+__device__ __forceinline__ void list_insert(uint32_t (&lk)[L], int (&li)[L], uint32_t k, int id) {
+  bool g[L];   // g[j]: entry j stays in front of the new one
 #pragma unroll
-  for (int j = 0; j < kList; ++j) g[j] = lk[j] >= k;
+  for (int j = 0; j < L; ++j) g[j] = lk[j] >= k;
 #pragma unroll
-  for (int j = kList - 1; j >= 0; --j) {
+  for (int j = L - 1; j >= 0; --j) {
     const bool gp = j == 0 ? true : g[j - 1];
     const uint32_t pk = j == 0 ? 0u : lk[j - 1];
     const int pi = j == 0 ? 0 : li[j - 1];
@@ -127,9 +129,14 @@ struct Cand {
 // Pass 1: block (c, q) keeps the top kList rows of chunk c of query q:
 // per-lane lists, the top of each wave, then the top of the block's waves.
 // A lane's rows of the chunk (two or three for a 151936-row head) are loaded
-// in one batch of up to kBatch1 before any insertion.
+// in one batch of up to kBatch1 before any insertion.  A lane that meets at
+// most L rows keeps them all in an L-entry list (L = 4 when every lane meets
+// at most 4, else kList), which makes the insertions and the wave's rounds
+// cheaper: 16 waves share the CU, so the pass is bound by instruction issue.
 constexpr int kWaves1 = kThreads1 / 64;
 constexpr int kBatch1 = 16;
+constexpr int kShortRun = 4;
+template <int L>
 __global__ __launch_bounds__(kThreads1) void shortlist_chunks(const float* __restrict__ scores, int64_t n, int64_t ld,
                                                               Cand* __restrict__ cand) {
   __shared__ uint32_t sk[kWaves1 * kList];
@@ -139,8 +146,8 @@ __global__ __launch_bounds__(kThreads1) void shortlist_chunks(const float* __res
   const int64_t cs = (n + kShortlistChunks - 1) / kShortlistChunks;
   const int64_t r0 = (int64_t)c * cs;
   const int64_t r1 = r0 + cs < n ? r0 + cs : n;
-  uint32_t lk[kList];
-  int li[kList];
+  uint32_t lk[L];
+  int li[L];
   empty_list(lk, li);
   const float* row = scores + (int64_t)q * ld;
   for (int64_t base = r0 + threadIdx.x; base < r1; base += kBatch1 * kThreads1) {
@@ -170,13 +177,13 @@ __global__ __launch_bounds__(kThreads1) void shortlist_chunks(const float* __res
   if (wave == 0) {
     // Lane t holds entries 4(t%4) .. 4(t%4)+3 of wave t/4's list: a sorted
     // four-entry list per lane, the 16 waves' lists between them.
-    static_assert(kWaves1 * kList == 4 * 64, "four entries per lane");
-    uint32_t k4[4];
-    int i4[4];
+    static_assert(kWaves1 * kList == kShortRun * 64, "four entries per lane");
+    uint32_t k4[kShortRun];
+    int i4[kShortRun];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      k4[j] = sk[4 * lane + j];
-      i4[j] = si[4 * lane + j];
+    for (int j = 0; j < kShortRun; ++j) {
+      k4[j] = sk[kShortRun * lane + j];
+      i4[j] = si[kShortRun * lane + j];
     }
     wave_top(k4, i4, ok, oi);
     Cand* out = cand + ((int64_t)q * kShortlistChunks + c) * kList;
@@ -310,7 +317,13 @@ __global__ __launch_bounds__(64 * kRescoreWaves) void rescore_kernel(Mxfp8View h
 hipError_t launch_shortlist(const float* scores, int64_t m, int64_t n, int64_t ld, int32_t size, void* cand,
                             int32_t* ids, float* vals, hipStream_t s) {
   Cand* c = static_cast<Cand*>(cand);
-  hipLaunchKernelGGL(shortlist_chunks, dim3(kShortlistChunks, (unsigned)m), dim3(kThreads1), 0, s, scores, n, ld, c);
+  const int64_t rows_per_lane = ((n + kShortlistChunks - 1) / kShortlistChunks + kThreads1 - 1) / kThreads1;
+  if (rows_per_lane <= kShortRun)
+    hipLaunchKernelGGL(shortlist_chunks<kShortRun>, dim3(kShortlistChunks, (unsigned)m), dim3(kThreads1), 0, s, scores,
+                       n, ld, c);
+  else
+    hipLaunchKernelGGL(shortlist_chunks<kList>, dim3(kShortlistChunks, (unsigned)m), dim3(kThreads1), 0, s, scores, n,
+                       ld, c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !ids) return e;
   hipLaunchKernelGGL(shortlist_merge, dim3((unsigned)m), dim3(64), 0, s, c, size, ids, vals);

@@ -73,7 +73,11 @@ def _check_list(ids, vals, scores, size):
 
 
 @pytest.mark.parametrize("m,n,size,ties", [(1, 151936, 16, False), (3, 1000, 16, True), (2, 17, 16, True),
-                                           (1, 16, 16, False), (4, 70000, 5, True), (1, 1024, 1, False)])
+                                           (1, 16, 16, False), (4, 70000, 5, True), (1, 1024, 1, False),
+                                           # up to 4 rows per lane of the first pass (four-entry lists), then more
+                                           # (full lists), and more than one load batch per lane
+                                           (1, 262144, 16, True), (2, 262145, 16, True), (1, 300000, 16, False),
+                                           (1, 1100000, 16, True)])
 def test_shortlist_exact(q3, m, n, size, ties):
     rng = np.random.default_rng(n + size)
     if ties:
