@@ -44,7 +44,8 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ lo
 // in token order, so every block gets the same masses bit for bit.  The kept
 // set is the `budget` experts of largest mass (equal mass: lower index), each
 // found by counting the experts that rank before it; the block's token then
-// ranks the kept experts by its logits the same way.  Block 0 also writes the
+// ranks the kept experts by its logits the same way (with up to 64 experts, in
+// registers of the one wave that holds them all).  Block 0 also writes the
 // kept set in ascending order.  When the round's logits fit (T*E floats up to
 // kStageFloats), the block first copies them all to LDS with every load issued
 // before the first use, so the per-token passes cost one memory latency in all
@@ -108,6 +109,37 @@ __global__ __launch_bounds__(1024) void budget_topk_kernel(const float* __restri
     }
   }
   __syncthreads();
+  if (E <= 64) {
+    // Every expert sits in wave 0, one per lane: masses, the kept set and the
+    // token's ranking stay in registers, each expert's value broadcast with
+    // readlane (same arithmetic and order as below, no LDS round trip per
+    // expert and no further barrier).
+    if (wave != 0) return;
+    const bool live = lane < E;
+    float m = 0.f, tk = 0.f;
+    if (live) {
+      for (int u = 0; u < T; ++u) m += expf(src[(int64_t)u * E + lane] - stats[2 * u]) / stats[2 * u + 1];
+      tk = src[(int64_t)t * E + lane];
+    }
+    int rank = 0;
+    for (int o = 0; o < E; ++o) {
+      const float mo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), o));
+      rank += ranks_before(mo, o, m, lane) ? 1 : 0;
+    }
+    const bool in = live && rank < budget;
+    const uint64_t keep = __ballot(in);
+    int r = 0;
+    for (uint64_t b = keep; b != 0; b &= b - 1) {
+      const int o = __builtin_ctzll(b);
+      const float to = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tk), o));
+      r += ranks_before(to, o, tk, lane) ? 1 : 0;
+    }
+    if (in) {
+      if (r < topk) ids[(int64_t)t * topk + r] = lane;
+      if (t == 0 && experts) experts[__popcll(keep & ((1ull << lane) - 1ull))] = lane;
+    }
+    return;
+  }
   if (e < E) {
     float m = 0.f;
     for (int u = 0; u < T; ++u) m += expf(src[(int64_t)u * E + e] - stats[2 * u]) / stats[2 * u + 1];
