@@ -28,6 +28,14 @@ def test_topk_matches_oracle(q3, t, E, topk):
     assert np.array_equal(ids, oracle.topk_route(logits, topk))
 
 
+@pytest.mark.parametrize("E", [40, 64, 65, 100])
+def test_topk_many_ties(q3, E):
+    """Equal logits go to the lower expert, with experts in one wave or several."""
+    logits = np.random.default_rng(E).integers(-2, 3, (6, E)).astype(np.float32)
+    ids = q3.q3_moe_topk(dev(logits), 7).cpu().numpy()
+    assert np.array_equal(ids, oracle.topk_route(logits, 7))
+
+
 def stack_experts(q3, layers):
     L = layers[0]
     st = q3.empty_stack(len(layers), L.n, L.k, "cuda")
