@@ -224,9 +224,10 @@ __global__ __launch_bounds__(64) void shortlist_merge(const Cand* __restrict__ c
 }
 
 // Rescore: block q scores the listed rows of query q with the MXFP8 head, one
-// wave per listed row.  Lane l takes elements 64l .. 64l+63 of each 4096-wide
-// slice of K: four 16-byte element loads, eight 16-byte activation loads and
-// its two scale bytes, all issued before any arithmetic.  With `cand` set the
+// wave per listed row.  Lane l takes elements 1024p + 16l .. +15 (p = 0..3) of
+// each 4096-wide slice of K: four 16-byte element loads (each instruction
+// reads 1 KB of the row contiguously), eight 16-byte activation loads and four
+// scale bytes, all issued before any arithmetic.  With `cand` set the
 // block first merges the query's chunk lists (pass 2 of the shortlist) and
 // writes the list to ids.
 constexpr int kRescoreWaves = kList;
@@ -264,24 +265,23 @@ __global__ __launch_bounds__(64 * kRescoreWaves) void rescore_kernel(Mxfp8View h
     const bool ok = id >= 0 && id < h.n;
     float acc = 0.f;
     for (int64_t k0 = 0; k0 < h.k; k0 += 4096) {
-      const int64_t kl = k0 + 64 * lane;            // the lane's first element of this slice
+      // Lane l takes elements k0 + 1024p + 16l .. +15 (p = 0..3): each element
+      // load reads 1 KB of the row contiguously, and the activations and the
+      // scale byte of those 16 elements follow the same positions.
       u32x4 e[4], xv[8];
-      uint32_t sb[2];
+      uint32_t sb[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const int64_t kp = kl + 16 * p;             // 16 elements, all in or all out (k % 32 == 0)
-        e[p] = bload128(er, ok && kp < h.k ? (uint32_t)(id * h.lde + kp) : kOob);
-      }
-#pragma unroll
-      for (int p = 0; p < 8; ++p) xv[p] = bload128(xr, kl + 8 * p < h.k ? (uint32_t)(2 * (kl + 8 * p)) : kOob);
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int64_t kg = kl + 32 * g;
-        sb[g] = bload8(sr, ok && kg < h.k ? (uint32_t)(id * h.lds + kg / 32) : kOob);
+        const int64_t kp = k0 + 1024 * p + 16 * lane;   // 16 elements, all in or all out (k % 32 == 0)
+        const bool in = kp < h.k;
+        e[p] = bload128(er, ok && in ? (uint32_t)(id * h.lde + kp) : kOob);
+        xv[2 * p] = bload128(xr, in ? (uint32_t)(2 * kp) : kOob);
+        xv[2 * p + 1] = bload128(xr, in ? (uint32_t)(2 * kp + 16) : kOob);
+        sb[p] = bload8(sr, ok && in ? (uint32_t)(id * h.lds + kp / 32) : kOob);
       }
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const float sc = e8m0_to_f32(sb[p / 2]);
+        const float sc = e8m0_to_f32(sb[p]);
         const uint32_t wd[4] = {e[p].x, e[p].y, e[p].z, e[p].w};
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
