@@ -211,9 +211,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   __syncthreads();
   const int64_t row = (int64_t)blockIdx.x * 256 + tid;
   if (row >= n) return;
+  // The slots' rows are loaded eight at a time before any of them is added
+  // (rows of slots without a routed expert lie in the same buffer and are
+  // read but never added), then summed in slot order.
   float sum = 0.f;
-  for (int q = 0; q < topk; ++q)
-    if (pw[q] != 0.f) sum += pw[q] * part[(int64_t)(tk * topk + q) * ldp + row];
+  for (int q0 = 0; q0 < topk; q0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = q0 + j < topk ? part[(int64_t)(tk * topk + q0 + j) * ldp + row] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (q0 + j < topk && pw[q0 + j] != 0.f) sum += pw[q0 + j] * v[j];
+  }
   out[(int64_t)tk * ldo + row] = sum;
 }
 
