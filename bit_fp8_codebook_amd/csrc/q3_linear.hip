@@ -949,10 +949,14 @@ hipError_t launch_wide(const KArgs& a, unsigned splits, hipStream_t s) {
 }
 
 // Sum of the K splits' partial planes in split order: y[r][c] = sum_z
-// part[z][r][c] (part rows of n floats, planes m*n apart).  Four columns per
-// thread.
-__global__ __launch_bounds__(256) void split_reduce_kernel(const float* part, int splits, int64_t m, int64_t n,
-                                                           float* y, int64_t ldy, int vec) {
+// part[z][r][c] (part rows of n floats, planes m*n apart), for S splits (a
+// power of two up to kMaxSplits).  Four columns per thread; every plane's
+// values are loaded before the first add, so the splits cost one memory
+// latency, not one each.
+constexpr int kMaxSplits = 16;
+template <int S>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* part, int64_t m, int64_t n, float* y,
+                                                           int64_t ldy, int vec) {
   const int64_t nq = (n + 3) / 4;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= m * nq) return;
@@ -961,14 +965,26 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* part, in
   const float* src = part + r * n + c;
   float* dst = y + r * ldy + c;
   if (vec && c + 3 < n) {
-    f32x4 acc = *reinterpret_cast<const f32x4*>(src);
-    for (int z = 1; z < splits; ++z) acc += *reinterpret_cast<const f32x4*>(src + z * plane);
+    f32x4 v[S];
+#pragma unroll
+    for (int z = 0; z < S; ++z) v[z] = *reinterpret_cast<const f32x4*>(src + z * plane);
+    f32x4 acc = v[0];
+#pragma unroll
+    for (int z = 1; z < S; ++z) acc += v[z];
     *reinterpret_cast<f32x4*>(dst) = acc;
   } else {
-    for (int v = 0; v < 4 && c + v < n; ++v) {
-      float acc = src[v];
-      for (int z = 1; z < splits; ++z) acc += src[z * plane + v];
-      dst[v] = acc;
+    const int qn = n - c < 4 ? (int)(n - c) : 4;   // columns of this thread
+    float v[4][S];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int z = 0; z < S; ++z) v[q][z] = src[z * plane + (q < qn ? q : 0)];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float acc = v[q][0];
+#pragma unroll
+      for (int z = 1; z < S; ++z) acc += v[q][z];
+      if (q < qn) dst[q] = acc;
     }
   }
 }
@@ -1194,8 +1210,17 @@ hipError_t launch_gemm_small_m(const PlaneView& w, const uint16_t* x, int64_t m,
   if (e != hipSuccess || pl.splits == 1) return e;
   const int64_t threads = m * ((w.n + 3) / 4);
   const int vec = ((uintptr_t)ws % 16 == 0) && (w.n % 4 == 0) && ((uintptr_t)y % 16 == 0) && (ldy % 4 == 0);
-  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                     static_cast<const float*>(ws), pl.splits, m, w.n, y, ldy, vec);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  const float* part = static_cast<const float*>(ws);
+  switch (pl.splits) {
+    case 2: hipLaunchKernelGGL(split_reduce_kernel<2>, grid, dim3(256), 0, s, part, m, w.n, y, ldy, vec); break;
+    case 4: hipLaunchKernelGGL(split_reduce_kernel<4>, grid, dim3(256), 0, s, part, m, w.n, y, ldy, vec); break;
+    case 8: hipLaunchKernelGGL(split_reduce_kernel<8>, grid, dim3(256), 0, s, part, m, w.n, y, ldy, vec); break;
+    case kMaxSplits:
+      hipLaunchKernelGGL(split_reduce_kernel<kMaxSplits>, grid, dim3(256), 0, s, part, m, w.n, y, ldy, vec);
+      break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
