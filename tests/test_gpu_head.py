@@ -129,7 +129,8 @@ def check_decision(ids, y8, best, y_ref_all, b_ref_all):
         assert lo >= hi
 
 
-@pytest.mark.parametrize("n,k,m,size", [(200, 4096, 1, 16), (300, 1056, 3, 7), (40, 32, 2, 16)])
+@pytest.mark.parametrize("n,k,m,size", [(200, 4096, 1, 16), (300, 1056, 3, 7), (40, 32, 2, 16),
+                                        (64, 4128, 2, 5), (90, 9216, 1, 16)])   # second, partial 4096-wide slice
 def test_rescore_parity_and_decision(q3, n, k, m, size):
     head, x = synth.make_head(n, k, m, seed=n * k + m)
     _, h8 = pack_head(q3, head)
