@@ -30,7 +30,6 @@ N(0,1) activations); no dataset or trained weight is involved.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -38,6 +37,8 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+from bench_traffic import source_hash  # noqa: E402  (hash of the library sources the counters were taken on)
 
 HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
@@ -48,16 +49,6 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "bit_fp8_codebook_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode())
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def to_dev(a):
@@ -118,16 +109,25 @@ def capture(fn, stream):
     return g
 
 
-def time_graph(g, stream, reps: int, warmup: int) -> float:
+TRIALS = 5
+
+
+def time_graph(g, stream, reps: int, warmup: int, trials: int = TRIALS):
+    """Median over `trials` timings of `reps` back-to-back replays (ms per
+    replay), and every trial's figure."""
     import torch
+    per = []
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             g.replay()
         torch.cuda.synchronize()
-        with Timer(stream) as t:
-            for _ in range(reps):
-                g.replay()
-    return t.ms / reps
+        for _ in range(trials):
+            with Timer(stream) as t:
+                for _ in range(reps):
+                    g.replay()
+            per.append(t.ms / reps)
+    s = sorted(per)
+    return s[len(s) // 2], per
 
 
 def algorithmic_bytes(n, k, m):
@@ -155,11 +155,12 @@ def linear_point(q3, synth, n, k, m, kernel, reps=20, warmup=3, name=""):
     stream = torch.cuda.Stream()
     cyc = cycles_for(len(ws))
     g = capture(lambda: [fn(w, xd, y) for _ in range(cyc) for w in ws], stream)
-    ms = time_graph(g, stream, reps, warmup)
+    ms, trials = time_graph(g, stream, reps, warmup)
     us = ms * 1e3 / (cyc * len(ws))
     payload = n * k * 13 // 32
     flops = 2.0 * m * n * k
     pt = dict(name=name, n=n, k=k, m=m, kernel=kernel, copies=len(ws), us_per_launch=round(us, 2),
+              trials_us=[round(t * 1e3 / (cyc * len(ws)), 2) for t in trials],
               payload_GBps=round(payload / us / 1e3, 1),
               pct_of_8TBps=round(100 * payload / us / 1e3 / HBM_PEAK_GBPS, 1),
               algorithmic_GBps=round(algorithmic_bytes(n, k, m) / us / 1e3, 1),
@@ -227,7 +228,7 @@ def moe_point(q3, synth, budget=None, fused=False, reps=20, warmup=3):
 
     stream = torch.cuda.Stream()
     g = capture(round_all, stream)
-    ms = time_graph(g, stream, reps, warmup)
+    ms, trials = time_graph(g, stream, reps, warmup)
     us = ms * 1e3 / (cyc * len(stacks))
     union = int(np.unique(ids.cpu().numpy()).size)
     payload = union * per_expert
@@ -238,12 +239,22 @@ def moe_point(q3, synth, budget=None, fused=False, reps=20, warmup=3):
     name = ("moe_mlp_round" if fused else "moe_verify_round") + ("" if budget is None else f"_budget{budget}")
     pt = dict(name=name, experts=E, tokens=t, topk=topk, budget=budget, experts_read=union,
               routing_mass_read=round(read_mass, 4),
-              copies=len(stacks), us_per_round=round(us, 2), union_payload_bytes=payload,
+              copies=len(stacks), us_per_round=round(us, 2),
+              trials_us=[round(t_ * 1e3 / (cyc * len(stacks)), 2) for t_ in trials],
+              union_payload_bytes=payload,
               payload_GBps=round(payload / us / 1e3, 1),
               pct_of_8TBps=round(100 * payload / us / 1e3 / HBM_PEAK_GBPS, 1),
               tokens_per_s=round(t / (us * 1e-6), 1),
               kernel=("router + fused SwiGLU gate/up + down with combine" if fused
                       else "mfma grouped + top-k router"))
+    if budget is None and not fused:
+        # Union pin: a round's two expert passes read |U| experts' planes and
+        # codebooks once (HBM counters of the same sources, when committed).
+        pt["union_bytes_with_codebooks"] = union * (per_expert + 8 * (st_gu0.n + st_dn0.n))
+        tr = moe_traffic()
+        if tr is not None:
+            pt["hbm_read_bytes_per_round"] = tr["read_bytes_per_round"]
+            pt["hbm_read_over_union_bytes"] = round(tr["read_bytes_per_round"] / pt["union_bytes_with_codebooks"], 4)
     del stacks, g
     torch.cuda.empty_cache()
     return pt
@@ -298,11 +309,12 @@ def draft_head_point(q3, synth, n=151936, k=4096, m=1, size=16, reps=10, warmup=
     stream = torch.cuda.Stream()
     cyc = cycles_for(len(ws))
     g = capture(lambda: [q3.q3_draft_head(w, h8, xd, size, work) for _ in range(cyc) for w in ws], stream)
-    ms = time_graph(g, stream, reps, warmup)
+    ms, trials = time_graph(g, stream, reps, warmup)
     us = ms * 1e3 / (cyc * len(ws))
     payload = w0.payload_bytes + m * size * (k + k // 32)     # 2-bit head + the listed MXFP8 rows
     pt = dict(name="draft head K=4096 N=151936 M=1 (2-bit shortlist of 16, MXFP8 rescore)", n=n, k=k, m=m,
-              shortlist=size, copies=len(ws), us_per_decision=round(us, 2), payload_bytes=payload,
+              shortlist=size, copies=len(ws), us_per_decision=round(us, 2),
+              trials_us=[round(t * 1e3 / (cyc * len(ws)), 2) for t in trials], payload_bytes=payload,
               payload_GBps=round(payload / us / 1e3, 1),
               pct_of_8TBps=round(100 * payload / us / 1e3 / HBM_PEAK_GBPS, 1),
               decisions_per_s=round(m / (us * 1e-6), 1),
@@ -310,6 +322,71 @@ def draft_head_point(q3, synth, n=151936, k=4096, m=1, size=16, reps=10, warmup=
     del ws, w0, h8, g, work
     torch.cuda.empty_cache()
     return pt
+
+
+# ------------------------------------------------------------ read ceilings
+
+def read_ceiling(nbytes: int, configs, reps: int = 10, warmup: int = 2, name: str = ""):
+    """The best a launch that only streams `nbytes` achieves on this GPU, timed
+    like the products: graph-replayed back-to-back launches over distinct
+    copies (one cycle >= 2x the last-level cache), median of 5 trials, over a
+    sweep of (blocks, loads in flight per thread).  Also the cost of one
+    dependent launch of an empty kernel (the per-launch floor)."""
+    import torch
+    import bench_ceiling
+    copies = copies_for(nbytes)
+    bufs = [torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    sp = stream.cuda_stream
+    cyc = cycles_for(copies)
+    launches = cyc * copies
+    sweep = []
+    for blocks, unroll in configs:
+        g = capture(lambda: [bench_ceiling.read(b, blocks, unroll, sink, sp) for _ in range(cyc) for b in bufs],
+                    stream)
+        ms, _ = time_graph(g, stream, reps, warmup)
+        sweep.append((round(ms * 1e3 / launches, 3), blocks, unroll))
+        del g
+    g = capture(lambda: [bench_ceiling.empty(256, sp) for _ in range(launches)], stream)
+    empty_us = time_graph(g, stream, reps, warmup)[0] * 1e3 / launches
+    del g, bufs
+    torch.cuda.empty_cache()
+    us, blocks, unroll = min(sweep)
+    return dict(name=name, bytes=nbytes, copies=copies, launches_per_graph=launches, us_per_launch=us,
+                GBps=round(nbytes / us / 1e3, 1), pct_of_8TBps=round(100 * nbytes / us / 1e3 / HBM_PEAK_GBPS, 1),
+                best_blocks=blocks, best_loads_in_flight_per_thread=unroll,
+                empty_kernel_us_per_launch=round(empty_us, 3),
+                sweep_us=[[u, b, r] for u, b, r in sweep])
+
+
+# Launch shapes swept per size: (blocks of 256 threads, 16-byte loads in flight per thread).
+CEILING_SWEEPS = {
+    "layer_4096x4096": (4096 * 4096 * 13 // 32,
+                        [(b, u) for b in (256, 512, 1024, 1664, 2048) for u in (1, 2, 4, 8)]),
+    "layer_K8192_N28672": (28672 * 8192 * 13 // 32,
+                           [(b, u) for b in (1024, 2048, 4096, 8192) for u in (2, 4, 8, 16)]),
+    "layer_K4096_N151936": (151936 * 4096 * 13 // 32, [(b, u) for b in (2048, 8192) for u in (4, 8)]),
+}
+
+
+def eager_us_per_call(fn, ws, xd, y, stream, rounds: int = 3):
+    """Per-call time of back-to-back calls issued from Python (no graph),
+    median of 5 trials of `rounds` passes over the copies: includes the host's
+    launch cost, which bounds it when a launch is short."""
+    import torch
+    per = []
+    with torch.cuda.stream(stream):
+        for w in ws:
+            fn(w, xd, y)
+        torch.cuda.synchronize()
+        for _ in range(TRIALS):
+            with Timer(stream) as t:
+                for _ in range(rounds):
+                    for w in ws:
+                        fn(w, xd, y)
+            per.append(t.ms * 1e3 / (rounds * len(ws)))
+    return round(sorted(per)[len(per) // 2], 3)
 
 
 # -------------------------------------------------------------- cpu baseline
@@ -361,6 +438,21 @@ def cpu_baseline(synth, budget_s=12.0):
                 single_thread=single)
 
 
+def _traffic_file():
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return t if t.get("source_hash") == source_hash() else None
+
+
+def _kernel_args(name: str, family: str):
+    if not (name.startswith(family + "<") and name.endswith(">")):
+        return None
+    return [a.strip() for a in name[len(family) + 1:-1].split(",")]
+
+
 def read_traffic(dot: bool):
     """(kernel name, per-launch HBM bytes) of the M=1 kernel of the measured
     layer from the committed counter file, or (family name, None) when that
@@ -369,24 +461,38 @@ def read_traffic(dot: bool):
     mode, vector-ALU, code bits>; the counter run covers only the 4096 x 4096
     launches."""
     family = "linear_kernel (vector-ALU, M=1)" if dot else "linear_kernel (matrix-core, M=1)"
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+    t = _traffic_file()
+    if t is None:
         return family, None
-    if t.get("source_hash") != source_hash():
-        return family, None
+
     def dense_m1(k):
-        if not (k.startswith("linear_kernel<") and k.endswith(">")):
-            return False
-        args = [a.strip() for a in k[len("linear_kernel<"):-1].split(",")]
-        return (len(args) == 7 and args[0] == "1" and args[3] in ("0", "false")
+        args = _kernel_args(k, "linear_kernel")
+        return (args is not None and len(args) == 7 and args[0] == "1" and args[3] in ("0", "false")
                 and args[5] == ("true" if dot else "false") and args[6] == "3")
     cands = [(v.get("dispatches", 0), k, v) for k, v in t.get("kernels", {}).items() if dense_m1(k)]
     if not cands:
         return family, None
     _, name, v = max(cands)
     return name, v
+
+
+def moe_traffic():
+    """HBM bytes the two grouped products of one plain verify round read, from
+    the committed counter file (None when absent or taken on other sources):
+    the expert passes are one kernel instance (grouping 1) dispatched once for
+    gate/up and once for down per round, so a round reads twice its average."""
+    t = _traffic_file()
+    if t is None:
+        return None
+    cands = []
+    for k, v in t.get("kernels", {}).items():
+        args = _kernel_args(k, "linear_kernel")
+        if args is not None and len(args) == 7 and args[3] == "1" and args[6] == "3" and v.get("read_bytes"):
+            cands.append((v.get("dispatches", 0), k, v))
+    if not cands:
+        return None
+    _, k, v = max(cands)
+    return dict(kernel=k, read_bytes_per_round=2 * v["read_bytes"], dispatches=v.get("dispatches"))
 
 
 # --------------------------------------------------------------------- main
@@ -400,10 +506,13 @@ def main():
     ap.add_argument("--kernel", choices=["auto", "gemv", "mfma"], default="auto")
     ap.add_argument("--no-points", action="store_true", help="skip the per-config points")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling probes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device copy first (scale reference for counter runs)")
     ap.add_argument("--only-vocab", action="store_true",
                     help="time only the K=4096 N=151936 M=64 point (for counter runs of its kernel) and print it")
+    ap.add_argument("--only-moe", action="store_true",
+                    help="time only the plain MoE verify round (for counter runs of the expert passes) and print it")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -414,7 +523,6 @@ def main():
                   file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     import bit_fp8_codebook_amd as q3
     import synth
@@ -431,6 +539,9 @@ def main():
     if args.only_vocab:
         print(json.dumps(linear_point(q3, synth, 151936, 4096, 64, "mfma", reps=args.steps, warmup=args.warmup,
                                       name="K=4096 N=151936 M=64")), flush=True)
+        return
+    if args.only_moe:
+        print(json.dumps(moe_point(q3, synth, reps=args.steps, warmup=args.warmup)), flush=True)
         return
 
     n = k = 4096
@@ -450,6 +561,7 @@ def main():
         if not ok:
             log(f"parity FAILED for {name}: {ratio:.3e}")
             sys.exit(1)
+    log(f"parity of the measured layer: {parity}")
 
     layers = args.layers or copies_for(w0.payload_bytes, minimum=64)
     ws = [w0] + [w0.clone() for _ in range(layers - 1)]
@@ -461,7 +573,7 @@ def main():
     probe = {}
     for name, fn in kernels.items():
         g = capture(lambda fn=fn: [fn(w, xd, y) for w in ws], stream)
-        probe[name] = time_graph(g, stream, 5, 2)
+        probe[name] = time_graph(g, stream, 5, 2, trials=1)[0]
         del g
     chosen = min(probe, key=probe.get) if args.kernel == "auto" else args.kernel
     fn = kernels[chosen]
@@ -479,6 +591,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms_step = t.ms / args.steps
+    # The same graph over 5 further trials of the same length, for the spread.
+    _, spread = time_graph(g, stream, args.steps, 1)
+    del g
+    eager = eager_us_per_call(fn, ws, xd, y, stream)
+    log(f"headline: {ms_step * 1e3 / layers:.3f} us per launch ({chosen}), eager {eager} us per call")
     payload = w0.payload_bytes
     value = layers * payload / (ms_step * 1e-3) / 1e9
     launch_us = ms_step * 1e3 / layers
@@ -487,7 +604,24 @@ def main():
     kname, traffic = read_traffic(dot=(chosen == "gemv"))
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic,
-                    kernel=kname, algorithmic_bytes_per_launch=alg, avg_launch_us=round(launch_us, 3))
+                    kernel=kname, algorithmic_bytes_per_launch=alg, avg_launch_us=round(launch_us, 3),
+                    trials_us_per_launch=[round(v * 1e3 / layers, 3) for v in spread],
+                    eager_us_per_call=eager)
+
+    ceilings = {}
+    if not args.no_ceiling:
+        for cname, (nbytes, cfgs) in CEILING_SWEEPS.items():
+            ceilings[cname] = read_ceiling(nbytes, cfgs, name=cname)
+            log(cname, {k_: v_ for k_, v_ in ceilings[cname].items() if k_ != "sweep_us"})
+        c = ceilings["layer_4096x4096"]
+        roofline["read_ceiling_us_per_launch"] = c["us_per_launch"]
+        roofline["pct_of_read_ceiling"] = round(100 * c["us_per_launch"] / launch_us, 1)
+
+    def with_ceiling(pt, cname):
+        if cname in ceilings:
+            pt["read_ceiling_us"] = ceilings[cname]["us_per_launch"]
+            pt["pct_of_read_ceiling"] = round(100 * ceilings[cname]["us_per_launch"] / pt["us_per_launch"], 1)
+        return pt
 
     points = []
     if not args.no_points:
@@ -496,11 +630,14 @@ def main():
                 points.append(linear_point(q3, synth, 4096, 4096, mm, kn, name=f"4096x4096 M={mm}"))
                 log(points[-1])
         for kn in ("gemv", "mfma"):
-            points.append(linear_point(q3, synth, 28672, 8192, 1, kn, name="K=8192 N=28672 M=1"))
+            points.append(with_ceiling(linear_point(q3, synth, 28672, 8192, 1, kn, name="K=8192 N=28672 M=1"),
+                                       "layer_K8192_N28672"))
             log(points[-1])
-        points.append(linear_point(q3, synth, 28672, 8192, 16, "mfma", name="K=8192 N=28672 M=16"))
+        points.append(with_ceiling(linear_point(q3, synth, 28672, 8192, 16, "mfma", name="K=8192 N=28672 M=16"),
+                                   "layer_K8192_N28672"))
         log(points[-1])
-        points.append(linear_point(q3, synth, 151936, 4096, 64, "mfma", reps=5, name="K=4096 N=151936 M=64"))
+        points.append(with_ceiling(linear_point(q3, synth, 151936, 4096, 64, "mfma", reps=5,
+                                                name="K=4096 N=151936 M=64"), "layer_K4096_N151936"))
         log(points[-1])
         # Verify batches on matrices with few row tiles: one pass, and K split
         # over blocks through a workspace (q3_gemm_small_m_ws).
@@ -543,6 +680,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "kernel_choice_ms_per_step": {k_: round(v_, 4) for k_, v_ in probe.items()},
+        "read_ceilings": ceilings,
         "points": points,
     }
     print(json.dumps(line), flush=True)

@@ -67,12 +67,12 @@ SIGNATURES = {
     "q3_unpack2": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), c_vp, c_vp, c_vp]),
     "q3_head2_scores": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), c_vp, c_i64, c_i64, c_vp, c_i64, c_vp]),
     "q3_shortlist_workspace_bytes": (c_i64, [c_i64]),
-    "q3_shortlist": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
+    "q3_shortlist": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_i32, c_vp, c_i64, c_vp, c_vp, c_vp]),
     "q3_rescore_fp8": (ctypes.c_int, [ctypes.POINTER(Q3Mxfp8Matrix), c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp,
                                       c_vp]),
     "q3_draft_head_workspace_bytes": (c_i64, [c_i64, c_i64]),
     "q3_draft_head": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), ctypes.POINTER(Q3Mxfp8Matrix), c_vp, c_i64, c_i64,
-                                     c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
+                                     c_i32, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp]),
 }
 
 STATUS = {0: "Q3_OK", 1: "Q3_ERR_INVALID_ARG", 2: "Q3_ERR_UNSUPPORTED_SHAPE", 3: "Q3_ERR_MISALIGNED",
@@ -117,6 +117,20 @@ def _ld(t: torch.Tensor) -> int:
     """Row pitch in elements of a 2-D tensor with contiguous rows; a single row's
     pitch is meaningless to torch (it may report 0), so pass the row length."""
     return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def _workspace(t: torch.Tensor, device):
+    """A caller-supplied workspace: a contiguous device tensor on the inputs'
+    device; its size in bytes goes to the library, which checks it."""
+    if not isinstance(t, torch.Tensor) or t.device != torch.device(device):
+        raise ValueError(f"workspace must be a tensor on {device} (the inputs' device)")
+    if not t.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return t
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
 
 
 def _dev(t: torch.Tensor, name: str):
@@ -193,12 +207,27 @@ def _tokens(x: torch.Tensor, w_k: int):
     return x
 
 
-def _out(y, m, n, device):
+def _out(y, m, n, device, name="y"):
+    """A caller-supplied output must be exactly [m][n] float32 with contiguous
+    rows on the inputs' device (its row pitch goes to the library, which writes
+    m rows of n values); None allocates one."""
     if y is None:
-        y = torch.empty((m, n), dtype=torch.float32, device=device)
-    if y.dtype != torch.float32 or y.stride(1) != 1:
-        raise ValueError("y must be float32 with contiguous rows")
+        return torch.empty((m, n), dtype=torch.float32, device=device)
+    _check_out(y, (m, n), torch.float32, device, name)
     return y
+
+
+def _check_out(t, shape, dtype, device, name):
+    if not isinstance(t, torch.Tensor) or t.device != torch.device(device):
+        raise ValueError(f"{name} must be a tensor on {device} (the inputs' device)")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    if len(shape) == 2 and shape[0] > 0 and shape[1] > 0 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have contiguous rows")
+    if len(shape) == 2 and shape[0] > 1 and shape[1] > 0 and t.stride(0) < shape[1]:
+        raise ValueError(f"{name} rows overlap (row pitch below the row length)")
+    if len(shape) == 1 and shape[0] > 1 and t.stride(0) != 1:
+        raise ValueError(f"{name} must be contiguous")
 
 
 def q3_quantize(w: torch.Tensor, codebook: torch.Tensor, codes: torch.Tensor = None, scales: torch.Tensor = None):
@@ -211,8 +240,12 @@ def q3_quantize(w: torch.Tensor, codebook: torch.Tensor, codes: torch.Tensor = N
         raise ValueError("codebook must be contiguous uint8 [n][8]")
     if codes is None:
         codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    else:
+        _check_out(codes, (n, k), torch.uint8, w.device, "codes")
     if scales is None:
         scales = torch.empty((n, k // 32), dtype=torch.uint8, device=w.device)
+    else:
+        _check_out(scales, (n, k // 32), torch.uint8, w.device, "scales")
     _check("q3_quantize", lib().q3_quantize(w.data_ptr(), _ld(w), codebook.data_ptr(), n, k, codes.data_ptr(),
                                             _ld(codes), scales.data_ptr(), _ld(scales), _stream(w)))
     return codes, scales
@@ -255,10 +288,10 @@ def q3_gemm_small_m_ws(w: PackedMatrix, x: torch.Tensor, y: torch.Tensor = None,
         nbytes = q3_gemm_small_m_workspace_bytes(w.n, w.k, m)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
     else:
-        _dev(workspace, "workspace")
+        _workspace(workspace, x.device)
     d = w.desc()
     _check("q3_gemm_small_m_ws", lib().q3_gemm_small_m_ws(ctypes.byref(d), x.data_ptr(), m, _ld(x), y.data_ptr(),
-                                                          _ld(y), workspace.data_ptr(), workspace.numel(),
+                                                          _ld(y), workspace.data_ptr(), _nbytes(workspace),
                                                           _stream(x)))
     return y
 
@@ -270,6 +303,10 @@ def q3_moe_topk(logits: torch.Tensor, topk: int, ids: torch.Tensor = None) -> to
     t, E = logits.shape
     if ids is None:
         ids = torch.empty((t, topk), dtype=torch.int32, device=logits.device)
+    else:
+        _check_out(ids, (t, topk), torch.int32, logits.device, "ids")
+        if not ids.is_contiguous():
+            raise ValueError("ids must be contiguous")
     _check("q3_moe_topk", lib().q3_moe_topk(logits.data_ptr(), t, E, topk, ids.data_ptr(), _stream(logits)))
     return ids
 
@@ -283,8 +320,14 @@ def q3_moe_budget_topk(logits: torch.Tensor, topk: int, budget: int, ids: torch.
     t, E = logits.shape
     if ids is None:
         ids = torch.empty((t, topk), dtype=torch.int32, device=logits.device)
+    else:
+        _check_out(ids, (t, topk), torch.int32, logits.device, "ids")
+        if not ids.is_contiguous():
+            raise ValueError("ids must be contiguous")
     if experts is None:
         experts = torch.empty(budget, dtype=torch.int32, device=logits.device)
+    else:
+        _check_out(experts, (budget,), torch.int32, logits.device, "experts")
     _check("q3_moe_budget_topk", lib().q3_moe_budget_topk(logits.data_ptr(), t, E, topk, budget, ids.data_ptr(),
                                                           experts.data_ptr(), _stream(logits)))
     return ids, experts
@@ -362,11 +405,13 @@ def q3_moe_mlp(gate_up: ExpertStack, down: ExpertStack, x: torch.Tensor, topk_id
         raise ValueError("logits must be fp32 [t][num_experts] with contiguous rows")
     if workspace is None:
         workspace = moe_mlp_workspace(gate_up, down, t, topk, x.device)
-    out = _out(out, t, down.n, x.device)
+    else:
+        _workspace(workspace, x.device)
+    out = _out(out, t, down.n, x.device, "out")
     gd, dd = gate_up.desc(), down.desc()
     _check("q3_moe_mlp", lib().q3_moe_mlp(ctypes.byref(gd), ctypes.byref(dd), x.data_ptr(), _ld(x),
                                           topk_ids.data_ptr(), t, topk, logits.data_ptr(), _ld(logits),
-                                          workspace.data_ptr(), workspace.numel(), out.data_ptr(), _ld(out),
+                                          workspace.data_ptr(), _nbytes(workspace), out.data_ptr(), _ld(out),
                                           _stream(x)))
     return out
 
@@ -453,10 +498,13 @@ def q3_shortlist(scores: torch.Tensor, size: int = 16, workspace: torch.Tensor =
     m, n = scores.shape
     if workspace is None:
         workspace = torch.empty(lib().q3_shortlist_workspace_bytes(m), dtype=torch.uint8, device=scores.device)
+    else:
+        _workspace(workspace, scores.device)
     ids = torch.empty((m, size), dtype=torch.int32, device=scores.device)
     vals = torch.empty((m, size), dtype=torch.float32, device=scores.device)
     _check("q3_shortlist", lib().q3_shortlist(scores.data_ptr(), m, n, _ld(scores), size, workspace.data_ptr(),
-                                              ids.data_ptr(), vals.data_ptr(), _stream(scores)))
+                                              _nbytes(workspace), ids.data_ptr(), vals.data_ptr(),
+                                              _stream(scores)))
     return ids, vals
 
 
@@ -485,11 +533,13 @@ def q3_draft_head(w2: PackedHead2, h: Mxfp8Head, x: torch.Tensor, size: int = 16
     m = x.shape[0]
     if workspace is None:
         workspace = draft_head_workspace(m, w2.n, x.device)
+    else:
+        _workspace(workspace, x.device)
     ids = torch.empty((m, size), dtype=torch.int32, device=x.device)
     y8 = torch.empty((m, size), dtype=torch.float32, device=x.device)
     best = torch.empty(m, dtype=torch.int32, device=x.device)
     d2, d8 = w2.desc(), h.desc()
     _check("q3_draft_head", lib().q3_draft_head(ctypes.byref(d2), ctypes.byref(d8), x.data_ptr(), m, _ld(x),
-                                                size, workspace.data_ptr(), ids.data_ptr(), y8.data_ptr(),
-                                                best.data_ptr(), _stream(x)))
+                                                size, workspace.data_ptr(), _nbytes(workspace), ids.data_ptr(),
+                                                y8.data_ptr(), best.data_ptr(), _stream(x)))
     return ids, y8, best

@@ -373,11 +373,12 @@ Q3_API q3_status q3_head2_scores(const q3_matrix* w2, const uint16_t* x, int64_t
 Q3_API int64_t q3_shortlist_workspace_bytes(int64_t m) { return m < 1 ? 0 : shortlist_ws(m); }
 
 Q3_API q3_status q3_shortlist(const float* scores, int64_t m, int64_t n, int64_t ld, int32_t size, void* workspace,
-                              int32_t* ids, float* vals, void* stream) {
+                              int64_t workspace_bytes, int32_t* ids, float* vals, void* stream) {
   if (!scores || !workspace || !ids) return Q3_ERR_INVALID_ARG;
   if (m < 1 || m > 65535 || n < 1 || n > 0x7FFFFFFF || size < 1 || size > q3::kShortlistMax || size > n)
     return Q3_ERR_UNSUPPORTED_SHAPE;
   if (ld < n) return Q3_ERR_INVALID_ARG;
+  if (workspace_bytes < shortlist_ws(m)) return Q3_ERR_INVALID_ARG;
   if (!aligned(scores, 4) || !aligned(workspace, 8) || !aligned(ids, 4) || !aligned(vals, 4)) return Q3_ERR_MISALIGNED;
   q3_status st = check_device();
   if (st != Q3_OK) return st;
@@ -404,8 +405,8 @@ Q3_API int64_t q3_draft_head_workspace_bytes(int64_t m, int64_t n) {
 }
 
 Q3_API q3_status q3_draft_head(const q3_matrix* w2, const q3_mxfp8_matrix* w8, const uint16_t* x, int64_t m,
-                               int64_t ldx, int32_t size, void* workspace, int32_t* ids, float* y8, int32_t* best,
-                               void* stream) {
+                               int64_t ldx, int32_t size, void* workspace, int64_t workspace_bytes, int32_t* ids,
+                               float* y8, int32_t* best, void* stream) {
   if (!w2) return Q3_ERR_INVALID_ARG;
   q3_status st = check_planes2(w2->n, w2->k, w2->code_plane, w2->scale_plane, w2->codebook);
   if (st != Q3_OK) return st;
@@ -415,6 +416,7 @@ Q3_API q3_status q3_draft_head(const q3_matrix* w2, const q3_mxfp8_matrix* w8, c
   if (size < 1 || size > q3::kShortlistMax || size > w2->n || w2->n > 0x7FFFFFFF) return Q3_ERR_UNSUPPORTED_SHAPE;
   float* scores = static_cast<float*>(workspace);
   if ((st = check_tokens(w2->k, w2->n, x, m, ldx, scores, w2->n, 16)) != Q3_OK) return st;
+  if (workspace_bytes < q3_draft_head_workspace_bytes(m, w2->n)) return Q3_ERR_INVALID_ARG;
   if (!aligned(workspace, 8) || !aligned(ids, 4) || !aligned(y8, 4) || !aligned(best, 4)) return Q3_ERR_MISALIGNED;
   if ((st = check_device()) != Q3_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);

@@ -24,6 +24,13 @@ hipError_t launch_unpack(const PlaneView& w, uint8_t* codes, uint8_t* scales, hi
 hipError_t launch_quantize(const float* w, int64_t ldw, const uint8_t* cb, int64_t n, int64_t k, uint8_t* codes,
                            int64_t ldc, uint8_t* scales, int64_t lds, hipStream_t s);
 
+// Split-K products on matrices with few row tiles (q3_splitk.hip): whether the
+// kernel takes (n, groups, m) on the matrix cores (dot false, m <= 16) or the
+// vector ALUs (dot true, m <= 8), and the launch.
+bool splitk_applies(int64_t n, int groups, int64_t m, bool dot);
+hipError_t launch_splitk(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
+                         bool dot, hipStream_t s);
+
 // VALU path, 1 <= m <= 8.
 hipError_t launch_gemv(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
                        hipStream_t s);

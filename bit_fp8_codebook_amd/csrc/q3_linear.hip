@@ -1178,6 +1178,9 @@ SmallMPlan plan_small_m(int64_t n, int groups, int64_t m) {
 }  // namespace
 
 int64_t gemm_small_m_workspace_bytes(int64_t n, int64_t k, int64_t m) {
+#ifndef Q3_NO_SPLITK
+  if (splitk_applies(n, (int)(k / 32), m, false)) return 0;
+#endif
   const SmallMPlan pl = plan_small_m(n, (int)(k / 32), m);
   return pl.splits > 1 ? (int64_t)pl.splits * m * n * 4 : 0;
 }
@@ -1185,6 +1188,9 @@ int64_t gemm_small_m_workspace_bytes(int64_t n, int64_t k, int64_t m) {
 hipError_t launch_gemm_small_m(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y,
                                int64_t ldy, void* ws, int64_t ws_bytes, hipStream_t s) {
   if (w.n == 0) return hipSuccess;
+#ifndef Q3_NO_SPLITK
+  if (splitk_applies(w.n, w.groups, m, false)) return launch_splitk(w, x, m, ldx, y, ldy, false, s);
+#endif
   KArgs a = base_args(w);
   a.x = x;
   a.ldx = ldx;
@@ -1241,6 +1247,9 @@ hipError_t launch_head2_scores(const PlaneView& w, const uint16_t* x, int64_t m,
 hipError_t launch_gemv(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
                        hipStream_t s) {
   if (w.n == 0) return hipSuccess;
+#ifndef Q3_NO_SPLITK
+  if (splitk_applies(w.n, w.groups, m, true)) return launch_splitk(w, x, m, ldx, y, ldy, true, s);
+#endif
   KArgs a = base_args(w);
   a.x = x;
   a.ldx = ldx;

@@ -1,9 +1,9 @@
 // Router of an MoE verify round over 3.25-bit experts.
 //
 // Hibana: Fast Agentic Inference on Unified-Memory Devices, "Adaptive
-// speculation" / "Expert sharing": a verify round must read each expert chosen
-// by at least one of its drafted tokens, and Hibana gives the round a shared
-// expert budget so it reads fewer.  These kernels pick each token's top-k
+// speculation" / "Expert sharing": checking several drafted tokens in one
+// round costs the weights of every expert any of them routes to, and a budget
+// of experts shared by the whole round caps that set.  These kernels pick each token's top-k
 // experts on the device, without or with a budget; the expert-grouped product
 // (q3_linear.hip) then reads each picked expert once, without the list of
 // picked experts ever coming back to the host.

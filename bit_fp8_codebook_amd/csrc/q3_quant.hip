@@ -124,7 +124,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
       float t[7];
 #pragma unroll
       for (int p = 0; p < 7; ++p) {
-        const float m = ldexpf(sm[p], s - 127);   // exact: at most 6 significant bits, >= 2^-136
+        // Exact: sm[p] (the sum of two E4M3 values) has at most 18 significant
+        // bits, none below 2^-9, so the scaled midpoint keeps every bit: its
+        // lowest stays at or above 2^-136 (fp32 subnormals reach 2^-149) and,
+        // with |w| <= 2^64 bounding s, its magnitude below 2^84.
+        const float m = ldexpf(sm[p], s - 127);
         t[p] = (upper >> p) & 1u ? below(m) : m;
       }
       const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};

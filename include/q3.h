@@ -238,7 +238,7 @@ Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t
  * x bf16 [t][ldx]; logits fp32 [t][ld_logits] (the router's, e.g. the input of
  * q3_moe_topk or q3_moe_budget_topk); out fp32 [t][ldo].  Ids outside
  * [0, num_experts) are skipped (weight 0, excluded from the softmax); a token
- * with none in range gets 0, and a round with none in range writes nothing.
+ * with none in range gets a row of zeros (every row of out is written).
  * Three launches (gate/up with the SwiGLU, down, combine), no host
  * synchronisation; only experts that appear in topk_ids are read, each once
  * per matrix.  Deterministic: the combine adds slots in slot order.
@@ -254,9 +254,10 @@ Q3_API q3_status q3_moe_mlp(const q3_expert_stack* gate_up, const q3_expert_stac
                             void* stream);
 
 /* ---- Two-bit draft head ------------------------------------------------------
- * (Hibana page, "Model surgery" / "Two-bit draft head": the drafter's output
- * head scores every vocabulary token; a 2-bit copy of it shortlists candidates
- * and the FP8 head rescores only those and decides.)  Readings of the page:
+ * (Hibana page, "Model surgery" / "Two-bit draft head": the drafter's
+ * vocabulary projection is first evaluated on a 2-bit copy to pick a handful
+ * of candidate tokens, and only those candidates are evaluated again with the
+ * FP8 weights, which make the choice.)  Readings of the page:
  *   2-bit copy : 2-bit codes into a 4-entry E4M3FN codebook per row and one
  *                E8M0 scale per group of 32, 2 + 8/32 = 2.25 bits per weight:
  *                  w2[n][k] = E4M3FN(cb4[n][code]) * 2^(scale[n][k/32] - 127).
@@ -304,10 +305,12 @@ Q3_API int64_t q3_shortlist_workspace_bytes(int64_t m);
  * larger first, equal scores to the lower row: ids int32 [m][size] and, if
  * vals is not NULL, their scores fp32 [m][size].  1 <= size <= 16,
  * size <= n, 1 <= m <= 65535; scores fp32 [m][ld], finite (not checked);
- * workspace: q3_shortlist_workspace_bytes(m) bytes of device memory, 8-byte
- * aligned, owned by the caller (its contents are scratch).  Two launches. */
+ * workspace: device memory of workspace_bytes bytes, at least
+ * q3_shortlist_workspace_bytes(m) (Q3_ERR_INVALID_ARG otherwise), 8-byte
+ * aligned, owned by the caller (its contents are scratch; calls that overlap
+ * in time must not share it).  Two launches. */
 Q3_API q3_status q3_shortlist(const float* scores, int64_t m, int64_t n, int64_t ld, int32_t size,
-                              void* workspace, int32_t* ids, float* vals, void* stream);
+                              void* workspace, int64_t workspace_bytes, int32_t* ids, float* vals, void* stream);
 
 /* FP8 rescoring of listed rows: y[i][j] = x[i] . w8[ids[i][j]] (fp32 [m][size])
  * and best[i] = the listed row with the largest y[i][.] (equal: lower row).
@@ -318,14 +321,16 @@ Q3_API q3_status q3_rescore_fp8(const q3_mxfp8_matrix* w8, const uint16_t* x, in
 
 /* The whole draft-head decision for 1 <= m <= 16 queries: 2-bit scores of all
  * rows, shortlist of `size`, FP8 rescoring and the decision, in four launches.
- * w2 and w8 must have the same n and k.  workspace:
- * q3_draft_head_workspace_bytes(m, n) bytes (8-byte aligned; the 2-bit scores
- * [m][n] then the shortlist scratch).  Outputs: ids [m][size] (the list),
- * y8 [m][size] (FP8 scores), best [m]. */
+ * w2 and w8 must have the same n and k.  workspace: device memory of
+ * workspace_bytes bytes, at least q3_draft_head_workspace_bytes(m, n)
+ * (Q3_ERR_INVALID_ARG otherwise), 8-byte aligned, any contents (the 2-bit
+ * scores [m][n] then the shortlist scratch; calls that overlap in time must
+ * not share it).  Outputs: ids [m][size] (the list), y8 [m][size] (FP8
+ * scores), best [m]. */
 Q3_API int64_t q3_draft_head_workspace_bytes(int64_t m, int64_t n);
 Q3_API q3_status q3_draft_head(const q3_matrix* w2, const q3_mxfp8_matrix* w8, const uint16_t* x, int64_t m,
-                               int64_t ldx, int32_t size, void* workspace, int32_t* ids, float* y8,
-                               int32_t* best, void* stream);
+                               int64_t ldx, int32_t size, void* workspace, int64_t workspace_bytes, int32_t* ids,
+                               float* y8, int32_t* best, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,4 +1,4 @@
-"""CPU oracle for the two-bit draft head: shortlist in 2 bits, decide in FP8.
+"""CPU oracle for the two-bit draft head: candidates picked on a 2-bit copy, the choice made on FP8 weights.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this module.  It shares no code with the GPU path
@@ -6,10 +6,10 @@ and imports nothing from it; numbers are decoded with the (pinned) helpers of
 the 3-bit oracle next to it.
 
 What it computes (Hibana: Fast Agentic Inference on Unified-Memory Devices --
-"Model surgery", subsection "Two-bit draft head"): the drafter's output head
-scores every vocabulary token; a 2-bit copy of that head is read to pick a
-short list of candidates, and only those candidates are scored again with the
-FP8 head, which makes the decision:
+"Model surgery", subsection "Two-bit draft head"): the drafter's vocabulary
+projection is evaluated on a 2-bit copy to pick a short list of candidate
+tokens, and only those candidates are evaluated again with the FP8 weights,
+which make the choice:
 
     s2[m][n] = sum_k x[m][k] * w2[n][k]                 (all n, 2-bit head)
     L[m]     = the S rows with the largest s2[m][.]     (S = 16 on the page)

@@ -123,19 +123,29 @@ def test_head_validation_rejects_before_any_hip_call(q3lib):
     mis = _lib.Q3Matrix(16, 64, fake, fake, fake + 2)                                    # codebook not 4-aligned
     assert q3lib.q3_head2_scores(ctypes.byref(mis), fake, 1, 64, fake, 16, None) == 3
     assert q3lib.q3_pack2(fake, 63, fake, 2, 16, 64, fake, fake, None) == 1
-    assert q3lib.q3_shortlist(fake, 1, 100, 100, 17, fake, fake, None, None) == 2         # size > 16
-    assert q3lib.q3_shortlist(fake, 1, 10, 10, 11, fake, fake, None, None) == 2           # size > n
-    assert q3lib.q3_shortlist(fake, 1, 100, 99, 16, fake, fake, None, None) == 1          # ld < n
-    assert q3lib.q3_shortlist(fake, 1, 100, 100, 16, fake + 4, fake, None, None) == 3     # workspace 8-aligned
-    assert q3lib.q3_shortlist(None, 1, 100, 100, 16, fake, fake, None, None) == 1
+    sw = q3lib.q3_shortlist_workspace_bytes(1)
+    assert q3lib.q3_shortlist(fake, 1, 100, 100, 17, fake, sw, fake, None, None) == 2         # size > 16
+    assert q3lib.q3_shortlist(fake, 1, 10, 10, 11, fake, sw, fake, None, None) == 2           # size > n
+    assert q3lib.q3_shortlist(fake, 1, 100, 99, 16, fake, sw, fake, None, None) == 1          # ld < n
+    assert q3lib.q3_shortlist(fake, 1, 100, 100, 16, fake + 4, sw, fake, None, None) == 3     # workspace 8-aligned
+    assert q3lib.q3_shortlist(None, 1, 100, 100, 16, fake, sw, fake, None, None) == 1
+    assert q3lib.q3_shortlist(fake, 1, 100, 100, 16, fake, sw - 8, fake, None, None) == 1     # workspace too small
+    assert q3lib.q3_shortlist(fake, 2, 100, 100, 16, fake, sw, fake, None, None) == 1         # sized for 1 query
     h8 = _lib.Q3Mxfp8Matrix(16, 64, fake, 64, fake, 2)
     assert q3lib.q3_rescore_fp8(ctypes.byref(h8), fake, 1, 64, fake, 17, fake, fake, None) == 2
     h8.ld_elements = 72                                                                    # not a multiple of 16
     assert q3lib.q3_rescore_fp8(ctypes.byref(h8), fake, 1, 64, fake, 16, fake, fake, None) == 3
     h8.ld_elements = 48                                                                    # < k
     assert q3lib.q3_rescore_fp8(ctypes.byref(h8), fake, 1, 64, fake, 16, fake, fake, None) == 1
+    dw = q3lib.q3_draft_head_workspace_bytes(1, 16)
     h8 = _lib.Q3Mxfp8Matrix(16, 96, fake, 96, fake, 3)                                     # k differs from w2's
-    assert q3lib.q3_draft_head(ctypes.byref(w2), ctypes.byref(h8), fake, 1, 96, 16, fake, fake, fake, fake, None) == 1
+    assert q3lib.q3_draft_head(ctypes.byref(w2), ctypes.byref(h8), fake, 1, 96, 16, fake, dw, fake, fake, fake,
+                               None) == 1
+    h8 = _lib.Q3Mxfp8Matrix(16, 64, fake, 64, fake, 2)
+    assert q3lib.q3_draft_head(ctypes.byref(w2), ctypes.byref(h8), fake, 1, 64, 16, fake, dw - 8, fake, fake, fake,
+                               None) == 1                                                    # workspace too small
+    assert q3lib.q3_draft_head(ctypes.byref(w2), ctypes.byref(h8), fake, 2, 64, 16, fake, dw, fake, fake, fake,
+                               None) == 1                                                    # sized for 1 query
 
 
 def test_status_strings(q3lib):
@@ -212,3 +222,31 @@ def test_validation_rejects_before_any_hip_call(q3lib):
     assert mlp(gu, dn) == 2                                                         # down k != I
     dn.k, dn.num_experts = 32, 3
     assert mlp(gu, dn) == 1                                                         # expert counts differ
+
+
+def test_binding_rejects_outputs_of_the_wrong_shape():
+    # A caller-supplied output goes to the library as a pointer and a row pitch,
+    # so the binding must see exactly the shape the call writes: a y with fewer
+    # rows than tokens would be written past its end.
+    import torch
+    from bit_fp8_codebook_amd import _lib
+    ok = torch.empty((3, 10), dtype=torch.float32)
+    assert _lib._out(ok, 3, 10, "cpu") is ok
+    assert _lib._out(torch.empty((8, 12), dtype=torch.float32)[:3, :10], 3, 10, "cpu") is not None  # strided rows
+    for bad in (torch.empty((2, 10), dtype=torch.float32),          # short: 2 rows for 3 tokens
+                torch.empty((3, 9), dtype=torch.float32),           # narrow
+                torch.empty((3, 10), dtype=torch.float64),          # wrong type
+                torch.empty((10, 3), dtype=torch.float32).t(),      # columns not contiguous
+                torch.empty((30,), dtype=torch.float32)):           # flat
+        with pytest.raises(ValueError):
+            _lib._out(bad, 3, 10, "cpu")
+    with pytest.raises(ValueError):
+        _lib._check_out(torch.empty((4, 7), dtype=torch.int32), (4, 8), torch.int32, "cpu", "ids")
+    with pytest.raises(ValueError):
+        _lib._check_out(torch.empty(15, dtype=torch.int32), (16,), torch.int32, "cpu", "experts")
+    with pytest.raises(ValueError):
+        _lib._check_out(torch.empty((4, 64), dtype=torch.uint8), (4, 2), torch.uint8, "cpu", "scales")
+    with pytest.raises(ValueError):
+        _lib._workspace(torch.empty((4, 8), dtype=torch.uint8)[:, :4], "cpu")        # not contiguous
+    assert _lib._nbytes(torch.empty(10, dtype=torch.float32)) == 40
+

@@ -63,3 +63,35 @@ def test_traffic_from_other_sources_is_not_reported(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", os.path.join(str(tmp_path), "missing.json"))
     assert bench.read_traffic(False) == ("linear_kernel (matrix-core, M=1)", None)
 
+
+
+def test_union_traffic_is_twice_the_expert_pass_average(tmp_path, monkeypatch):
+    # Gate/up and down are one kernel instance (grouping 1), one dispatch each per round.
+    k = {n: v for n, v in KERNELS.items() if ", 1, 0, false, 3>" not in n}
+    k["linear_kernel<1, 1, 4, 1, 0, false, 3>"] = {"read_bytes": 41_000_000, "write_bytes": 10, "dispatches": 40}
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", _write_traffic(tmp_path, bench.source_hash(), k))
+    t = bench.moe_traffic()
+    assert t["read_bytes_per_round"] == 82_000_000 and t["kernel"] == "linear_kernel<1, 1, 4, 1, 0, false, 3>"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", _write_traffic(tmp_path, "1" * 16, k))
+    assert bench.moe_traffic() is None
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i, (kern, val) in enumerate(rows):
+            f.write(f'{i},"{kern}",{counter},{val}\n')
+    return str(path)
+
+
+def test_counter_files_are_scaled_by_the_calibration_copy(tmp_path):
+    import bench_traffic
+    kern = "void q3::(anonymous namespace)::linear_kernel<1, 1, 4, 0, 0, true, 3>(q3::KArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    # The counter sees half of the copy's 256 MiB read and all of its write.
+    f = _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [(copy, 128 * 1024), (copy, 10), (kern, 3000), (kern, 3200)])
+    w = _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [(copy, 256 * 1024), (kern, 16)])
+    out = bench_traffic.merge([(f, w)])
+    v = out["kernels"]["linear_kernel<1, 1, 4, 0, 0, true, 3>"]
+    assert v["read_bytes"] == 2 * 3100 * 1024 and v["write_bytes"] == 16 * 1024 and v["dispatches"] == 2
+    assert out["source_hash"] == bench.source_hash()

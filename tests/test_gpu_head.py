@@ -185,10 +185,11 @@ def test_draft_head_end_to_end(q3, n, k, m):
     check_decision(ids, y8, best, y_all, b_all)
 
 
-def test_draft_head_full_size_sampled(q3):
-    """Vocabulary-sized head (K=4096, N=151936), one query: 2-bit scores on
-    sampled rows, the list consistent with the GPU's scores, FP8 scores of the
-    listed rows and the decision."""
+def test_draft_head_full_size(q3):
+    """Vocabulary-sized head (K=4096, N=151936), one query: the 2-bit scores of
+    every row against the oracle's fp64 scores, the list valid against those
+    fp64 scores on every row (and exactly the ranking of the GPU's own scores),
+    FP8 scores of the listed rows and the decision."""
     n, k = 151936, 4096
     head, x = synth.make_head(n, k, 1, seed=0)
     w2, h8 = pack_head(q3, head)
@@ -196,11 +197,10 @@ def test_draft_head_full_size_sampled(q3):
     ids, y8, best = q3.q3_draft_head(w2, h8, xd, 16)
     ids, y8, best = ids.cpu().numpy(), y8.cpu().numpy(), best.cpu().numpy()
     s2 = q3.q3_head2_scores(w2, xd).cpu().numpy()
-    assert np.array_equal(ids, ranked(s2, 16))
-    rows = np.sort(np.concatenate([np.random.default_rng(1).choice(n, 200, replace=False), [0, n - 1]]))
-    cp, sp = oracle.pack2(head.codes[rows], head.scales[rows])
-    s_ref, bound = oracle.linear2(cp, sp, head.codebook[rows], len(rows), k, x)
-    assert_close(s2[:, rows], s_ref, bound, "full-size 2-bit scores")
+    cp, sp = oracle.pack2(head.codes, head.scales)
+    s64, b64 = oracle.linear2(cp, sp, head.codebook, n, k, x)
+    assert_close(s2, s64, b64, "full-size 2-bit scores")
+    check_list_valid(ids, s2, s64, b64)
     y_all, b_all = oracle_rescore_all(head, x)
     assert_close(y8, y_all[:, ids[0]], b_all[:, ids[0]], "full-size rescore")
     check_decision(ids, y8, best, y_all, b_all)

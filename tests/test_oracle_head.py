@@ -1,4 +1,4 @@
-"""Pins of the two-bit draft-head oracle (shortlist in 2 bits, decide in FP8)
+"""Pins of the two-bit draft-head oracle (a 2-bit candidate list, the choice on FP8 weights)
 against facts fixed independently of its own code: the 2.25 bits/weight
 count, hand-derived words and offsets, torch's FP8/bf16 decoders and fp64
 matmul, exact rational brute force, and brute-force ranking."""
