@@ -62,6 +62,9 @@ SIGNATURES = {
     "q3_moe_mlp_workspace_bytes": (c_i64, [c_i64, c_i64, c_i32, c_i32]),
     "q3_moe_mlp": (ctypes.c_int, [ctypes.POINTER(Q3ExpertStack), ctypes.POINTER(Q3ExpertStack), c_vp, c_i64, c_vp,
                                   c_i32, c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
+    "q3_moe_mlp_noalloc_max_bytes": (c_i64, []),
+    "q3_moe_mlp_noalloc": (ctypes.c_int, [ctypes.POINTER(Q3ExpertStack), ctypes.POINTER(Q3ExpertStack), c_vp, c_i64,
+                                          c_vp, c_i32, c_i32, c_vp, c_i64, c_vp, c_i64, c_vp]),
     "q3_layout2": (ctypes.c_int, [c_i64, c_i64, ctypes.POINTER(Q3LayoutInfo)]),
     "q3_pack2": (ctypes.c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp]),
     "q3_unpack2": (ctypes.c_int, [ctypes.POINTER(Q3Matrix), c_vp, c_vp, c_vp]),
@@ -414,6 +417,30 @@ def q3_moe_mlp(gate_up: ExpertStack, down: ExpertStack, x: torch.Tensor, topk_id
                                           workspace.data_ptr(), _nbytes(workspace), out.data_ptr(), _ld(out),
                                           _stream(x)))
     return out
+
+
+def q3_moe_mlp_noalloc(gate_up: ExpertStack, down: ExpertStack, x: torch.Tensor, topk_ids: torch.Tensor,
+                       logits: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
+    """q3_moe_mlp with the library's own scratch memory instead of a workspace
+    (for callers that cannot allocate; calls that overlap on one GPU race)."""
+    _dev(x, "x"), _dev(topk_ids, "topk_ids"), _dev(logits, "logits")
+    t, topk = topk_ids.shape
+    if topk_ids.dtype != torch.int32 or not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be contiguous int32 [t][topk]")
+    if x.dim() != 2 or x.shape[1] != gate_up.k or x.stride(1) != 1 or x.shape[0] < t:
+        raise ValueError("x must be [t][k] with contiguous rows")
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1 or logits.shape[0] < t:
+        raise ValueError("logits must be fp32 [t][num_experts] with contiguous rows")
+    out = _out(out, t, down.n, x.device, "out")
+    gd, dd = gate_up.desc(), down.desc()
+    _check("q3_moe_mlp_noalloc", lib().q3_moe_mlp_noalloc(ctypes.byref(gd), ctypes.byref(dd), x.data_ptr(), _ld(x),
+                                                          topk_ids.data_ptr(), t, topk, logits.data_ptr(),
+                                                          _ld(logits), out.data_ptr(), _ld(out), _stream(x)))
+    return out
+
+
+def q3_moe_mlp_noalloc_max_bytes() -> int:
+    return lib().q3_moe_mlp_noalloc_max_bytes()
 
 
 # ------------------------------------------------------- two-bit draft head

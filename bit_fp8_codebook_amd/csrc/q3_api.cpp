@@ -319,6 +319,33 @@ Q3_API q3_status q3_moe_mlp(const q3_expert_stack* gate_up, const q3_expert_stac
                                      h, part, mlp_ldp(down->n), out, ldo, static_cast<hipStream_t>(stream)));
 }
 
+Q3_API int64_t q3_moe_mlp_noalloc_max_bytes(void) { return q3::kScratchBytes; }
+
+Q3_API q3_status q3_moe_mlp_noalloc(const q3_expert_stack* gate_up, const q3_expert_stack* down, const uint16_t* x,
+                                    int64_t ldx, const int32_t* topk_ids, int32_t t, int32_t topk,
+                                    const float* logits, int64_t ld_logits, float* out, int64_t ldo, void* stream) {
+  q3_status st = check_stack(gate_up);
+  if (st != Q3_OK) return st;
+  if ((st = check_stack(down)) != Q3_OK) return st;
+  if (gate_up->num_experts != down->num_experts) return Q3_ERR_INVALID_ARG;
+  if (gate_up->n % 64 || down->k != gate_up->n / 2) return Q3_ERR_UNSUPPORTED_SHAPE;
+  if (!x || !topk_ids || !logits || !out) return Q3_ERR_INVALID_ARG;
+  if (t < 1 || topk < 1 || int64_t(t) * topk > 64) return Q3_ERR_UNSUPPORTED_SHAPE;
+  if (ldx < gate_up->k || ldo < down->n || ld_logits < gate_up->num_experts) return Q3_ERR_INVALID_ARG;
+  if (q3_moe_mlp_workspace_bytes(gate_up->n, down->n, t, topk) > q3::kScratchBytes) return Q3_ERR_UNSUPPORTED_SHAPE;
+  if (ldx % 8 || !aligned(x, 16) || !aligned(out, 4) || !aligned(topk_ids, 4) || !aligned(logits, 4))
+    return Q3_ERR_MISALIGNED;
+  if ((st = check_device()) != Q3_OK) return st;
+  void* scratch = nullptr;
+  if (q3::scratch_address(&scratch) != hipSuccess) return Q3_ERR_HIP;
+  const int64_t pairs = int64_t(t) * topk;
+  uint8_t* ws = static_cast<uint8_t*>(scratch);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws);
+  float* part = reinterpret_cast<float*>(ws + mlp_h_bytes(pairs, gate_up->n / 2));
+  return from_hip(q3::launch_moe_mlp(view_of(gate_up), view_of(down), x, ldx, topk_ids, t, topk, logits, ld_logits,
+                                     h, part, mlp_ldp(down->n), out, ldo, static_cast<hipStream_t>(stream)));
+}
+
 Q3_API q3_status q3_layout2(int64_t n, int64_t k, q3_layout_info* out) {
   if (!out) return Q3_ERR_INVALID_ARG;
   q3_status st = check_shape(n, k);

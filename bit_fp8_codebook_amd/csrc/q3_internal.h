@@ -90,6 +90,11 @@ hipError_t launch_moe_combine(const float* part, int64_t ldp, const int32_t* ids
                               int32_t num_experts, const float* logits, int64_t ld_logits, int64_t n, float* out,
                               int64_t ldo, hipStream_t s);
 
+// Library-owned scratch (q3_noalloc.hip): kScratchBytes of device memory per
+// GPU; scratch_address gives this device's copy (looked up once per device).
+constexpr int64_t kScratchBytes = int64_t(4) << 20;
+hipError_t scratch_address(void** out);
+
 // Fused expert MLP of a verify round, three launches: gate/up with SwiGLU into
 // h (bf16 [2*pairs][I], high and low term per pair), down into part (fp32
 // [pairs][ldp]), then the combine.

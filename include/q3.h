@@ -253,6 +253,27 @@ Q3_API q3_status q3_moe_mlp(const q3_expert_stack* gate_up, const q3_expert_stac
                             int64_t ld_logits, void* workspace, int64_t workspace_bytes, float* out, int64_t ldo,
                             void* stream);
 
+/* q3_moe_mlp without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): h and the per-pair outputs live in scratch memory the
+ * library owns, q3_moe_mlp_noalloc_max_bytes() bytes per GPU (4 MiB, allocated
+ * with the library's code object on each GPU it runs on and held until the
+ * process ends).  The call allocates and frees nothing.  Same arguments,
+ * results and errors as q3_moe_mlp without workspace / workspace_bytes, and
+ * bitwise the same outputs; a round whose q3_moe_mlp_workspace_bytes(...)
+ * exceeds the scratch size is rejected with Q3_ERR_UNSUPPORTED_SHAPE before
+ * any launch (e.g. 64 pairs allow I + ceil(n_down/4)*4 <= 16384).  Every call
+ * on one GPU uses that GPU's one scratch array: calls that overlap in time on
+ * the same GPU (different streams, or different host threads without
+ * ordering) race and must not be issued; calls in one stream's order are
+ * safe.  The scratch keeps the last call's contents; nothing in it needs to
+ * start at zero. */
+Q3_API int64_t q3_moe_mlp_noalloc_max_bytes(void);
+Q3_API q3_status q3_moe_mlp_noalloc(const q3_expert_stack* gate_up, const q3_expert_stack* down,
+                                    const uint16_t* x, int64_t ldx, const int32_t* topk_ids, int32_t t,
+                                    int32_t topk, const float* logits, int64_t ld_logits, float* out,
+                                    int64_t ldo, void* stream);
+
 /* ---- Two-bit draft head ------------------------------------------------------
  * (Hibana page, "Model surgery" / "Two-bit draft head": the drafter's
  * vocabulary projection is first evaluated on a 2-bit copy to pick a handful

@@ -35,6 +35,7 @@ def test_header_declares_the_entry_points():
                                          "q3_shortlist_workspace_bytes", "q3_shortlist", "q3_rescore_fp8",
                                          "q3_draft_head_workspace_bytes", "q3_draft_head", "q3_moe_budget_topk",
                                          "q3_moe_mlp_workspace_bytes", "q3_moe_mlp", "q3_quantize",
+                                         "q3_moe_mlp_noalloc", "q3_moe_mlp_noalloc_max_bytes",
                                          "q3_gemm_small_m_workspace_bytes", "q3_gemm_small_m_ws"])
 
 
@@ -250,3 +251,22 @@ def test_binding_rejects_outputs_of_the_wrong_shape():
         _lib._workspace(torch.empty((4, 8), dtype=torch.uint8)[:, :4], "cpu")        # not contiguous
     assert _lib._nbytes(torch.empty(10, dtype=torch.float32)) == 40
 
+
+def test_noalloc_mlp_validation(q3lib):
+    # The library's scratch holds 4 MiB per GPU; rounds whose intermediate
+    # buffers need more are rejected on the host, before any HIP call.
+    from bit_fp8_codebook_amd import _lib
+    assert q3lib.q3_moe_mlp_noalloc_max_bytes() == 4 << 20
+    fake = 0x1000
+    # 64 pairs need 256 * (I + ceil(n_down / 4) * 4) bytes: I = 8192 with n_down = 8192 fits exactly.
+    gu = _lib.Q3ExpertStack(4, 2 * 8192, 64, fake, 1 << 30, fake, 1 << 26, fake, 1 << 20)
+    dn = _lib.Q3ExpertStack(4, 8192, 8192, fake, 1 << 30, fake, 1 << 26, fake, 1 << 20)
+    assert q3lib.q3_moe_mlp_workspace_bytes(2 * 8192, 8192, 8, 8) == 4 << 20
+    call = lambda g, d, t=8, topk=8, logits=fake: q3lib.q3_moe_mlp_noalloc(
+        ctypes.byref(g), ctypes.byref(d), fake, 64, fake, t, topk, logits, 4, fake, 8200, None)
+    assert call(gu, dn, logits=None) == 1
+    assert call(gu, dn, t=9) == 2                                                   # 72 pairs
+    dn.n = 8193                                                                      # one more output row
+    assert call(gu, dn) == 2                                                        # exceeds the scratch
+    dn.n, dn.k = 8192, 4096
+    assert call(gu, dn) == 2                                                        # down k != I
