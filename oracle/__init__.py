@@ -10,3 +10,4 @@ from .q3_oracle import (E4M3FN_TABLE, bf16_decode, dequantize, e4m3fn_decode, e8
 from .q2_head import (decide, dequantize2, layout2, linear2, mxfp8_dequantize, pack2, pack_group2,  # noqa: F401
                       rescore, shortlist, unpack2, unpack_group2, word_offset2)
 from .q3_quant import choose_scales, codebook_values, quantize, snap  # noqa: F401,E402
+from .q3_fit import fit_codebook, fit_row, grid_values, group_exponents, lloyd, round_e4m3fn  # noqa: F401,E402
