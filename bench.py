@@ -21,7 +21,8 @@ The same line carries:
                 (K=8192, N=28672), M = 64 (K=4096, N=151936), the
                 expert-grouped MoE verify round and the two-bit draft head
                 (2-bit shortlist of 16 over N=151936, MXFP8 rescore), each on
-                cold rotating copies.
+                cold rotating copies; the quantizer and the per-row codebook
+                fit on the K=8192 N=28672 matrix.
 
 Inputs are synthetic and seeded (codes uniform 0..7, per-row codebooks of
 N(0,1) draws rounded to E4M3, power-of-two group scales 2^-10..2^-4, bf16
@@ -288,6 +289,36 @@ def quantize_point(q3, synth, n=28672, k=8192, reps=10, warmup=2):
               algorithmic_bytes=alg, GBps=round(alg / us / 1e3, 1),
               pct_of_8TBps=round(100 * alg / us / 1e3 / HBM_PEAK_GBPS, 1), kernel="quantize_kernel")
     del w, codes, scales, cb
+    torch.cuda.empty_cache()
+    return pt
+
+
+def fit_point(q3, n=28672, k=8192, reps=5, warmup=1):
+    """Per-row codebook fitting on the K=8192 N=28672 matrix: fp32 weights
+    (N(0,1) drawn on the GPU from a fixed seed) -> one 8-entry E4M3FN codebook
+    per row, one launch.  Algorithmic bytes: 4 per weight read, 8 per row written."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    w = torch.randn((n, k), generator=gen, device="cuda", dtype=torch.float32)
+    cb = torch.empty((n, 8), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    per = []
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            q3.q3_fit_codebook(w, cb)
+        stream.synchronize()
+        for _ in range(TRIALS):
+            with Timer(stream) as t:
+                for _ in range(reps):
+                    q3.q3_fit_codebook(w, cb)
+            per.append(t.ms * 1e3 / reps)
+    us = sorted(per)[len(per) // 2]
+    alg = n * k * 4 + n * 8
+    pt = dict(name=f"codebook fit K={k} N={n} (fp32 -> per-row E4M3FN codebooks)", n=n, k=k,
+              us_per_launch=round(us, 1), trials_us=[round(v, 1) for v in per], algorithmic_bytes=alg,
+              GBps=round(alg / us / 1e3, 1), pct_of_8TBps=round(100 * alg / us / 1e3 / HBM_PEAK_GBPS, 1),
+              rows_per_s=round(n / (us * 1e-6), 1), kernel="fit_kernel")
+    del w, cb
     torch.cuda.empty_cache()
     return pt
 
@@ -652,6 +683,8 @@ def main():
         points.append(draft_head_point(q3, synth))
         log(points[-1])
         points.append(quantize_point(q3, synth))
+        log(points[-1])
+        points.append(fit_point(q3))
         log(points[-1])
         points.append(linear_point(q3, synth, 1024, 1024, 1, chosen, name="1024x1024 M=1"))
         log(points[-1])

@@ -58,6 +58,7 @@ SIGNATURES = {
     "q3_grouped_expert_gemv": (ctypes.c_int, [ctypes.POINTER(Q3ExpertStack), c_vp, c_i64, c_i32, c_vp, c_i32,
                                               c_i32, c_vp, c_i64, c_vp]),
     "q3_quantize": (ctypes.c_int, [c_vp, c_i64, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
+    "q3_fit_codebook": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
     "q3_moe_budget_topk": (ctypes.c_int, [c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "q3_moe_mlp_workspace_bytes": (c_i64, [c_i64, c_i64, c_i32, c_i32]),
     "q3_moe_mlp": (ctypes.c_int, [ctypes.POINTER(Q3ExpertStack), ctypes.POINTER(Q3ExpertStack), c_vp, c_i64, c_vp,
@@ -252,6 +253,22 @@ def q3_quantize(w: torch.Tensor, codebook: torch.Tensor, codes: torch.Tensor = N
     _check("q3_quantize", lib().q3_quantize(w.data_ptr(), _ld(w), codebook.data_ptr(), n, k, codes.data_ptr(),
                                             _ld(codes), scales.data_ptr(), _ld(scales), _stream(w)))
     return codes, scales
+
+
+def q3_fit_codebook(w: torch.Tensor, codebook: torch.Tensor = None) -> torch.Tensor:
+    """fp32 weights [n][k] -> fitted per-row codebooks uint8 [n][8] (E4M3FN, ascending)."""
+    _dev(w, "w")
+    if w.dtype != torch.float32 or w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be float32 [n][k] with contiguous rows")
+    n, k = w.shape
+    if codebook is None:
+        codebook = torch.empty((n, 8), dtype=torch.uint8, device=w.device)
+    else:
+        _check_out(codebook, (n, 8), torch.uint8, w.device, "codebook")
+        if not codebook.is_contiguous():
+            raise ValueError("codebook must be contiguous")
+    _check("q3_fit_codebook", lib().q3_fit_codebook(w.data_ptr(), _ld(w), n, k, codebook.data_ptr(), _stream(w)))
+    return codebook
 
 
 def q3_gemv(w: PackedMatrix, x: torch.Tensor, y: torch.Tensor = None) -> torch.Tensor:

@@ -176,6 +176,18 @@ Q3_API q3_status q3_quantize(const float* w, int64_t ldw, const uint8_t* codeboo
                                       static_cast<hipStream_t>(stream)));
 }
 
+Q3_API q3_status q3_fit_codebook(const float* w, int64_t ldw, int64_t n, int64_t k, uint8_t* codebook,
+                                 void* stream) {
+  q3_status st = check_shape(n, k);
+  if (st != Q3_OK) return st;
+  if (k > (int64_t(1) << 18) || n > 0x7FFFFFFF) return Q3_ERR_UNSUPPORTED_SHAPE;
+  if (n > 0 && (!w || !codebook)) return Q3_ERR_INVALID_ARG;
+  if (ldw < k) return Q3_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || ldw % 4 || !aligned(codebook, 8)) return Q3_ERR_MISALIGNED;
+  if ((st = check_device()) != Q3_OK) return st;
+  return from_hip(q3::launch_fit_codebook(w, ldw, n, k, codebook, static_cast<hipStream_t>(stream)));
+}
+
 Q3_API q3_status q3_gemv(const q3_matrix* w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
                          void* stream) {
   q3_status st = check_matrix(w);

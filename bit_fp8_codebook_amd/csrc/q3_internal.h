@@ -31,6 +31,10 @@ bool splitk_applies(int64_t n, int groups, int64_t m, bool dot);
 hipError_t launch_splitk(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
                          bool dot, hipStream_t s);
 
+// Codebook fitting: the 8 E4M3FN entries of each row's codebook from its fp32
+// weights (q3_fit.hip), k <= 2^18.
+hipError_t launch_fit_codebook(const float* w, int64_t ldw, int64_t n, int64_t k, uint8_t* cb, hipStream_t s);
+
 // VALU path, 1 <= m <= 8.
 hipError_t launch_gemv(const PlaneView& w, const uint16_t* x, int64_t m, int64_t ldx, float* y, int64_t ldy,
                        hipStream_t s);

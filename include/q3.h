@@ -137,13 +137,36 @@ Q3_API q3_status q3_layout(int64_t n, int64_t k, q3_layout_info* out);
  *   codebook    [n][8] E4M3FN bytes without NaN entries (not checked), 8-byte aligned
  *   codes       [n][ldc] uint8 out, 8-byte aligned, ldc % 8 == 0, ldc >= k
  *   scale_bytes [n][lds] uint8 out, lds >= k/32
- * k > 0, k % 32 == 0.  One launch; codebook fitting is not part of it.
+ * k > 0, k % 32 == 0.  One launch; the codebooks may come from q3_fit_codebook.
  * A group whose largest magnitude is below max|codebook| * 2^-111 (an all-zero
  * group included) or above max|codebook| * 2^113 gets a scale byte outside
  * [16, 240], the range in which the products below dequantise exactly; their
  * outputs for rows with such groups are then not covered by the 1e-3 bound. */
 Q3_API q3_status q3_quantize(const float* w, int64_t ldw, const uint8_t* codebook, int64_t n, int64_t k,
                              uint8_t* codes, int64_t ldc, uint8_t* scale_bytes, int64_t lds, void* stream);
+
+/* Fit each row's codebook to its weights (the step before q3_quantize; the
+ * page's "Three-bit weights" illustration fits the 8-entry FP8 codebook to the
+ * weights it serves; the procedure is this library's reading, every decision
+ * exact, so results are bit-identical to exact arithmetic):
+ *   1. per group of 32: e = the smallest integer with max|w| <= 2^e (0 for an
+ *      all-zero group);
+ *   2. q = round(w * 2^(12 - e)), ties to even (integers in [-4096, 4096]);
+ *   3. 1-D k-means (Lloyd) with 8 centroids on the row's q: start at the
+ *      values of ranks floor((2i+1)K/16) of the sorted q; each q joins its
+ *      nearest centroid (equal distances: lower index); a centroid with
+ *      points becomes their exact mean, one without keeps its value; the
+ *      centroids are re-sorted by value (stable); stop when no centroid
+ *      changes or after 64 updates;
+ *   4. codebook[r][i] = centroid i / 2^12 rounded to the nearest E4M3FN value,
+ *      ties to the even significand (-0 for a negative centroid rounding to 0).
+ * Entries come out in ascending order.
+ *   w        [n][ldw] fp32, finite (not checked); 16-byte aligned, ldw % 4 == 0,
+ *            ldw >= k; 0 < k <= 262144, k % 32 == 0
+ *   codebook [n][8] uint8 out (E4M3FN), 8-byte aligned
+ * One launch, one block per row. */
+Q3_API q3_status q3_fit_codebook(const float* w, int64_t ldw, int64_t n, int64_t k, uint8_t* codebook,
+                                 void* stream);
 
 /* Pack unpacked codes and scales into the planes ("Three-bit weights": a
  * 3-bit index per weight, one 8-bit scale per group of 32).

@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
                                          "q3_shortlist_workspace_bytes", "q3_shortlist", "q3_rescore_fp8",
                                          "q3_draft_head_workspace_bytes", "q3_draft_head", "q3_moe_budget_topk",
                                          "q3_moe_mlp_workspace_bytes", "q3_moe_mlp", "q3_quantize",
-                                         "q3_moe_mlp_noalloc", "q3_moe_mlp_noalloc_max_bytes",
+                                         "q3_moe_mlp_noalloc", "q3_moe_mlp_noalloc_max_bytes", "q3_fit_codebook",
                                          "q3_gemm_small_m_workspace_bytes", "q3_gemm_small_m_ws"])
 
 
@@ -199,6 +199,14 @@ def test_validation_rejects_before_any_hip_call(q3lib):
     assert q3lib.q3_grouped_expert_gemv(ctypes.byref(st), fake, 64, 0, fake, 8, 8, fake, 16, None) == 1
     st.code_expert_stride = 776                                                     # not 16-aligned
     assert q3lib.q3_grouped_expert_gemv(ctypes.byref(st), fake, 64, 0, fake, 8, 8, fake, 16, None) == 3
+    # codebook fitting
+    assert q3lib.q3_fit_codebook(fake, 64, 4, 48, fake, None) == 2            # k % 32 != 0
+    assert q3lib.q3_fit_codebook(fake, 1 << 19, 4, 1 << 19, fake, None) == 2  # k above 2^18
+    assert q3lib.q3_fit_codebook(fake, 60, 4, 64, fake, None) == 1            # ldw < k
+    assert q3lib.q3_fit_codebook(fake + 4, 64, 4, 64, fake, None) == 3        # w not 16-aligned
+    assert q3lib.q3_fit_codebook(fake, 66, 4, 64, fake, None) == 3            # ldw % 4
+    assert q3lib.q3_fit_codebook(fake, 64, 4, 64, fake + 4, None) == 3        # codebook not 8-aligned
+    assert q3lib.q3_fit_codebook(None, 64, 4, 64, fake, None) == 1
     # quantizer
     assert q3lib.q3_quantize(fake, 64, fake, 4, 48, fake, 64, fake, 2, None) == 2       # k % 32 != 0
     assert q3lib.q3_quantize(fake, 60, fake, 4, 64, fake, 64, fake, 2, None) == 1       # ldw < k
