@@ -194,7 +194,45 @@ __global__ __launch_bounds__(64 * kW) void splitk_kernel(SplitArgs a) {
   }
 
   float* const red = reinterpret_cast<float*>(lds + kRed);
-  if constexpr (!kDot) {
+  if constexpr (!kDot && NT == 1 && kHS == 1) {
+    // One token, one half-step: the activations go to registers right away
+    // (every lane reads its quad's 128 bytes), the token's 16 row sums are
+    // gathered into lanes 0..15 (lane 16*(r/4) holds rows 4*(r/4)..+3), and
+    // the waves' sums meet as 16 floats each.
+    u32x4 xv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xv[e] = *reinterpret_cast<const u32x4*>(xw + 128u * kb + 16u * e);
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x2 wv[16];
+      dequant_group_bf16(w[0][0][t], w[0][1][t], w[0][2][t], (sc[0] >> (8 * t)) & 0xFFu, cbv.x, cbv.y, wv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const u32x4 au = {__builtin_bit_cast(uint32_t, wv[4 * e]), __builtin_bit_cast(uint32_t, wv[4 * e + 1]),
+                          __builtin_bit_cast(uint32_t, wv[4 * e + 2]), __builtin_bit_cast(uint32_t, wv[4 * e + 3])};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, au), __builtin_bit_cast(bf16x8, xv[4 * t + e]),
+                                                    d, 0, 0, 0);
+      }
+    }
+    float r = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float dv = __shfl(d[v], 16 * (i >> 2), 64);
+      if ((i & 3) == v) r = dv;
+    }
+    if (lane < 16) red[wave * 16 + lane] = r;
+    __syncthreads();
+    if (wave == 0 && lane < 16) {
+      float v = red[lane];
+#pragma unroll
+      for (int q = 1; q < kW; ++q) v += red[q * 16 + lane];
+      if (row < a.n) {
+        if (a.y_rsrc) store_y1(a.y, a.ldy, a.n, m, row, v);
+        else a.y[row] = v;
+      }
+    }
+  } else if constexpr (!kDot) {
     // Lanes of absent tokens read the last token's activations: their output
     // columns repeat it and are never stored.
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
@@ -231,6 +269,37 @@ __global__ __launch_bounds__(64 * kW) void splitk_kernel(SplitArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (row0 + e < a.n) a.y[o + e] = v[e];
+      }
+    }
+  } else if constexpr (kDot && NT == 1 && kHS == 1) {
+    // One token, one half-step on the vector ALUs: activations to registers
+    // first, then the dot products, the four quads of a row added by lane
+    // exchanges, and the waves' 16 row sums after one barrier.
+    u32x4 xv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xv[e] = *reinterpret_cast<const u32x4*>(xw + 128u * kb + 16u * e);
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x2 wv[16];
+      dequant_group_bf16(w[0][0][t], w[0][1][t], w[0][2][t], (sc[0] >> (8 * t)) & 0xFFu, cbv.x, cbv.y, wv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc = __builtin_amdgcn_fdot2_f32_bf16(wv[4 * e + q], as_bf16x2(xv[4 * t + e][q]), acc, false);
+    }
+    acc += __shfl_xor(acc, 32, 64);
+    acc += __shfl_xor(acc, 16, 64);
+    if (lane < 16) red[wave * 16 + lane] = acc;
+    __syncthreads();
+    if (wave == 0 && lane < 16) {
+      float v = red[lane];
+#pragma unroll
+      for (int q = 1; q < kW; ++q) v += red[q * 16 + lane];
+      if (row < a.n) {
+        if (a.y_rsrc) store_y1(a.y, a.ldy, a.n, m, row, v);
+        else a.y[row] = v;
       }
     }
   } else {
