@@ -46,6 +46,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 LLC_BYTES = 256 << 20
 METRIC = "packed-weight HBM GB/s and % of MI355X peak at M=1/8/64; oracle-exact"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+MOE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_moe_round.json")
 
 
 def log(*a):
@@ -111,12 +112,15 @@ def capture(fn, stream):
 
 
 TRIALS = 5
+REPS = 0          # --reps: replays per trial for every point (0: each point's own default)
 
 
-def time_graph(g, stream, reps: int, warmup: int, trials: int = TRIALS):
+def time_graph(g, stream, reps: int, warmup: int, trials: int = None):
     """Median over `trials` timings of `reps` back-to-back replays (ms per
     replay), and every trial's figure."""
     import torch
+    trials = TRIALS if trials is None else trials
+    reps = REPS or reps
     per = []
     with torch.cuda.stream(stream):
         for _ in range(warmup):
@@ -469,9 +473,9 @@ def cpu_baseline(synth, budget_s=12.0):
                 single_thread=single)
 
 
-def _traffic_file():
+def _traffic_file(path=None):
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path or TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -488,18 +492,17 @@ def read_traffic(dot: bool):
     """(kernel name, per-launch HBM bytes) of the M=1 kernel of the measured
     layer from the committed counter file, or (family name, None) when that
     file was taken on other sources.  Kernels are named by their template
-    arguments <tokens or column tiles, row tiles, waves, grouped, activation
-    mode, vector-ALU, code bits>; the counter run covers only the 4096 x 4096
-    launches."""
-    family = "linear_kernel (vector-ALU, M=1)" if dot else "linear_kernel (matrix-core, M=1)"
+    arguments."""
+    family = "splitk_kernel (vector-ALU, M=1)" if dot else "splitk_kernel (matrix-core, M=1)"
     t = _traffic_file()
     if t is None:
         return family, None
 
     def dense_m1(k):
-        args = _kernel_args(k, "linear_kernel")
-        return (args is not None and len(args) == 7 and args[0] == "1" and args[3] in ("0", "false")
-                and args[5] == ("true" if dot else "false") and args[6] == "3")
+        # The 4096 x 4096 layer at one token runs the split-K kernel: 16 waves,
+        # one half-step each, one token (template <waves, half-steps, vector-ALU, tokens>).
+        args = _kernel_args(k, "splitk_kernel")
+        return args == ["16", "1", "true" if dot else "false", "1"]
     cands = [(v.get("dispatches", 0), k, v) for k, v in t.get("kernels", {}).items() if dense_m1(k)]
     if not cands:
         return family, None
@@ -511,8 +514,9 @@ def moe_traffic():
     """HBM bytes the two grouped products of one plain verify round read, from
     the committed counter file (None when absent or taken on other sources):
     the expert passes are one kernel instance (grouping 1) dispatched once for
-    gate/up and once for down per round, so a round reads twice its average."""
-    t = _traffic_file()
+    gate/up and once for down per round, so a round reads twice its average
+    (counters of a run that times only the plain round)."""
+    t = _traffic_file(MOE_TRAFFIC_FILE)
     if t is None:
         return None
     cands = []
@@ -529,6 +533,7 @@ def moe_traffic():
 # --------------------------------------------------------------------- main
 
 def main():
+    global REPS, TRIALS
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -544,7 +549,10 @@ def main():
                     help="time only the K=4096 N=151936 M=64 point (for counter runs of its kernel) and print it")
     ap.add_argument("--only-moe", action="store_true",
                     help="time only the plain MoE verify round (for counter runs of the expert passes) and print it")
+    ap.add_argument("--reps", type=int, default=0, help="graph replays per trial for every point (profiler runs)")
+    ap.add_argument("--trials", type=int, default=TRIALS, help="trials per point (median reported)")
     args = ap.parse_args()
+    REPS, TRIALS = args.reps, max(1, args.trials)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -45,7 +45,8 @@ def per_kernel(path, counter):
     return vals
 
 
-KEYS = ("linear_kernel<", "wide_kernel<", "split_reduce_kernel<", "pack_kernel", "unpack_kernel",
+KEYS = ("splitk_kernel<", "linear_kernel<", "wide_kernel<", "split_reduce_kernel<", "fit_kernel", "pack_kernel",
+        "unpack_kernel",
         "budget_topk_kernel", "topk_kernel", "combine_kernel", "quantize_kernel", "shortlist_chunks",
         "rescore_kernel", "read_kernel<", "copyBuffer")
 

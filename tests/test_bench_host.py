@@ -40,8 +40,9 @@ def _write_traffic(tmp_path, source_hash, kernels):
 
 
 KERNELS = {
-    "linear_kernel<1, 1, 4, 0, 0, true, 3>": {"read_bytes": 7_029_704, "write_bytes": 16_384, "dispatches": 633},
-    "linear_kernel<1, 1, 4, 0, 0, false, 3>": {"read_bytes": 7_053_214, "write_bytes": 16_384, "dispatches": 1344},
+    "splitk_kernel<16, 1, true, 1>": {"read_bytes": 7_029_704, "write_bytes": 16_384, "dispatches": 633},
+    "splitk_kernel<16, 1, false, 1>": {"read_bytes": 7_053_214, "write_bytes": 16_384, "dispatches": 1344},
+    "splitk_kernel<4, 1, false, 1>": {"read_bytes": 5, "write_bytes": 5, "dispatches": 99999},
     "linear_kernel<1, 1, 8, 1, 0, false, 3>": {"read_bytes": 1, "write_bytes": 1, "dispatches": 99999},
     "linear_kernel<1, 1, 8, 0, 0, false, 2>": {"read_bytes": 2, "write_bytes": 2, "dispatches": 99999},
     "pack_kernel": {"read_bytes": 3, "write_bytes": 3, "dispatches": 1},
@@ -51,17 +52,17 @@ KERNELS = {
 def test_traffic_is_read_for_the_matching_sources(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", _write_traffic(tmp_path, bench.source_hash(), KERNELS))
     name, v = bench.read_traffic(True)
-    assert name == "linear_kernel<1, 1, 4, 0, 0, true, 3>" and v["read_bytes"] == 7_029_704
-    # the matrix-core instance; expert passes and 2-bit kernels are never taken for it
+    assert name == "splitk_kernel<16, 1, true, 1>" and v["read_bytes"] == 7_029_704
+    # the matrix-core instance; other shapes' instances, expert passes and 2-bit kernels are never taken for it
     name, v = bench.read_traffic(False)
-    assert name == "linear_kernel<1, 1, 4, 0, 0, false, 3>" and v["read_bytes"] == 7_053_214
+    assert name == "splitk_kernel<16, 1, false, 1>" and v["read_bytes"] == 7_053_214
 
 
 def test_traffic_from_other_sources_is_not_reported(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", _write_traffic(tmp_path, "0" * 16, KERNELS))
-    assert bench.read_traffic(True) == ("linear_kernel (vector-ALU, M=1)", None)
+    assert bench.read_traffic(True) == ("splitk_kernel (vector-ALU, M=1)", None)
     monkeypatch.setattr(bench, "TRAFFIC_FILE", os.path.join(str(tmp_path), "missing.json"))
-    assert bench.read_traffic(False) == ("linear_kernel (matrix-core, M=1)", None)
+    assert bench.read_traffic(False) == ("splitk_kernel (matrix-core, M=1)", None)
 
 
 
@@ -69,10 +70,10 @@ def test_union_traffic_is_twice_the_expert_pass_average(tmp_path, monkeypatch):
     # Gate/up and down are one kernel instance (grouping 1), one dispatch each per round.
     k = {n: v for n, v in KERNELS.items() if ", 1, 0, false, 3>" not in n}
     k["linear_kernel<1, 1, 4, 1, 0, false, 3>"] = {"read_bytes": 41_000_000, "write_bytes": 10, "dispatches": 40}
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", _write_traffic(tmp_path, bench.source_hash(), k))
+    monkeypatch.setattr(bench, "MOE_TRAFFIC_FILE", _write_traffic(tmp_path, bench.source_hash(), k))
     t = bench.moe_traffic()
     assert t["read_bytes_per_round"] == 82_000_000 and t["kernel"] == "linear_kernel<1, 1, 4, 1, 0, false, 3>"
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", _write_traffic(tmp_path, "1" * 16, k))
+    monkeypatch.setattr(bench, "MOE_TRAFFIC_FILE", _write_traffic(tmp_path, "1" * 16, k))
     assert bench.moe_traffic() is None
 
 
