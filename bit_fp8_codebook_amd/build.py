@@ -62,6 +62,52 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# Host-side sanitizers for the C ABI's validation code (a separate library,
+# loaded only by the CPU sanitizer test): every -fsanitize applies to the host
+# pass alone; device code is built as usual.
+ASAN_DIR = os.path.join(PKG, "_build_asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libq3_asan.so")
+ASAN_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+              "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The clang ASan runtime to preload into an uninstrumented interpreter."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("clang's ASan runtime (libclang_rt.asan-x86_64.so) not found under /opt/rocm/lib/llvm")
+    return hits[-1]
+
+
+def _compile_asan(src: str) -> str:
+    obj = os.path.join(ASAN_DIR, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *[f for f in COMMON if f != "-O3"], *DEVICE_FLAGS, *ASAN_FLAGS, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build_asan(verbose: bool = True) -> str:
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    srcs = sources()
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile_asan, srcs))
+    tmp = ASAN_LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libasan", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, ASAN_LIB)
+    if verbose:
+        print(f"built {ASAN_LIB}")
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
     build()
+    if len(sys.argv) > 1 and sys.argv[1] == "asan":
+        build_asan()
     sys.exit(0)
