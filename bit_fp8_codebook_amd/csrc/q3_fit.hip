@@ -38,13 +38,6 @@ constexpr int kFitThreads = 256;
 constexpr int kChunk = (kBins + kFitThreads - 1) / kFitThreads;   // bins per thread in the scans
 constexpr int kMaxUpdates = 64;
 
-struct Cent {
-  int64_t s, c;   // the centroid is s / c (c > 0)
-};
-
-__device__ __forceinline__ bool cent_less(Cent a, Cent b) { return a.s * b.c < b.s * a.c; }
-__device__ __forceinline__ bool cent_eq(Cent a, Cent b) { return a.s * b.c == b.s * a.c; }
-
 // floor(num / den) for den > 0, exact: a double estimate corrected by the
 // exact integer comparisons (|num|, den < 2^53).
 __device__ __forceinline__ int64_t floor_div(int64_t num, int64_t den) {
@@ -141,29 +134,29 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(const float* __restric
 
   // Prefix arrays: cnt[b] = #q < b - kHalf, psum[b] = sum of those q.
   {
+    // each thread owns bins [b0, b0 + kChunk): it reads its counts, and reads
+    // each again just before overwriting it with the prefix
     const int b0 = t * kChunk;
-    int c[kChunk];
     int lc = 0, ls = 0;
-#pragma unroll
     for (int i = 0; i < kChunk; ++i) {
       const int b = b0 + i;
-      c[i] = b < kBins ? cnt[b] : 0;
-      lc += c[i];
-      ls += c[i] * (b - kHalf);
+      const int c = b < kBins ? cnt[b] : 0;
+      lc += c;
+      ls += c * (b - kHalf);
     }
     int tc, ts;
     const int pc = block_scan(lc, tmp, &tc);
     const int ps = block_scan(ls, tmp, &ts);
     int rc = pc, rs = ps;
-#pragma unroll
     for (int i = 0; i < kChunk; ++i) {
       const int b = b0 + i;
       if (b < kBins) {
+        const int c = cnt[b];
         cnt[b] = rc;
         psum[b] = rs;
+        rc += c;
+        rs += c * (b - kHalf);
       }
-      rc += c[i];
-      rs += c[i] * (b - kHalf);
     }
     if (t == 0) {
       cnt[kBins] = tc;
@@ -173,62 +166,90 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(const float* __restric
   __syncthreads();
   if (t != 0) return;
 
-  // 3: Lloyd on the prefix arrays (one lane).
+  // 3: Lloyd on the prefix arrays (one lane).  The centroids are held as
+  // separate sum and count arrays indexed only by compile-time constants (fully
+  // unrolled loops, selects), so they stay in registers.
   const int64_t K = cnt[kBins];
-  Cent cur[8];
+  int64_t cs[8], cc[8];                          // centroid a is cs[a] / cc[a]
+#pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int64_t r = (2 * i + 1) * K / 16;      // value of rank r: the smallest b with #q <= b-kHalf > r
+    // value of rank r (0-based) of the sorted q: the smallest b with
+    // #q <= b - kHalf greater than r, by a fixed-length binary search
+    const int64_t r = (2 * i + 1) * K / 16;
     int lo = 0, hi = kBins - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (cnt[mid + 1] > r) hi = mid;
-      else lo = mid + 1;
+#pragma unroll
+    for (int step = 0; step < 14; ++step) {     // 2^14 > kBins
+      const int mid = (lo + hi) >> 1;            // mid + 1 <= kBins: in bounds
+      const bool open = lo < hi, up = cnt[mid + 1] <= r;
+      lo = open && up ? mid + 1 : lo;
+      hi = open && !up ? mid : hi;
     }
-    cur[i] = Cent{lo - kHalf, 1};
+    cs[i] = lo - kHalf;
+    cc[i] = 1;
   }
   for (int it = 0; it < kMaxUpdates; ++it) {
-    Cent nxt[8];
-    for (int i = 0; i < 8; ++i) nxt[i] = cur[i];
     // Runs of equal centroids: the first index of a run takes the q between
     // the midpoints to the neighbouring distinct values (a q on a midpoint
-    // goes to the lower run); the others get none.
-    int lo_q = -kHalf - 1;                       // q of the run start lie above this
-    int i = 0;
-    while (i < 8) {
-      int j = i;
-      while (j + 1 < 8 && cent_eq(cur[j + 1], cur[i])) ++j;
-      int hi_q = kHalf;
-      if (j + 1 < 8) {
-        const Cent a = cur[i], b = cur[j + 1];
-        const int64_t m = floor_div(a.s * b.c + b.s * a.c, 2 * a.c * b.c);
-        hi_q = (int)(m < -kHalf - 1 ? -kHalf - 1 : (m > kHalf ? kHalf : m));
+    // goes to the lower run); the others get none and keep their value.
+    int64_t ns[8], nc[8];
+    int lo_q = -kHalf - 1;                       // q of the current run lie above this
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      ns[a] = cs[a];
+      nc[a] = cc[a];
+      bool start = true;
+      if (a > 0) start = cs[a] * cc[a - 1] != cs[a - 1] * cc[a];
+      bool have = false;                         // the next distinct value after this run
+      int64_t bs = cs[a], bc = cc[a];
+#pragma unroll
+      for (int b = 7; b > a; --b) {
+        const bool d = cs[b] * cc[a] != cs[a] * cc[b];
+        have = have || d;
+        bs = d ? cs[b] : bs;                     // ends on the smallest such b
+        bc = d ? cc[b] : bc;
       }
-      if (hi_q < lo_q) hi_q = lo_q;
-      const int64_t n_in = cnt[hi_q + kHalf + 1] - cnt[lo_q + kHalf + 1];
-      if (n_in > 0) nxt[i] = Cent{(int64_t)psum[hi_q + kHalf + 1] - psum[lo_q + kHalf + 1], n_in};
-      lo_q = hi_q;
-      i = j + 1;
-    }
-    // Stable insertion sort by value.
-    for (int a = 1; a < 8; ++a) {
-      const Cent x = nxt[a];
-      int b = a - 1;
-      while (b >= 0 && cent_less(x, nxt[b])) {
-        nxt[b + 1] = nxt[b];
-        --b;
+      if (start) {
+        int hi_q = kHalf;
+        if (have) {
+          const int64_t m = floor_div(cs[a] * bc + bs * cc[a], 2 * cc[a] * bc);
+          hi_q = (int)(m < -kHalf - 1 ? -kHalf - 1 : (m > kHalf ? kHalf : m));
+        }
+        hi_q = hi_q < lo_q ? lo_q : hi_q;
+        const int64_t n_in = cnt[hi_q + kHalf + 1] - cnt[lo_q + kHalf + 1];
+        const int64_t s_in = (int64_t)psum[hi_q + kHalf + 1] - psum[lo_q + kHalf + 1];
+        ns[a] = n_in > 0 ? s_in : ns[a];
+        nc[a] = n_in > 0 ? n_in : nc[a];
+        lo_q = hi_q;
       }
-      nxt[b + 1] = x;
     }
+    // Sort by value with adjacent compare-exchanges (stable: equal values never swap).
+#pragma unroll
+    for (int pass = 0; pass < 7; ++pass)
+#pragma unroll
+      for (int a = 0; a < 7 - pass; ++a) {
+        const bool sw = ns[a + 1] * nc[a] < ns[a] * nc[a + 1];
+        const int64_t xs = ns[a], xc = nc[a], ys = ns[a + 1], yc = nc[a + 1];
+        ns[a] = sw ? ys : xs;
+        nc[a] = sw ? yc : xc;
+        ns[a + 1] = sw ? xs : ys;
+        nc[a + 1] = sw ? xc : yc;
+      }
     bool same = true;
-    for (int a = 0; a < 8; ++a) same = same && cent_eq(nxt[a], cur[a]);
-    for (int a = 0; a < 8; ++a) cur[a] = nxt[a];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      same = same && ns[a] * cc[a] == cs[a] * nc[a];
+      cs[a] = ns[a];
+      cc[a] = nc[a];
+    }
     if (same) break;
   }
 
   // 4: round to E4M3FN.
   uint32_t lo = 0, hi = 0;
-  for (int a = 0; a < 4; ++a) lo |= (uint32_t)round_e4m3fn(cur[a].s, cur[a].c) << (8 * a);
-  for (int a = 0; a < 4; ++a) hi |= (uint32_t)round_e4m3fn(cur[a + 4].s, cur[a + 4].c) << (8 * a);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) lo |= (uint32_t)round_e4m3fn(cs[a], cc[a]) << (8 * a);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) hi |= (uint32_t)round_e4m3fn(cs[a + 4], cc[a + 4]) << (8 * a);
   *reinterpret_cast<u32x2*>(cb + row * 8) = u32x2{lo, hi};
 }
 
