@@ -23,8 +23,8 @@
 // in LDS (integer atomics: exact counts), two block scans turn it into prefix
 // counts and prefix sums, and since 1-D clusters are contiguous ranges of q
 // between the midpoints of neighbouring distinct centroids, each update is a
-// few exact integer operations on the prefix arrays (one lane), however long
-// the row.
+// few exact operations on the prefix arrays, however long the row: eight lanes,
+// one per centroid, with exact rationals in fp64.
 #include "q3_device.h"
 #include "q3_internal.h"
 
@@ -38,13 +38,27 @@ constexpr int kFitThreads = 256;
 constexpr int kChunk = (kBins + kFitThreads - 1) / kFitThreads;   // bins per thread in the scans
 constexpr int kMaxUpdates = 64;
 
-// floor(num / den) for den > 0, exact: a double estimate corrected by the
-// exact integer comparisons (|num|, den < 2^53).
-__device__ __forceinline__ int64_t floor_div(int64_t num, int64_t den) {
-  int64_t q = (int64_t)floor((double)num / (double)den);
-  while ((q + 1) * den <= num) ++q;
-  while (q * den > num) --q;
-  return q;
+// floor of the midpoint (as/ac + bs/bc) / 2 of two centroids, exact: every
+// operand is an integer below 2^53 in magnitude (products < 2^49), so the
+// double estimate is corrected by exact comparisons.
+__device__ __forceinline__ int64_t floor_mid(double as, double ac, double bs, double bc) {
+  const double num = as * bc + bs * ac, den = 2.0 * ac * bc;
+  double q = floor(num / den);
+  while ((q + 1.0) * den <= num) q += 1.0;
+  while (q * den > num) q -= 1.0;
+  return (int64_t)q;
+}
+
+__device__ __forceinline__ int clamp_q(int64_t m) {
+  return (int)(m < -kHalf - 1 ? -kHalf - 1 : (m > kHalf ? kHalf : m));
+}
+
+// The value of this lane lands in lane `dst` (ds_permute: each lane pushes).
+__device__ __forceinline__ double permute_to(int dst, double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_permute(dst * 4, (int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_permute(dst * 4, (int)(uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 // E4M3FN magnitude of byte b (0..0x7E) in units of 2^-9.
@@ -164,18 +178,21 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(const float* __restric
     }
   }
   __syncthreads();
-  if (t != 0) return;
+  if (t >= 64) return;
 
-  // 3: Lloyd on the prefix arrays (one lane).  The centroids are held as
-  // separate sum and count arrays indexed only by compile-time constants (fully
-  // unrolled loops, selects), so they stay in registers.
+  // 3: Lloyd on the prefix arrays, one centroid per lane: lane a of every
+  // group of eight lanes holds centroid a as an exact rational s/c (|s| <= 2^30,
+  // 1 <= c <= 2^18) in two doubles, so every cross product (< 2^49) and every
+  // sum of two of them is exact in fp64 and compares exactly.  The eight
+  // groups of the wave compute the same thing; group 0's lanes are read.
+  const int a = t & 7;
+  const int g0 = t & ~7;                         // first lane of this group
   const int64_t K = cnt[kBins];
-  int64_t cs[8], cc[8];                          // centroid a is cs[a] / cc[a]
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  double cs, cc;
+  {
     // value of rank r (0-based) of the sorted q: the smallest b with
     // #q <= b - kHalf greater than r, by a fixed-length binary search
-    const int64_t r = (2 * i + 1) * K / 16;
+    const int64_t r = (2 * a + 1) * K / 16;
     int lo = 0, hi = kBins - 1;
 #pragma unroll
     for (int step = 0; step < 14; ++step) {     // 2^14 > kBins
@@ -184,73 +201,50 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(const float* __restric
       lo = open && up ? mid + 1 : lo;
       hi = open && !up ? mid : hi;
     }
-    cs[i] = lo - kHalf;
-    cc[i] = 1;
+    cs = (double)(lo - kHalf);
+    cc = 1.0;
   }
   for (int it = 0; it < kMaxUpdates; ++it) {
-    // Runs of equal centroids: the first index of a run takes the q between
-    // the midpoints to the neighbouring distinct values (a q on a midpoint
-    // goes to the lower run); the others get none and keep their value.
-    int64_t ns[8], nc[8];
-    int lo_q = -kHalf - 1;                       // q of the current run lie above this
+    // Runs of equal centroids (the centroids are sorted): the first lane of a
+    // run takes the q between the midpoints to the neighbouring distinct values
+    // (a q on a midpoint goes to the lower run); the others get none and keep
+    // their value.
+    const double ps = __shfl(cs, g0 + (a > 0 ? a - 1 : 0), 64);
+    const double pc = __shfl(cc, g0 + (a > 0 ? a - 1 : 0), 64);
+    const bool start = a == 0 || ps * cc != cs * pc;
+    const uint32_t starts = (uint32_t)__ballot(start) & 0xFFu;    // group 0's lanes
+    const uint32_t above = starts >> (a + 1);
+    const int nb = above ? a + 1 + __builtin_ctz(above) : a;     // next run's first lane
+    const double ns = __shfl(cs, g0 + nb, 64);
+    const double nc = __shfl(cc, g0 + nb, 64);
+    int hi_q = kHalf, lo_q = -kHalf - 1;
+    if (above) hi_q = clamp_q(floor_mid(cs, cc, ns, nc));
+    if (a > 0) lo_q = clamp_q(floor_mid(ps, pc, cs, cc));
+    hi_q = hi_q < lo_q ? lo_q : hi_q;
+    const int n_in = cnt[hi_q + kHalf + 1] - cnt[lo_q + kHalf + 1];
+    const int s_in = psum[hi_q + kHalf + 1] - psum[lo_q + kHalf + 1];
+    const bool take = start && n_in > 0;
+    const double ts = take ? (double)s_in : cs;
+    const double tc = take ? (double)n_in : cc;
+    // Stable rank by value: centroids below, and equal ones at lower lanes.
+    int rank = 0;
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      ns[a] = cs[a];
-      nc[a] = cc[a];
-      bool start = true;
-      if (a > 0) start = cs[a] * cc[a - 1] != cs[a - 1] * cc[a];
-      bool have = false;                         // the next distinct value after this run
-      int64_t bs = cs[a], bc = cc[a];
-#pragma unroll
-      for (int b = 7; b > a; --b) {
-        const bool d = cs[b] * cc[a] != cs[a] * cc[b];
-        have = have || d;
-        bs = d ? cs[b] : bs;                     // ends on the smallest such b
-        bc = d ? cc[b] : bc;
-      }
-      if (start) {
-        int hi_q = kHalf;
-        if (have) {
-          const int64_t m = floor_div(cs[a] * bc + bs * cc[a], 2 * cc[a] * bc);
-          hi_q = (int)(m < -kHalf - 1 ? -kHalf - 1 : (m > kHalf ? kHalf : m));
-        }
-        hi_q = hi_q < lo_q ? lo_q : hi_q;
-        const int64_t n_in = cnt[hi_q + kHalf + 1] - cnt[lo_q + kHalf + 1];
-        const int64_t s_in = (int64_t)psum[hi_q + kHalf + 1] - psum[lo_q + kHalf + 1];
-        ns[a] = n_in > 0 ? s_in : ns[a];
-        nc[a] = n_in > 0 ? n_in : nc[a];
-        lo_q = hi_q;
-      }
+    for (int b = 0; b < 8; ++b) {
+      const double bs = __shfl(ts, g0 + b, 64), bc = __shfl(tc, g0 + b, 64);
+      const double l = bs * tc, r = ts * bc;
+      rank += (l < r || (l == r && b < a)) ? 1 : 0;
     }
-    // Sort by value with adjacent compare-exchanges (stable: equal values never swap).
-#pragma unroll
-    for (int pass = 0; pass < 7; ++pass)
-#pragma unroll
-      for (int a = 0; a < 7 - pass; ++a) {
-        const bool sw = ns[a + 1] * nc[a] < ns[a] * nc[a + 1];
-        const int64_t xs = ns[a], xc = nc[a], ys = ns[a + 1], yc = nc[a + 1];
-        ns[a] = sw ? ys : xs;
-        nc[a] = sw ? yc : xc;
-        ns[a + 1] = sw ? xs : ys;
-        nc[a + 1] = sw ? xc : yc;
-      }
-    bool same = true;
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      same = same && ns[a] * cc[a] == cs[a] * nc[a];
-      cs[a] = ns[a];
-      cc[a] = nc[a];
-    }
-    if (same) break;
+    // Lane g0 + rank receives this centroid.
+    const double ss = permute_to(g0 + rank, ts);
+    const double sc = permute_to(g0 + rank, tc);
+    const bool same = ss * cc == cs * sc;
+    cs = ss;
+    cc = sc;
+    if (((uint32_t)__ballot(same) & 0xFFu) == 0xFFu) break;
   }
 
-  // 4: round to E4M3FN.
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int a = 0; a < 4; ++a) lo |= (uint32_t)round_e4m3fn(cs[a], cc[a]) << (8 * a);
-#pragma unroll
-  for (int a = 0; a < 4; ++a) hi |= (uint32_t)round_e4m3fn(cs[a + 4], cc[a + 4]) << (8 * a);
-  *reinterpret_cast<u32x2*>(cb + row * 8) = u32x2{lo, hi};
+  // 4: round to E4M3FN, one entry per lane.
+  if (t < 8) cb[row * 8 + a] = round_e4m3fn((int64_t)cs, (int64_t)cc);
 }
 
 }  // namespace
