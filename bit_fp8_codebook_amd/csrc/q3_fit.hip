@@ -104,18 +104,25 @@ __device__ int block_scan(int v, int* tmp, int* total) {
   return incl - v;
 }
 
+// kNarrow (rows shorter than 65536): the prefix counts fit 16 bits, so the
+// histogram is counted in the prefix-sum array and the prefix counts take half
+// the space (49 KB of LDS instead of 65 KB: three blocks per CU instead of two).
+template <bool kNarrow>
 __global__ __launch_bounds__(kFitThreads) void fit_kernel(const float* __restrict__ w, int64_t ldw, int64_t k,
                                                           uint8_t* __restrict__ cb) {
   extern __shared__ __align__(16) int smem[];
-  int* cnt = smem;                       // kBins + 1: counts, then prefix counts
-  int* psum = smem + (kBins + 1);        // kBins + 1: prefix sums of q
+  int* psum = smem;                                                 // kBins + 1: prefix sums of q
+  int* cnt32 = smem + (kBins + 1);                                  // kBins + 1 (wide rows)
+  uint16_t* cnt16 = reinterpret_cast<uint16_t*>(smem + (kBins + 1));   // kBins + 1 (narrow rows)
+  int* hist = kNarrow ? psum : cnt32;                               // counts before the scan
+  auto cnt = [&](int b) -> int { return kNarrow ? (int)cnt16[b] : cnt32[b]; };   // #q < b - kHalf
   __shared__ int tmp[kFitThreads];
   const int t = threadIdx.x;
   const int64_t row = blockIdx.x;
   const float* wr = w + row * ldw;
   const int groups = (int)(k / 32);
 
-  for (int b = t; b < kBins + 1; b += kFitThreads) cnt[b] = 0;
+  for (int b = t; b < kBins + 1; b += kFitThreads) hist[b] = 0;
   __syncthreads();
 
   // 1-2: exponent of each group, grid values, histogram.
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(const float* __restric
         // exact scaling by a power of two (|result| <= 4096; results below
         // 2^-126 round to zero either way), then round half to even
         const int q = (int)rintf(ldexpf(v[i][j], kGridBits - e));
-        atomicAdd(&cnt[q + kHalf], 1);
+        atomicAdd(&hist[q + kHalf], 1);
       }
   }
   __syncthreads();
@@ -154,7 +161,7 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(const float* __restric
     int lc = 0, ls = 0;
     for (int i = 0; i < kChunk; ++i) {
       const int b = b0 + i;
-      const int c = b < kBins ? cnt[b] : 0;
+      const int c = b < kBins ? hist[b] : 0;
       lc += c;
       ls += c * (b - kHalf);
     }
@@ -165,15 +172,17 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(const float* __restric
     for (int i = 0; i < kChunk; ++i) {
       const int b = b0 + i;
       if (b < kBins) {
-        const int c = cnt[b];
-        cnt[b] = rc;
+        const int c = hist[b];          // this thread's own bin: read before it is overwritten
+        if constexpr (kNarrow) cnt16[b] = (uint16_t)rc;
+        else cnt32[b] = rc;
         psum[b] = rs;
         rc += c;
         rs += c * (b - kHalf);
       }
     }
     if (t == 0) {
-      cnt[kBins] = tc;
+      if constexpr (kNarrow) cnt16[kBins] = (uint16_t)tc;
+      else cnt32[kBins] = tc;
       psum[kBins] = ts;
     }
   }
@@ -187,7 +196,7 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(const float* __restric
   // groups of the wave compute the same thing; group 0's lanes are read.
   const int a = t & 7;
   const int g0 = t & ~7;                         // first lane of this group
-  const int64_t K = cnt[kBins];
+  const int64_t K = cnt(kBins);
   double cs, cc;
   {
     // value of rank r (0-based) of the sorted q: the smallest b with
@@ -197,7 +206,7 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(const float* __restric
 #pragma unroll
     for (int step = 0; step < 14; ++step) {     // 2^14 > kBins
       const int mid = (lo + hi) >> 1;            // mid + 1 <= kBins: in bounds
-      const bool open = lo < hi, up = cnt[mid + 1] <= r;
+      const bool open = lo < hi, up = cnt(mid + 1) <= r;
       lo = open && up ? mid + 1 : lo;
       hi = open && !up ? mid : hi;
     }
@@ -221,7 +230,7 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(const float* __restric
     if (above) hi_q = clamp_q(floor_mid(cs, cc, ns, nc));
     if (a > 0) lo_q = clamp_q(floor_mid(ps, pc, cs, cc));
     hi_q = hi_q < lo_q ? lo_q : hi_q;
-    const int n_in = cnt[hi_q + kHalf + 1] - cnt[lo_q + kHalf + 1];
+    const int n_in = cnt(hi_q + kHalf + 1) - cnt(lo_q + kHalf + 1);
     const int s_in = psum[hi_q + kHalf + 1] - psum[lo_q + kHalf + 1];
     const bool take = start && n_in > 0;
     const double ts = take ? (double)s_in : cs;
@@ -247,20 +256,25 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(const float* __restric
   if (t < 8) cb[row * 8 + a] = round_e4m3fn((int64_t)cs, (int64_t)cc);
 }
 
-}  // namespace
-
-hipError_t launch_fit_codebook(const float* w, int64_t ldw, int64_t n, int64_t k, uint8_t* cb, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  const size_t shm = 2 * (kBins + 1) * sizeof(int);
-  static bool allowed = false;   // one attribute call; idempotent if it races
+template <bool kNarrow>
+hipError_t launch_fit(const float* w, int64_t ldw, int64_t n, int64_t k, uint8_t* cb, hipStream_t s) {
+  const size_t shm = (kBins + 1) * sizeof(int) + (kBins + 1) * (kNarrow ? sizeof(uint16_t) : sizeof(int));
+  static bool allowed = false;   // one attribute call per variant; idempotent if it races
   if (!allowed) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fit_kernel),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fit_kernel<kNarrow>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     if (e != hipSuccess) return e;
     allowed = true;
   }
-  hipLaunchKernelGGL(fit_kernel, dim3((unsigned)n), dim3(kFitThreads), shm, s, w, ldw, k, cb);
+  hipLaunchKernelGGL(fit_kernel<kNarrow>, dim3((unsigned)n), dim3(kFitThreads), shm, s, w, ldw, k, cb);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fit_codebook(const float* w, int64_t ldw, int64_t n, int64_t k, uint8_t* cb, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  return k < 65536 ? launch_fit<true>(w, ldw, n, k, cb, s) : launch_fit<false>(w, ldw, n, k, cb, s);
 }
 
 }  // namespace q3
