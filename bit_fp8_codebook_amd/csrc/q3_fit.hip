@@ -259,13 +259,9 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(const float* __restric
 template <bool kNarrow>
 hipError_t launch_fit(const float* w, int64_t ldw, int64_t n, int64_t k, uint8_t* cb, hipStream_t s) {
   const size_t shm = (kBins + 1) * sizeof(int) + (kBins + 1) * (kNarrow ? sizeof(uint16_t) : sizeof(int));
-  static bool allowed = false;   // one attribute call per variant; idempotent if it races
-  if (!allowed) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fit_kernel<kNarrow>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    if (e != hipSuccess) return e;
-    allowed = true;
-  }
+  static LdsAllowance seen;
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(fit_kernel<kNarrow>), shm, seen);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fit_kernel<kNarrow>, dim3((unsigned)n), dim3(kFitThreads), shm, s, w, ldw, k, cb);
   return hipGetLastError();
 }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace q3 {
 
 struct PlaneView {
@@ -105,5 +107,14 @@ hipError_t scratch_address(void** out);
 hipError_t launch_moe_mlp(const ExpertView& gu, const ExpertView& dn, const uint16_t* x, int64_t ldx,
                           const int32_t* ids, int32_t t, int32_t topk, const float* logits, int64_t ld_logits,
                           uint16_t* h, float* part, int64_t ldp, float* out, int64_t ldo, hipStream_t s);
+
+// Dynamic LDS above 64 KB must be allowed per kernel on each device.  One
+// LdsAllowance per kernel (a zero-initialised static) remembers, per device,
+// the largest size already allowed, so later launches cost one atomic load.
+constexpr int kMaxDevices = 64;
+struct LdsAllowance {
+  std::atomic<size_t> bytes[kMaxDevices];
+};
+hipError_t allow_dynamic_lds(const void* kernel, size_t bytes, LdsAllowance& seen);
 
 }  // namespace q3

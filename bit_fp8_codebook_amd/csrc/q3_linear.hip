@@ -902,21 +902,12 @@ size_t stream_bytes(int slice) { return 2u * slice * (1024u + kRowPad) + 1024u; 
 
 size_t reduce_bytes(int vals, int r, int w) { return (size_t)w * r * vals * 64 * 4; }
 
-// Dynamic LDS above 64 KB must be allowed per kernel; raise each kernel's limit
-// once to the largest size this file ever requests.
+// Dynamic LDS above 64 KB must be allowed per kernel and device.
 template <int NT, int R, int kW, int kGrouped, int kMode, bool kDot, int kBits>
 hipError_t allow_lds(size_t bytes) {
-  static std::atomic<size_t> allowed{64 * 1024};   // per kernel instantiation
-  if (bytes <= allowed.load(std::memory_order_acquire)) return hipSuccess;
-  const hipError_t e =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(linear_kernel<NT, R, kW, kGrouped, kMode, kDot, kBits>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) {
-    size_t cur = allowed.load(std::memory_order_acquire);
-    while (cur < bytes && !allowed.compare_exchange_weak(cur, bytes)) {
-    }
-  }
-  return e;
+  static LdsAllowance seen;   // per kernel instantiation
+  return allow_dynamic_lds(reinterpret_cast<const void*>(linear_kernel<NT, R, kW, kGrouped, kMode, kDot, kBits>),
+                           bytes, seen);
 }
 
 template <int NT, int R, int kW, int kGrouped, int kMode, bool kDot, int kBits>
@@ -935,13 +926,9 @@ template <int NT, int R>
 hipError_t launch_wide(const KArgs& a, unsigned splits, hipStream_t s) {
   constexpr int kRowsPerBlock = R * kWideWaves;
   const size_t shm = stream_bytes(16 * NT);
-  static std::atomic<bool> allowed{false};
-  if (!allowed.load(std::memory_order_acquire)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(wide_kernel<NT, R>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    if (e != hipSuccess) return e;
-    allowed.store(true, std::memory_order_release);
-  }
+  static LdsAllowance seen;
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(wide_kernel<NT, R>), shm, seen);
+  if (e != hipSuccess) return e;
   const int64_t tiles = (a.n + 15) / 16;
   const dim3 grid((unsigned)((tiles + kRowsPerBlock - 1) / kRowsPerBlock), 1, splits);
   hipLaunchKernelGGL((wide_kernel<NT, R>), grid, dim3(64 * kWideWaves), shm, s, a);

@@ -1,22 +1,23 @@
-// Library-owned scratch memory for callers that cannot allocate device memory
+// Per-device state of the library.
+//
+// Library-owned scratch memory, for callers that cannot allocate device memory
 // (code under HIP graph capture, tight serving loops, harnesses that forbid
 // hipMalloc): the fused expert MLP's intermediate buffers (the SwiGLU
 // activations and the per-pair down outputs) live in one file-scope device
-// array instead of a caller workspace.
+// array instead of a caller workspace.  Each GPU the library runs on holds its
+// own copy of the array (allocated with the code object, held until the process
+// ends); its device address is looked up once per device with
+// hipGetSymbolAddress and kept here.  Host code never passes the array's name
+// itself to a kernel or a copy: in host code that name is only a stand-in for
+// the symbol, not a device address.
 //
-// Each GPU the library runs on holds its own copy of the array (allocated with
-// the code object, held until the process ends); its device address is looked
-// up once per device with hipGetSymbolAddress and kept here.  Host code never
-// passes the array's name itself to a kernel or a copy: in host code that name
-// is only a stand-in for the symbol, not a device address.
+// The dynamic-LDS allowances of the kernels, which are per device too.
 #include <atomic>
 
 #include "q3_internal.h"
 
 namespace q3 {
 namespace {
-
-constexpr int kMaxDevices = 64;
 
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
@@ -39,6 +40,21 @@ hipError_t scratch_address(void** out) {
     g_scratch_ptr[dev].store(p, std::memory_order_release);
   }
   *out = p;
+  return hipSuccess;
+}
+
+hipError_t allow_dynamic_lds(const void* kernel, size_t bytes, LdsAllowance& seen) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool tracked = dev >= 0 && dev < kMaxDevices;
+  if (tracked && bytes <= seen.bytes[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess || !tracked) return e;
+  size_t cur = seen.bytes[dev].load(std::memory_order_acquire);
+  while (cur < bytes && !seen.bytes[dev].compare_exchange_weak(cur, bytes)) {
+  }
   return hipSuccess;
 }
 

@@ -360,15 +360,9 @@ size_t splitk_lds() {
 template <int kW, int kHS, bool kDot, int NT>
 hipError_t launch_one_split(const SplitArgs& a, hipStream_t s) {
   const size_t shm = splitk_lds<kW, kHS, kDot, NT>();
-  if (shm > 64 * 1024) {
-    static bool allowed = false;   // one attribute call per instantiation; idempotent if it races
-    if (!allowed) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(splitk_kernel<kW, kHS, kDot, NT>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-      if (e != hipSuccess) return e;
-      allowed = true;
-    }
-  }
+  static LdsAllowance seen;
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(splitk_kernel<kW, kHS, kDot, NT>), shm, seen);
+  if (e != hipSuccess) return e;
   const int64_t tiles = (a.n + 15) / 16;
   hipLaunchKernelGGL((splitk_kernel<kW, kHS, kDot, NT>), dim3((unsigned)tiles), dim3(64 * kW), shm, s, a);
   return hipGetLastError();
