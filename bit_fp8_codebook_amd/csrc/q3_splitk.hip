@@ -33,7 +33,9 @@
 //   * vector ALUs (1..8 tokens): v_dot2_f32_bf16 per token, then the four
 //     quads of a row are added with lane exchanges.
 // The waves' partial sums meet after a single block barrier and are added in
-// wave order, so results are run-to-run identical.
+// wave order, so results are run-to-run identical.  One token on the matrix
+// cores with K from 3072 up takes whole 512-k steps per wave instead
+// (splitk_full_kernel: 16-byte loads, half as many load instructions).
 #include "q3_device.h"
 #include "q3_internal.h"
 
@@ -350,6 +352,90 @@ __global__ __launch_bounds__(64 * kW) void splitk_kernel(SplitArgs a) {
   }
 }
 
+// One token on the matrix cores, whole 512-k steps: wave w takes step w of the
+// block's tile, so every lane reads its three code words and four scale bytes
+// with 16-byte and 4-byte loads (half as many load instructions as half-steps)
+// and the step's 1 KB of activations with one 16-byte load per lane.  kW waves
+// (a power of two at least the step count; waves past it load nothing and add
+// zero).
+template <int kW>
+__global__ __launch_bounds__(64 * kW) void splitk_full_kernel(SplitArgs a) {
+  extern __shared__ __align__(16) uint8_t lds[];   // kW x 1 KB activations, then kW x 16 partial sums
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15, kb = lane >> 4;
+  const uint32_t gp = (uint32_t)a.G;                // a multiple of 16 here
+  const int steps = (int)(gp / 16);
+  const int64_t tiles = (a.n + 15) / 16;
+  const int64_t T = blockIdx.x;
+  const bool live = wave < steps;
+  const rsrc_t cr = make_rsrc(a.code, (uint32_t)(tiles * 192 * gp));
+  const rsrc_t sr = make_rsrc(a.scale, (uint32_t)(tiles * 16 * gp));
+  const rsrc_t cbr = make_rsrc(a.cb, (uint32_t)(a.n * 8));
+  const rsrc_t xr = make_rsrc(a.x, (uint32_t)((int64_t)a.G * 64));
+  uint8_t* const xw = lds + wave * 1024u;
+
+  // Activations first (lane l: bytes 16l..16l+15 of the step), then the weights.
+  const u32x4 xin = bload128(xr, live ? 1024u * (uint32_t)wave + 16u * lane : kOob);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint32_t base = live ? (uint32_t)T * 192u * gp + 3072u * (uint32_t)wave + 16u * lane : kOob;
+  const u32x4 w0 = bload128_stream(cr, base), w1 = bload128_stream(cr, base + 1024u),
+              w2 = bload128_stream(cr, base + 2048u);
+  const uint32_t sc = bload32_stream(sr, live ? (uint32_t)T * 16u * gp + 256u * (uint32_t)wave + 4u * lane : kOob);
+  const int64_t row = T * 16 + i;
+  const u32x2 cbv = bload64(cbr, row < a.n ? (uint32_t)row * 8u : kOob);
+  *reinterpret_cast<u32x4*>(xw + 16u * lane) = xin;
+  __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order: its own stores are read next
+
+  // Lane (i, kb) holds group t of quad kb for row i; its activations sit at
+  // 256 kb + 64 t of the step.  B is token 0's activations in every lane
+  // (columns 1..15 repeat column 0 and are dropped).
+  f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    u32x4 xv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xv[e] = *reinterpret_cast<const u32x4*>(xw + 256u * kb + 64u * t + 16u * e);
+    bf16x2 wv[16];
+    dequant_group_bf16(w0[t], w1[t], w2[t], (sc >> (8 * t)) & 0xFFu, cbv.x, cbv.y, wv);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const u32x4 au = {__builtin_bit_cast(uint32_t, wv[4 * e]), __builtin_bit_cast(uint32_t, wv[4 * e + 1]),
+                        __builtin_bit_cast(uint32_t, wv[4 * e + 2]), __builtin_bit_cast(uint32_t, wv[4 * e + 3])};
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, au), __builtin_bit_cast(bf16x8, xv[e]), d,
+                                                  0, 0, 0);
+    }
+  }
+  // Row sums of column 0 into lanes 0..15 (lane 16*(r/4) holds rows 4*(r/4)..+3),
+  // then the waves' sums in wave order.
+  float r = 0.f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float dv = __shfl(d[v], 16 * (i >> 2), 64);
+    if ((i & 3) == v) r = dv;
+  }
+  float* const red = reinterpret_cast<float*>(lds + kW * 1024u);
+  if (lane < 16) red[wave * 16 + lane] = r;
+  __syncthreads();
+  if (wave == 0 && lane < 16) {
+    float v = red[lane];
+#pragma unroll
+    for (int q = 1; q < kW; ++q) v += red[q * 16 + lane];
+    if (row < a.n) {
+      if (a.y_rsrc) store_y1(a.y, a.ldy, a.n, 1, row, v);
+      else a.y[row] = v;
+    }
+  }
+}
+
+template <int kW>
+hipError_t launch_full(const SplitArgs& a, hipStream_t s) {
+  const size_t shm = (size_t)kW * (1024 + 64);
+  const int64_t tiles = (a.n + 15) / 16;
+  hipLaunchKernelGGL(splitk_full_kernel<kW>, dim3((unsigned)tiles), dim3(64 * kW), shm, s, a);
+  return hipGetLastError();
+}
+
 template <int kW, int kHS, bool kDot, int NT>
 size_t splitk_lds() {
   constexpr int kTok = NT;
@@ -366,6 +452,21 @@ hipError_t launch_one_split(const SplitArgs& a, hipStream_t s) {
   const int64_t tiles = (a.n + 15) / 16;
   hipLaunchKernelGGL((splitk_kernel<kW, kHS, kDot, NT>), dim3((unsigned)tiles), dim3(64 * kW), shm, s, a);
   return hipGetLastError();
+}
+
+// Whole steps per wave for one token on the matrix cores where that measured
+// faster than half-steps on MI355X (graph-replayed launches over cold copies):
+// from K = 3072 up (K = 4096, N = 8192: 5.09 -> 4.65 us; K = 8192, N = 4096:
+// 5.21 -> 4.76 us; K = 6144, N = 4096: 5.04 -> 4.58 us), except K = 4096 with
+// 224..256 row tiles (one 16-wave half-step block per CU), where half-steps
+// were as fast or 1% faster; at K <= 2048 half-steps were as fast or faster.
+// Only matrices of whole steps (K % 512 == 0).
+bool use_full_steps(int64_t n, int groups, int64_t m, bool dot) {
+  if (dot || m != 1 || groups % 16 != 0) return false;
+  const int steps = groups / 16;
+  const int64_t tiles = (n + 15) / 16;
+  if (steps <= 4 || steps > kSplitMaxWaves) return false;
+  return !(steps == 8 && tiles >= 224 && tiles <= 256);
 }
 
 // Waves per block and half-steps per wave for a matrix of `groups` groups per
@@ -429,6 +530,11 @@ hipError_t launch_splitk(const PlaneView& w, const uint16_t* x, int64_t m, int64
   a.ldy = ldy;
   a.vec_y = ((uintptr_t)y % 16 == 0) && (ldy % 4 == 0);
   a.y_rsrc = ((m - 1) * ldy + w.n) * 4 < (int64_t(1) << 31);
+  if (use_full_steps(w.n, w.groups, m, dot)) {
+    const int steps = w.groups / 16;
+    if (steps <= 8) return launch_full<8>(a, s);
+    return launch_full<16>(a, s);
+  }
   const SplitShape sh = split_shape(w.groups);
   if (sh.hs == 1) {
     switch (sh.w) {

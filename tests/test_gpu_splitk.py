@@ -3,7 +3,8 @@ block per 16-row tile, K dealt out to up to 16 waves in half-steps of 8 groups
 per quad): every output against the oracle, |y - y_ref| <= 1e-3 * sum|x w|.
 
 The cases span every wave count (2, 4, 8, 16 waves: K = 32..4096), two
-half-steps per wave (K above 4096, up to 8 tokens), last steps holding 1, 2
+half-steps per wave (K above 4096, up to 8 tokens), one token with whole
+steps per wave (K from 3072 up, with waves past the last step), last steps holding 1, 2
 or 3 quads (K % 512 != 0), ragged row counts, the 512-tile boundary (the next
 matrix takes the earlier kernels), 1..16 tokens on the matrix cores and one
 token on the vector ALUs, strided and unaligned operands, run-to-run
@@ -38,6 +39,9 @@ CASES = [
     (8192, 4096, 1), (8192, 4096, 16),                    # 512 tiles: the largest the kernel takes
     (8193, 4096, 1),                                      # 513 tiles: earlier kernels
     (1, 4096, 1), (17, 4096, 16),
+    # one token on the matrix cores, whole steps per wave (K >= 3072, K % 512 == 0)
+    (3000, 3072, 1), (2048, 4096, 1), (4608, 4096, 1), (5000, 6144, 1), (100, 8192, 1), (17, 5120, 1),
+    (3584, 4096, 1), (4097, 4096, 1),                     # 224 and 257 tiles: either side of the half-step range
 ]
 
 
@@ -52,11 +56,12 @@ def test_splitk_parity(q3, n, k, m):
         assert_close(q3.q3_gemv(w, xd).cpu().numpy(), y_ref, bound, f"vector ALUs n={n} k={k} m={m}")
 
 
-@pytest.mark.parametrize("m", [1, 3, 16])
-def test_splitk_strided_and_unaligned(q3, m):
+@pytest.mark.parametrize("m,k", [(1, 4096), (3, 4096), (16, 4096), (1, 3072)])
+def test_splitk_strided_and_unaligned(q3, m, k):
     # x rows 4160 elements apart; y rows 4101 floats apart starting one float
-    # into the buffer, so outputs leave one by one.
-    n, k = 4096, 4096
+    # into the buffer, so outputs leave one by one.  K = 3072 at one token
+    # takes whole steps per wave.
+    n = 4096
     layer, x = synth.make_linear(n, k, m, seed=40 + m)
     w = pack_layer(q3, layer)
     xbig = torch.zeros((m, 4160), dtype=torch.int16, device="cuda")
@@ -85,6 +90,13 @@ def test_splitk_deterministic(q3):
     g1 = q3.q3_gemv(w, xd[:1]).cpu().numpy()
     g2 = q3.q3_gemv(w, xd[:1]).cpu().numpy()
     assert np.array_equal(g1.view(np.uint32), g2.view(np.uint32))
+    # one token, whole steps per wave
+    layer, x = synth.make_linear(2048, 8192, 1, seed=92)
+    w = pack_layer(q3, layer)
+    xd = dev(x)
+    f1 = q3.q3_gemm_small_m(w, xd).cpu().numpy()
+    f2 = q3.q3_gemm_small_m(w, xd).cpu().numpy()
+    assert np.array_equal(f1.view(np.uint32), f2.view(np.uint32))
 
 
 def test_splitk_needs_no_workspace(q3):
