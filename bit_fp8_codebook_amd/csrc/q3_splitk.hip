@@ -48,6 +48,7 @@ constexpr int64_t kSplitMaxTiles = Q3_SPLITK_MAX_TILES;
 #else
 constexpr int64_t kSplitMaxTiles = 512;
 #endif
+constexpr int64_t kFullMaxTiles = 1536;        // one token on whole steps (K = 4096 or 8192)
 constexpr uint32_t kHalfStepBytes = 512;   // activations of one token over one half-step (4 quads x 128 B)
 
 struct SplitArgs {
@@ -506,10 +507,20 @@ hipError_t launch_split_w(const SplitArgs& a, bool dot, hipStream_t s) {
 // The split-K kernel takes dense products of up to 16 tokens (one on the vector
 // ALUs) on matrices of at most 512 row tiles and K up to 16384 (at most
 // two half-steps per wave, then at most 8 tokens: the activations of every
-// half-step are staged at once).
+// half-step are staged at once), and one token on the matrix cores with whole
+// steps on matrices of up to 1536 row tiles at K = 4096 or 8192.
 bool splitk_applies(int64_t n, int groups, int64_t m, bool dot) {
   if (n < 1 || m < 1 || m > (dot ? 1 : 16)) return false;
-  if ((n + 15) / 16 > kSplitMaxTiles) return false;
+  const int64_t tiles = (n + 15) / 16;
+  if (tiles > kSplitMaxTiles) {
+    // One token on whole steps also beats the tall kernel up to 1536 row tiles
+    // when the steps fill the block's waves (K = 4096 or 8192), measured:
+    // 11008 x 4096 6.97 -> 5.49 us, 16384 x 4096 10.27 -> 7.08 us, 24576 x 4096
+    // 10.66 -> 9.84 us, 12288 x 8192 11.45 -> 10.12 us, 16384 x 8192 17.12 ->
+    // 12.53 us; from 1792 tiles (28672 x 8192: 18.2 vs 18.8 us) it does not.
+    const int steps = groups / 16;
+    return tiles <= kFullMaxTiles && (steps == 8 || steps == 16) && use_full_steps(n, groups, m, dot);
+  }
   const SplitShape sh = split_shape(groups);
   return sh.hs == 1 || (sh.hs == 2 && m <= 8);
 }

@@ -4,7 +4,8 @@ per quad): every output against the oracle, |y - y_ref| <= 1e-3 * sum|x w|.
 
 The cases span every wave count (2, 4, 8, 16 waves: K = 32..4096), two
 half-steps per wave (K above 4096, up to 8 tokens), one token with whole
-steps per wave (K from 3072 up, with waves past the last step), last steps holding 1, 2
+steps per wave (K from 3072 up, with waves past the last step; up to 1536
+row tiles at K = 4096 and 8192, and the first matrices past each limit), last steps holding 1, 2
 or 3 quads (K % 512 != 0), ragged row counts, the 512-tile boundary (the next
 matrix takes the earlier kernels), 1..16 tokens on the matrix cores and one
 token on the vector ALUs, strided and unaligned operands, run-to-run
@@ -42,6 +43,8 @@ CASES = [
     # one token on the matrix cores, whole steps per wave (K >= 3072, K % 512 == 0)
     (3000, 3072, 1), (2048, 4096, 1), (4608, 4096, 1), (5000, 6144, 1), (100, 8192, 1), (17, 5120, 1),
     (3584, 4096, 1), (4097, 4096, 1),                     # 224 and 257 tiles: either side of the half-step range
+    # one token, whole steps, past 512 tiles (K = 4096 or 8192, up to 1536 tiles)
+    (11008, 4096, 1), (16385, 4096, 1), (24576, 4096, 1), (24577, 4096, 1), (12288, 8192, 1), (9000, 6144, 1),
 ]
 
 
