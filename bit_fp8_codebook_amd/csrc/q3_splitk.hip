@@ -353,15 +353,15 @@ __global__ __launch_bounds__(64 * kW) void splitk_kernel(SplitArgs a) {
   }
 }
 
-// One token on the matrix cores, whole 512-k steps: wave w takes step w of the
-// block's tile, so every lane reads its three code words and four scale bytes
-// with 16-byte and 4-byte loads (half as many load instructions as half-steps)
-// and the step's 1 KB of activations with one 16-byte load per lane.  kW waves
-// (a power of two at least the step count; waves past it load nothing and add
-// zero).
-template <int kW>
+// One token on the matrix cores, whole 512-k steps: wave w takes steps w,
+// w + kW, ... (kSPW of them) of the block's tile, so every lane reads its
+// three code words and four scale bytes per step with 16-byte and 4-byte loads
+// (half as many load instructions as half-steps) and each step's 1 KB of
+// activations with one 16-byte load per lane.  kW * kSPW covers the step count;
+// steps past it load nothing and add zero.
+template <int kW, int kSPW>
 __global__ __launch_bounds__(64 * kW) void splitk_full_kernel(SplitArgs a) {
-  extern __shared__ __align__(16) uint8_t lds[];   // kW x 1 KB activations, then kW x 16 partial sums
+  extern __shared__ __align__(16) uint8_t lds[];   // kW x kSPW KB activations, then kW x 16 partial sums
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15, kb = lane >> 4;
@@ -369,23 +369,35 @@ __global__ __launch_bounds__(64 * kW) void splitk_full_kernel(SplitArgs a) {
   const int steps = (int)(gp / 16);
   const int64_t tiles = (a.n + 15) / 16;
   const int64_t T = blockIdx.x;
-  const bool live = wave < steps;
   const rsrc_t cr = make_rsrc(a.code, (uint32_t)(tiles * 192 * gp));
   const rsrc_t sr = make_rsrc(a.scale, (uint32_t)(tiles * 16 * gp));
   const rsrc_t cbr = make_rsrc(a.cb, (uint32_t)(a.n * 8));
   const rsrc_t xr = make_rsrc(a.x, (uint32_t)((int64_t)a.G * 64));
-  uint8_t* const xw = lds + wave * 1024u;
+  uint8_t* const xw = lds + wave * (1024u * kSPW);
 
-  // Activations first (lane l: bytes 16l..16l+15 of the step), then the weights.
-  const u32x4 xin = bload128(xr, live ? 1024u * (uint32_t)wave + 16u * lane : kOob);
+  // Activations first (lane l: bytes 16l..16l+15 of each of its steps), then the weights.
+  u32x4 xin[kSPW];
+#pragma unroll
+  for (int u = 0; u < kSPW; ++u) {
+    const int st = wave + kW * u;
+    xin[u] = bload128(xr, st < steps ? 1024u * (uint32_t)st + 16u * lane : kOob);
+  }
   __builtin_amdgcn_sched_barrier(0);
-  const uint32_t base = live ? (uint32_t)T * 192u * gp + 3072u * (uint32_t)wave + 16u * lane : kOob;
-  const u32x4 w0 = bload128_stream(cr, base), w1 = bload128_stream(cr, base + 1024u),
-              w2 = bload128_stream(cr, base + 2048u);
-  const uint32_t sc = bload32_stream(sr, live ? (uint32_t)T * 16u * gp + 256u * (uint32_t)wave + 4u * lane : kOob);
+  u32x4 w0[kSPW], w1[kSPW], w2[kSPW];
+  uint32_t sc[kSPW];
+#pragma unroll
+  for (int u = 0; u < kSPW; ++u) {
+    const int st = wave + kW * u;
+    const uint32_t base = st < steps ? (uint32_t)T * 192u * gp + 3072u * (uint32_t)st + 16u * lane : kOob;
+    w0[u] = bload128_stream(cr, base);
+    w1[u] = bload128_stream(cr, base + 1024u);
+    w2[u] = bload128_stream(cr, base + 2048u);
+    sc[u] = bload32_stream(sr, st < steps ? (uint32_t)T * 16u * gp + 256u * (uint32_t)st + 4u * lane : kOob);
+  }
   const int64_t row = T * 16 + i;
   const u32x2 cbv = bload64(cbr, row < a.n ? (uint32_t)row * 8u : kOob);
-  *reinterpret_cast<u32x4*>(xw + 16u * lane) = xin;
+#pragma unroll
+  for (int u = 0; u < kSPW; ++u) *reinterpret_cast<u32x4*>(xw + 1024u * u + 16u * lane) = xin[u];
   __builtin_amdgcn_wave_barrier();   // a wave's LDS accesses complete in order: its own stores are read next
 
   // Lane (i, kb) holds group t of quad kb for row i; its activations sit at
@@ -393,20 +405,23 @@ __global__ __launch_bounds__(64 * kW) void splitk_full_kernel(SplitArgs a) {
   // (columns 1..15 repeat column 0 and are dropped).
   f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    u32x4 xv[4];
+  for (int u = 0; u < kSPW; ++u)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) xv[e] = *reinterpret_cast<const u32x4*>(xw + 256u * kb + 64u * t + 16u * e);
-    bf16x2 wv[16];
-    dequant_group_bf16(w0[t], w1[t], w2[t], (sc >> (8 * t)) & 0xFFu, cbv.x, cbv.y, wv);
+    for (int t = 0; t < 4; ++t) {
+      u32x4 xv[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const u32x4 au = {__builtin_bit_cast(uint32_t, wv[4 * e]), __builtin_bit_cast(uint32_t, wv[4 * e + 1]),
-                        __builtin_bit_cast(uint32_t, wv[4 * e + 2]), __builtin_bit_cast(uint32_t, wv[4 * e + 3])};
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, au), __builtin_bit_cast(bf16x8, xv[e]), d,
-                                                  0, 0, 0);
+      for (int e = 0; e < 4; ++e)
+        xv[e] = *reinterpret_cast<const u32x4*>(xw + 1024u * u + 256u * kb + 64u * t + 16u * e);
+      bf16x2 wv[16];
+      dequant_group_bf16(w0[u][t], w1[u][t], w2[u][t], (sc[u] >> (8 * t)) & 0xFFu, cbv.x, cbv.y, wv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const u32x4 au = {__builtin_bit_cast(uint32_t, wv[4 * e]), __builtin_bit_cast(uint32_t, wv[4 * e + 1]),
+                          __builtin_bit_cast(uint32_t, wv[4 * e + 2]), __builtin_bit_cast(uint32_t, wv[4 * e + 3])};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, au), __builtin_bit_cast(bf16x8, xv[e]),
+                                                    d, 0, 0, 0);
+      }
     }
-  }
   // Row sums of column 0 into lanes 0..15 (lane 16*(r/4) holds rows 4*(r/4)..+3),
   // then the waves' sums in wave order.
   float r = 0.f;
@@ -415,7 +430,7 @@ __global__ __launch_bounds__(64 * kW) void splitk_full_kernel(SplitArgs a) {
     const float dv = __shfl(d[v], 16 * (i >> 2), 64);
     if ((i & 3) == v) r = dv;
   }
-  float* const red = reinterpret_cast<float*>(lds + kW * 1024u);
+  float* const red = reinterpret_cast<float*>(lds + kW * kSPW * 1024u);
   if (lane < 16) red[wave * 16 + lane] = r;
   __syncthreads();
   if (wave == 0 && lane < 16) {
@@ -429,11 +444,11 @@ __global__ __launch_bounds__(64 * kW) void splitk_full_kernel(SplitArgs a) {
   }
 }
 
-template <int kW>
+template <int kW, int kSPW>
 hipError_t launch_full(const SplitArgs& a, hipStream_t s) {
-  const size_t shm = (size_t)kW * (1024 + 64);
+  const size_t shm = (size_t)kW * (1024 * kSPW + 64);
   const int64_t tiles = (a.n + 15) / 16;
-  hipLaunchKernelGGL(splitk_full_kernel<kW>, dim3((unsigned)tiles), dim3(64 * kW), shm, s, a);
+  hipLaunchKernelGGL((splitk_full_kernel<kW, kSPW>), dim3((unsigned)tiles), dim3(64 * kW), shm, s, a);
   return hipGetLastError();
 }
 
@@ -543,8 +558,13 @@ hipError_t launch_splitk(const PlaneView& w, const uint16_t* x, int64_t m, int64
   a.y_rsrc = ((m - 1) * ldy + w.n) * 4 < (int64_t(1) << 31);
   if (use_full_steps(w.n, w.groups, m, dot)) {
     const int steps = w.groups / 16;
-    if (steps <= 8) return launch_full<8>(a, s);
-    return launch_full<16>(a, s);
+    if (steps <= 8) return launch_full<8, 1>(a, s);
+    // K = 8192 past 1024 row tiles: 8-wave blocks of two steps per wave (four
+    // blocks per CU instead of two), measured 18.3 -> 17.0 us at 24576 x 8192
+    // and 15.2 -> 14.7 us at 20480 x 8192; at 1024 tiles and fewer the 16-wave
+    // blocks were faster.
+    if ((w.n + 15) / 16 > 1024) return launch_full<8, 2>(a, s);
+    return launch_full<16, 1>(a, s);
   }
   const SplitShape sh = split_shape(w.groups);
   if (sh.hs == 1) {

@@ -45,6 +45,7 @@ CASES = [
     (3584, 4096, 1), (4097, 4096, 1),                     # 224 and 257 tiles: either side of the half-step range
     # one token, whole steps, past 512 tiles (K = 4096 or 8192, up to 1536 tiles)
     (11008, 4096, 1), (16385, 4096, 1), (24576, 4096, 1), (24577, 4096, 1), (12288, 8192, 1), (9000, 6144, 1),
+    (16400, 8192, 1), (24576, 8192, 1),                   # K = 8192 past 1024 tiles: two steps per wave
 ]
 
 
