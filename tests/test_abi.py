@@ -97,6 +97,9 @@ def test_gemm_small_m_workspace_sizes(q3lib):
     assert ws(4096, 4096, 64) == 4 * 64 * 4096 * 4
     assert ws(8192, 28672, 16) == 4 * 16 * 8192 * 4
     assert ws(8192, 28672, 64) == 2 * 64 * 8192 * 4
+    # one token on whole steps past 512 row tiles (K = 4096, 8192, up to 1536 tiles): the split-K kernel
+    assert ws(24576, 8192, 1) == 0
+    assert ws(24576, 4096, 1) == 0
     # invalid shapes report no workspace
     assert ws(4096, 4096, 65) == 0
     assert ws(4096, 4100, 16) == 0

@@ -107,6 +107,7 @@ def test_splitk_needs_no_workspace(q3):
     # The workspace entry point reports no workspace for shapes this kernel takes.
     assert q3.q3_gemm_small_m_workspace_bytes(4096, 4096, 16) == 0
     assert q3.q3_gemm_small_m_workspace_bytes(4096, 8192, 8) == 0
+    assert q3.q3_gemm_small_m_workspace_bytes(24576, 8192, 1) == 0      # whole steps past 512 tiles
     layer, x = synth.make_linear(2048, 2048, 6, seed=3)
     w = pack_layer(q3, layer)
     y_ref, bound = oracle_linear(layer, x)
