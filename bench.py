@@ -554,6 +554,10 @@ def main():
                     help="time only the K=4096 N=151936 M=64 point (for counter runs of its kernel) and print it")
     ap.add_argument("--only-moe", action="store_true",
                     help="time only the plain MoE verify round (for counter runs of the expert passes) and print it")
+    ap.add_argument("--only-layer", action="store_true",
+                    help="time only the 4096x4096 M=1 layer on the matrix cores (counter runs) and print it")
+    ap.add_argument("--only-stream", action="store_true",
+                    help="time only the K=8192 N=28672 M=1 stream on the matrix cores (counter runs) and print it")
     ap.add_argument("--reps", type=int, default=0, help="graph replays per trial for every point (profiler runs)")
     ap.add_argument("--trials", type=int, default=TRIALS, help="trials per point (median reported)")
     args = ap.parse_args()
@@ -586,6 +590,11 @@ def main():
         return
     if args.only_moe:
         print(json.dumps(moe_point(q3, synth, reps=args.steps, warmup=args.warmup)), flush=True)
+        return
+    if args.only_layer or args.only_stream:
+        n_, k_ = (4096, 4096) if args.only_layer else (28672, 8192)
+        print(json.dumps(linear_point(q3, synth, n_, k_, 1, "mfma", reps=args.steps, warmup=args.warmup,
+                                      name=f"K={k_} N={n_} M=1")), flush=True)
         return
 
     n = k = 4096
