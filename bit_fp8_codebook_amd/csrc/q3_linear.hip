@@ -1058,9 +1058,16 @@ hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t
   const Shape sh = kGrouped ? Shape{kGrouped == kSwiGLU ? 2 : 1, kExpertWaves, kExpertSplitK}
                             : pick_shape(a.n, a.G, full_k, tokens_in_slice, kDot);
   a.sk = full_k ? sh.sk : 1;
+  // Streamed activations in one pass on fewer than 1536 row tiles: 4-wave
+  // blocks, twice as many as with 8 (measured: 8192 x 28672 at 16 tokens
+  // 65.0 -> 49.7 us, 14336 x 8192 21.6 -> 16.9 us, 4096 x 8192 20.8 -> 15.9 us;
+  // 28672 x 8192 the same either way).  Products split over blocks keep the
+  // 8-wave blocks their split count was planned for.
+  Shape shape = sh;
+  if (!kGrouped && !full_k && splits == 1 && (a.n + 15) / 16 < 1536) shape.w = 4;
   const int steps = (((a.G + 3) & ~3) + 15) / 16;
   while (a.sk > 1 && a.sk > steps) a.sk /= 2;   // every wave gets at least one step
-  if (a.sk < 1 || a.sk > sh.w || sh.w % a.sk != 0) return hipErrorInvalidValue;
+  if (a.sk < 1 || a.sk > shape.w || shape.w % a.sk != 0) return hipErrorInvalidValue;
   const int mode = full_k ? kShared : kStream;
 #ifndef Q3_NO_WIDE
   // Two or more column tiles of streamed activations on whole steps: the wide
@@ -1073,17 +1080,17 @@ hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t
   if (mode == kShared) splits = 1;
   size_t shm = mode == kShared ? fk : stream_bytes(kSlice);
   if (mode != kStream && a.sk > 1) {
-    const size_t red = reduce_bytes(kDot ? NT : 4 * NT, sh.r, sh.w);
+    const size_t red = reduce_bytes(kDot ? NT : 4 * NT, shape.r, shape.w);
     if (shm < red) shm = red;
   }
   if constexpr (kGrouped == kSwiGLU) {
-    return launch_r<NT, 2, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, 1, s);
+    return launch_r<NT, 2, kGrouped, kDot, kBits>(a, shape.w, mode, shm, grid_y, 1, s);
   } else if constexpr (kGrouped || kDot) {
-    return launch_r<NT, 1, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, splits, s);
+    return launch_r<NT, 1, kGrouped, kDot, kBits>(a, shape.w, mode, shm, grid_y, splits, s);
   } else {
-    switch (sh.r) {
-      case 1: return launch_r<NT, 1, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, splits, s);
-      case 2: return launch_r<NT, 2, kGrouped, kDot, kBits>(a, sh.w, mode, shm, grid_y, splits, s);
+    switch (shape.r) {
+      case 1: return launch_r<NT, 1, kGrouped, kDot, kBits>(a, shape.w, mode, shm, grid_y, splits, s);
+      case 2: return launch_r<NT, 2, kGrouped, kDot, kBits>(a, shape.w, mode, shm, grid_y, splits, s);
       default: return hipErrorInvalidValue;
     }
   }

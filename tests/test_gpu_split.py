@@ -58,6 +58,19 @@ def test_split_parity_down_projection_sampled_rows(q3, n, k, m):
     rows = np.sort(np.concatenate([np.random.default_rng(m).choice(n, 120, replace=False), [0, 15, 16, n - 1]]))
     y_ref, bound = oracle_linear(layer, x, rows=rows)
     assert_close(y[:, rows], y_ref, bound, f"down projection m={m}")
+    # the one-pass product (no workspace) on the same shape
+    y1 = q3.q3_gemm_small_m(w, dev(x)).cpu().numpy()
+    assert_close(y1[:, rows], y_ref, bound, f"down projection one pass m={m}")
+
+
+@pytest.mark.parametrize("n,k,m", [(1000, 9216, 8), (520, 24576, 3), (4096, 28672, 4)])
+def test_vector_alu_streamed_activations(q3, n, k, m):
+    """q3_gemv with activations too large to stage whole in LDS (streamed one
+    512-k step at a time), on matrices with few row tiles."""
+    layer, x = synth.make_linear(n, k, m, seed=7 * n + m)
+    w = pack_layer(q3, layer)
+    y_ref, bound = oracle_linear(layer, x)
+    assert_close(q3.q3_gemv(w, dev(x)).cpu().numpy(), y_ref, bound, f"gemv streamed n={n} k={k} m={m}")
 
 
 def test_split_deterministic_and_workspace_contents_irrelevant(q3):
