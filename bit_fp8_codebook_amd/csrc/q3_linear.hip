@@ -1073,8 +1073,10 @@ hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t
   // Two or more column tiles of streamed activations on whole steps: the wide
   // kernel (one wave per SIMD, many row tiles, activations loaded into LDS).
   if constexpr (!kGrouped && !kDot && kBits == 3 && NT >= kWideMinNT) {
-    if (mode == kStream && a.G % 16 == 0)
+    if (mode == kStream && a.G % 16 == 0) {
+      if (wide_rows == 1) return launch_wide<NT, 1>(a, splits, s);
       return wide_rows == 2 ? launch_wide<NT, 2>(a, splits, s) : launch_wide<NT, 5>(a, splits, s);
+    }
   }
 #endif
   if (mode == kShared) splits = 1;
@@ -1138,7 +1140,7 @@ KArgs base_args(const PlaneView& w) {
 #define Q3_SPLIT_MIN_STEPS 2
 #endif
 struct SmallMPlan {
-  int wide_rows;   // row tiles per wave of the wide kernel
+  int wide_rows;   // row tiles per wave of the wide kernel (1, 2 or 5)
   int splits;      // K splits over blocks
 };
 
@@ -1158,6 +1160,14 @@ SmallMPlan plan_small_m(int64_t n, int groups, int64_t m) {
     // nearly empty round (N = 65536: 46 vs 50 us; N = 98304: 89 vs 74 us).
     const int64_t rounds5 = ((tiles + 19) / 20 + 255) / 256, rounds2 = ((tiles + 7) / 8 + 255) / 256;
     if (rounds2 * 50 < rounds5 * 90) pl.wide_rows = 2;
+    // 512..1535 row tiles at K <= 4096: one row tile per wave (a grid of 128
+    // blocks and more) in one pass beats two tiles per wave split over blocks
+    // (8192 x 4096 at 64 tokens: 17.7 -> 16.0 us; 12288 x 4096: 19.2 -> 16.4 us).
+    // At K = 8192 the splits pay more (8192 x 8192: 25.4 us split, 27.0 in one pass).
+    if (tiles >= 512 && tiles < 1536 && groups <= 128) {
+      pl.wide_rows = 1;
+      return pl;
+    }
     blocks = (tiles + 4 * pl.wide_rows - 1) / (4 * pl.wide_rows);
     target = Q3_SPLIT_TARGET_WIDE;
   } else {
@@ -1196,6 +1206,11 @@ hipError_t launch_gemm_small_m(const PlaneView& w, const uint16_t* x, int64_t m,
   SmallMPlan pl = plan_small_m(w.n, w.groups, m);
   const int64_t need = pl.splits > 1 ? (int64_t)pl.splits * m * w.n * 4 : 0;
   if (pl.splits > 1 && (ws == nullptr || ws_bytes < need)) pl.splits = 1;   // no workspace: one pass
+  // A wide product in one pass on fewer than 1536 row tiles: one row tile per
+  // wave, twice the grid of two (4096 x 4096 at 64 tokens 20.9 -> 15.8 us, at
+  // 32 tokens 14.8 -> 11.7 us; 4096 x 8192 at 64 tokens 36.4 -> 26.7 us; at
+  // 1792 tiles two tiles per wave stay faster, 28672 x 8192: 39.8 vs 53.8 us).
+  if (pl.splits == 1 && pl.wide_rows == 2 && (w.n + 15) / 16 < 1536) pl.wide_rows = 1;
   if (pl.splits > 1) {
     a.y = static_cast<float*>(ws);
     a.ldy = w.n;

@@ -97,6 +97,10 @@ def test_gemm_small_m_workspace_sizes(q3lib):
     assert ws(4096, 4096, 64) == 4 * 64 * 4096 * 4
     assert ws(8192, 28672, 16) == 4 * 16 * 8192 * 4
     assert ws(8192, 28672, 64) == 2 * 64 * 8192 * 4
+    # 17..64 tokens on 512..1535 row tiles at K <= 4096: one pass, one row tile per wave
+    assert ws(8192, 4096, 64) == 0
+    assert ws(12000, 4096, 40) == 0
+    assert ws(8192, 8192, 64) == 2 * 64 * 8192 * 4
     # one token on whole steps past 512 row tiles (K = 4096, 8192, up to 1536 tiles): the split-K kernel
     assert ws(24576, 8192, 1) == 0
     assert ws(24576, 4096, 1) == 0

@@ -155,3 +155,18 @@ def test_wide_five_row_tiles_sampled_rows(q3, n, k, m, split):
     rows = np.sort(np.concatenate([rng.choice(n, 120, replace=False), [0, 15, 16, 319, 320, n - 1]]))
     y_ref, bound = oracle_linear(layer, x, rows=rows)
     assert_close(y[:, rows], y_ref, bound, f"n={n} k={k} m={m}")
+
+
+@pytest.mark.parametrize("n,k,m", [(8192, 4096, 64), (12000, 4096, 40), (20000, 2048, 17)])
+def test_wide_one_row_tile_per_wave(q3, n, k, m):
+    """512..1535 row tiles at K <= 4096 with 17..64 tokens: one row tile per wave
+    of the wide kernel, in one pass through both entry points (sampled rows)."""
+    assert splits_of(q3, n, k, m) == 1
+    layer, x = synth.make_linear(n, k, m, seed=3 * n + m)
+    w = pack_layer(q3, layer)
+    xd = dev(x)
+    rows = np.sort(np.concatenate([np.random.default_rng(n).choice(n, 200, replace=False), [0, 15, 16, n - 1]]))
+    y_ref, bound = oracle_linear(layer, x, rows=rows)
+    assert_close(q3.q3_gemm_small_m(w, xd).cpu().numpy()[:, rows], y_ref, bound, f"one pass n={n} k={k} m={m}")
+    assert_close(q3.q3_gemm_small_m_ws(w, xd).cpu().numpy()[:, rows], y_ref, bound, f"workspace n={n} k={k} m={m}")
+
