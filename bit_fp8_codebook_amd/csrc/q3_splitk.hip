@@ -30,7 +30,7 @@
 //     in lane (i, kb) -- lanes past the tokens repeat the last one, whose
 //     extra output columns are dropped -- so one instruction stream serves any
 //     token count up to 16;
-//   * vector ALUs (1..8 tokens): v_dot2_f32_bf16 per token, then the four
+//   * vector ALUs (1..4 tokens): v_dot2_f32_bf16 per token, then the four
 //     quads of a row are added with lane exchanges.
 // The waves' partial sums meet after a single block barrier and are added in
 // wave order, so results are run-to-run identical.  One token on the matrix
@@ -511,22 +511,39 @@ hipError_t launch_split_w(const SplitArgs& a, bool dot, hipStream_t s) {
     if constexpr (kHS == 1) return launch_one_split<kW, kHS, false, 16>(a, s);
     return hipErrorInvalidValue;
   }
-  switch (a.m) {
-    case 1: return launch_one_split<kW, kHS, true, 1>(a, s);
-    default: return hipErrorInvalidValue;
+  if constexpr (kHS == 1) {
+    switch (a.m) {
+      case 1: return launch_one_split<kW, kHS, true, 1>(a, s);
+      case 2: return launch_one_split<kW, kHS, true, 2>(a, s);
+      case 3: return launch_one_split<kW, kHS, true, 3>(a, s);
+      case 4: return launch_one_split<kW, kHS, true, 4>(a, s);
+      default: return hipErrorInvalidValue;
+    }
   }
+  if (a.m == 1) return launch_one_split<kW, kHS, true, 1>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// The split-K kernel takes dense products of up to 16 tokens (one on the vector
-// ALUs) on matrices of at most 512 row tiles and K up to 16384 (at most
+// The split-K kernel takes dense products of up to 16 tokens (up to 4 on the
+// vector ALUs, on at most 256 row tiles past one) on matrices of at most 512 row tiles and K up to 16384 (at most
 // two half-steps per wave, then at most 8 tokens: the activations of every
 // half-step are staged at once), and one token on the matrix cores with whole
 // steps on matrices of up to 1536 row tiles at K = 4096 or 8192.
 bool splitk_applies(int64_t n, int groups, int64_t m, bool dot) {
-  if (n < 1 || m < 1 || m > (dot ? 1 : 16)) return false;
+  if (n < 1 || m < 1 || m > (dot ? 4 : 16)) return false;
   const int64_t tiles = (n + 15) / 16;
+  if (dot && m > 1) {
+    // 2..4 tokens on the vector ALUs, one half-step per wave, on matrices of
+    // at most 256 row tiles, measured against the stream kernel: 4096 x 4096 at
+    // 2 and 3 tokens 5.35 -> 4.15 and 6.02 -> 4.55 us, 2048 x 2048 at 4 tokens
+    // 4.95 -> 3.81 us; at 512 tiles the stream kernel was as fast or faster,
+    // and 4 tokens over 16 waves (K > 2048) spill registers (4096 x 4096: 7.11
+    // vs 6.78 us).
+    const SplitShape sh = split_shape(groups);
+    return tiles <= 256 && sh.hs == 1 && (m <= 3 || sh.w <= 8);
+  }
   if (tiles > kSplitMaxTiles) {
     // One token on whole steps also beats the tall kernel up to 1536 row tiles
     // when the steps fill the block's waves (K = 4096 or 8192), measured:
