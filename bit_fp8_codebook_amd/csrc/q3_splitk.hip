@@ -20,9 +20,9 @@
 // (row i, quad kb) holds two groups' three code words in 8 bytes per word --
 // and half-step u goes to wave u % W (a 4096 x 4096 launch: 256 blocks of 16
 // waves, one half-step each).  Every wave first issues all of its loads: the
-// activations of its half-steps straight into its own LDS region
-// (buffer-to-LDS loads, no registers, no block barrier), then its code words,
-// scale bytes and the row codebook.  It waits only for its own activations,
+// activations of its half-steps, into its own LDS region (through registers
+// and one LDS store for 1..4 tokens, buffer-to-LDS loads above that; no block
+// barrier), then its code words, scale bytes and the row codebook.  It waits only for its own activations,
 // dequantises each group exactly to bf16 (codebook byte permute, then the
 // scaled FP8 -> bf16 conversion with the group's E8M0 scale) and multiplies:
 //   * matrix cores (1..16 tokens): the group's 16 bf16 pairs are the A
@@ -35,7 +35,8 @@
 // The waves' partial sums meet after a single block barrier and are added in
 // wave order, so results are run-to-run identical.  One token on the matrix
 // cores with K from 3072 up takes whole 512-k steps per wave instead
-// (splitk_full_kernel: 16-byte loads, half as many load instructions).
+// (splitk_full_kernel: 16-byte loads, half as many load instructions), on
+// matrices of up to 1536 row tiles at K = 4096 and 8192.
 #include "q3_device.h"
 #include "q3_internal.h"
 
