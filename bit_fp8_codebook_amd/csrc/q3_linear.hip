@@ -598,17 +598,23 @@ void linear_kernel(KArgs a) {
       if (tid < 64) *reinterpret_cast<u32x4*>(lds + zero_base + 16u * tid) = u32x4{0u, 0u, 0u, 0u};
       put(0, xr);
       __syncthreads();
+      // Each step's activations are requested before its weights: loads
+      // complete in issue order, so the LDS store of the activations (and the
+      // barrier behind it) then waits for them alone while the weights are
+      // still in flight (measured: 28672 x 8192 at 16 tokens 23.6 -> 21.8 us,
+      // K = 28672, N = 8192 at 16 tokens 49.7 -> 46.9 us in one pass and
+      // 24.9 -> 22.9 us split over blocks).
       for (int s = s0; s < s1; s += 2) {
-        load_step(p, rt, last_ok, s + 1, s1, B);
         fetch(s + 1, xr);
+        load_step(p, rt, last_ok, s + 1, s1, B);
         __builtin_amdgcn_sched_barrier(0);
         run(A, 0u, rstride, zero_base, 0u);
         __builtin_amdgcn_sched_barrier(0);
         put(1, xr);   // buffer 1 was last read at step s-1
         __syncthreads();
         if (s + 1 >= s1) break;
-        load_step(p, rt, last_ok, s + 2, s1, A);
         fetch(s + 2, xr);
+        load_step(p, rt, last_ok, s + 2, s1, A);
         __builtin_amdgcn_sched_barrier(0);
         run(B, buf_bytes, rstride, zero_base, 0u);
         __builtin_amdgcn_sched_barrier(0);
