@@ -8,7 +8,7 @@ steps per wave (K from 3072 up, with waves past the last step; up to 1536
 row tiles at K = 4096 and 8192, and the first matrices past each limit), last steps holding 1, 2
 or 3 quads (K % 512 != 0), ragged row counts, the 512-tile boundary (the next
 matrix takes the earlier kernels), 1..16 tokens on the matrix cores and one
-token on the vector ALUs, strided and unaligned operands, run-to-run
+to four tokens on the vector ALUs, strided and unaligned operands, run-to-run
 determinism and graph replays."""
 import numpy as np
 import pytest
@@ -34,6 +34,7 @@ CASES = [
     (16, 32, 1), (37, 96, 3), (5, 160, 16),              # one step, 1 quad (2 waves)
     (130, 800, 2), (1000, 768, 5), (64, 1024, 16),       # two steps, partial second (4 waves)
     (333, 1056, 7), (2048, 2048, 1), (2048, 2048, 9),    # 8 waves; K = 1056 ends on a 1-quad step
+    (2048, 2048, 4), (1000, 1056, 4), (130, 800, 3), (4096, 4096, 3),   # 3 and 4 tokens on the vector ALUs
     (4096, 4096, 1), (4096, 4096, 2), (4096, 4096, 4), (4095, 4096, 8), (4096, 4096, 12), (4096, 4096, 16),
     (100, 4000, 15),                                      # 16 waves, last step of 3 quads
     (4096, 8192, 1), (1000, 8192, 8), (300, 6176, 4),    # two half-steps per wave
