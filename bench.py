@@ -654,9 +654,17 @@ def main():
     launch_us = ms_step * 1e3 / layers
     alg = algorithmic_bytes(n, k, m)
     achieved = alg / (launch_us * 1e-6) / 1e9
-    kname, traffic = read_traffic(dot=(chosen == "gemv"))
+    kname, counted = read_traffic(dot=(chosen == "gemv"))
+    # traffic: HBM bytes per launch (read + written, copy-calibrated counters);
+    # the two directions and the dispatch count beside it.
+    traffic = None
+    if counted is not None and counted.get("read_bytes") is not None and counted.get("write_bytes") is not None:
+        traffic = int(counted["read_bytes"]) + int(counted["write_bytes"])
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic,
+                    traffic_read_bytes=None if traffic is None else int(counted["read_bytes"]),
+                    traffic_write_bytes=None if traffic is None else int(counted["write_bytes"]),
+                    traffic_counted_dispatches=None if traffic is None else counted.get("dispatches"),
                     kernel=kname, algorithmic_bytes_per_launch=alg, avg_launch_us=round(launch_us, 3),
                     trials_us_per_launch=[round(v * 1e3 / layers, 3) for v in spread],
                     eager_us_per_call=eager)
