@@ -30,7 +30,8 @@
 // Activations are staged in LDS once per block ("full-K" mode) or, when they do
 // not fit, one 512-k step at a time into a double buffer ("stream" mode).  The
 // next step's code words and scales are loaded before the current step is
-// computed; all loads are buffer loads whose out-of-range offsets read as zero,
+// computed (in stream mode right behind that step's activations, which are
+// requested first); all loads are buffer loads whose out-of-range offsets read as zero,
 // so rows past n, padding groups and absent tokens need no branches.  In full-K
 // mode the waves of a block may split K (few rows); partial sums are then
 // added through LDS in a fixed order, so results are run-to-run identical.
