@@ -106,6 +106,22 @@ def _brute_update(q, cents):
     return [new[j] for j in order]
 
 
+def test_nearest_equal_distances_go_to_the_lower_centroid():
+    # Grid values exactly midway between two centroids, integer and rational
+    # (9/2 and 11/2 around 5), checked against exact Fraction distances with
+    # the lower index taken on equal distances.
+    cents = [(-8, 1), (0, 1), (2, 1), (9, 2), (11, 2), (20, 3), (10, 1), (60, 1)]
+    q = np.array([-4, 1, 5, 8, 3, 6, 35, 61, -9, 0, 2], dtype=np.int64)
+    got = q3_fit.nearest(q, cents)
+    cv = [Fraction(sn, c) for sn, c in cents]
+    for x, j in zip(q.tolist(), got.tolist()):
+        d = [abs(x - c) for c in cv]
+        assert j == d.index(min(d)), (x, j)
+    # hand-derived: -4 ties -8/0 -> 0; 1 ties 0/2 -> 1; 5 ties 9/2 and 11/2 -> 3;
+    # 8 is nearest 20/3 -> 5; 35 ties 10/60 -> 6
+    assert got.tolist()[:4] == [0, 1, 3, 5] and got[6] == 6
+
+
 def _sse(q, cents):
     cv = [Fraction(s, c) for s, c in cents]
     return sum(min((int(x) - c) ** 2 for c in cv) for x in q)
