@@ -94,6 +94,18 @@ def make_linear(n: int, k: int, m: int, seed: int = 0):
     return layer, draw_x(rs[3], m, k)
 
 
+def make_layer_on_device(n: int, k: int, m: int, seed: int = 0, device: str = "cuda"):
+    """A layer too large to draw on the host: codes uint8 [n][k] drawn on the
+    device (torch's generator there, seeded, uniform over 0..7, a torch tensor),
+    the codebook, scales and bf16 activations x[m][k] drawn as in make_linear
+    (numpy arrays).  Returns (codes, codebook, scales, x)."""
+    rs = _streams(seed, 4)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(rs[0].integers(0, 2 ** 63 - 1)))
+    codes = torch.randint(0, 8, (n, k), dtype=torch.uint8, device=device, generator=g)
+    return codes, draw_codebook(rs[1], n), draw_scales(rs[2], n, k), draw_x(rs[3], m, k)
+
+
 @dataclass
 class MoEInputs:
     experts_gu: list = field(default_factory=list)   # Layer per expert (gate/up)

@@ -186,6 +186,11 @@ def test_validation_rejects_before_any_hip_call(q3lib):
     assert q3lib.q3_gemv(ctypes.byref(mis), fake, 1, 64, fake, 16, None) == 3
     huge = _lib.Q3Matrix(1 << 20, 8192, fake, fake, fake)                          # code plane >= 2 GiB
     assert q3lib.q3_gemv(ctypes.byref(huge), fake, 1, 8192, fake, 1 << 20, None) == 2
+    # one 16-row tile past the largest accepted K = 8192 matrix (43349 tiles of 49152 code bytes stay
+    # below 2 GiB - 16 MiB; 43350 do not): rejected (tests/test_gpu_limits.py runs the largest one)
+    over = _lib.Q3Matrix(16 * 43349 + 1, 8192, fake, fake, fake)
+    assert q3lib.q3_gemv(ctypes.byref(over), fake, 1, 8192, fake, 16 * 43349 + 1, None) == 2
+    assert q3lib.q3_gemm_small_m(ctypes.byref(over), fake, 16, 8192, fake, 16 * 43349 + 1, None) == 2
     nul = _lib.Q3Matrix(16, 64, fake, None, fake)
     assert q3lib.q3_gemv(ctypes.byref(nul), fake, 1, 64, fake, 16, None) == 1
     assert q3lib.q3_pack(fake, 63, fake, 2, 16, 64, fake, fake, None) == 1        # ldc < k
