@@ -13,6 +13,7 @@
 //
 // The dynamic-LDS allowances of the kernels, which are per device too.
 #include <atomic>
+#include <mutex>
 
 #include "q3_internal.h"
 
@@ -50,12 +51,15 @@ hipError_t allow_dynamic_lds(const void* kernel, size_t bytes, LdsAllowance& see
   if (e != hipSuccess) return e;
   const bool tracked = dev >= 0 && dev < kMaxDevices;
   if (tracked && bytes <= seen.bytes[dev].load(std::memory_order_acquire)) return hipSuccess;
+  // Raising the allowance is serialized, so that the attribute only grows: two
+  // threads raising it at once to different sizes could otherwise leave the
+  // smaller one set while the larger one is recorded.
+  static std::mutex raise;
+  std::lock_guard<std::mutex> lock(raise);
+  if (tracked && bytes <= seen.bytes[dev].load(std::memory_order_acquire)) return hipSuccess;
   e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e != hipSuccess || !tracked) return e;
-  size_t cur = seen.bytes[dev].load(std::memory_order_acquire);
-  while (cur < bytes && !seen.bytes[dev].compare_exchange_weak(cur, bytes)) {
-  }
-  return hipSuccess;
+  if (e == hipSuccess && tracked) seen.bytes[dev].store(bytes, std::memory_order_release);
+  return e;
 }
 
 }  // namespace q3
