@@ -242,7 +242,8 @@ Q3_API q3_status q3_moe_budget_topk(const float* logits, int32_t t, int32_t num_
  * x[i*topk + j][:] when x_by_slot == 1 (down projection, one activation per
  * pair).  x bf16 with row pitch ldx elements; y fp32 [t*topk][ldy].
  * topk_ids is a device int32 [t][topk] array (e.g. from q3_moe_topk); ids
- * outside [0, num_experts) are skipped.  t*topk <= 64. */
+ * outside [0, num_experts) are skipped (their rows of y are not written).
+ * t*topk <= 64. */
 Q3_API q3_status q3_grouped_expert_gemv(const q3_expert_stack* w, const uint16_t* x, int64_t ldx,
                                         int32_t x_by_slot, const int32_t* topk_ids, int32_t t,
                                         int32_t topk, float* y, int64_t ldy, void* stream);

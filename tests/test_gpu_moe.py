@@ -316,6 +316,29 @@ def test_moe_mlp_workspace_reuse_and_determinism(q3):
                 assert np.array_equal(out, first)
 
 
+def test_grouped_skips_out_of_range_ids(q3):
+    """Pairs whose id lies outside [0, E) are skipped: their rows of y keep what
+    they held, and the other pairs still match the oracle."""
+    moe = synth.make_moe(num_experts=6, k_gu=64, n_gu=48, k_dn=32, n_dn=40, tokens=3, topk=2, seed=17)
+    ids = oracle.topk_route(moe.logits, 2)
+    bad = ids.copy()
+    bad[0, 1] = -1
+    bad[2, 0] = 6
+    bad[2, 1] = 1 << 20
+    st_gu, st_dn = stack_experts(q3, moe.experts_gu), stack_experts(q3, moe.experts_dn)
+    x_dn = np.ascontiguousarray(moe.x_dn[:, :2]).reshape(6, -1)
+    for st, layers, xin, xref, by_slot in [(st_gu, moe.experts_gu, moe.x, moe.x, False),
+                                          (st_dn, moe.experts_dn, x_dn, moe.x_dn[:, :2], True)]:
+        y = torch.full((6, st.n), 7.25, dtype=torch.float32, device="cuda")
+        q3.q3_grouped_expert_gemv(st, dev(xin), dev(bad), by_slot, y)
+        y = y.cpu().numpy().reshape(3, 2, -1)
+        ref, b = oracle.grouped_linear(planes(layers), ids, xref, by_slot)
+        for i, j in [(0, 0), (1, 0), (1, 1)]:
+            assert_close(y[i, j][None], ref[i, j][None], b[i, j][None], f"pair ({i}, {j})")
+        for i, j in [(0, 1), (2, 0), (2, 1)]:
+            assert np.all(y[i, j] == 7.25), f"skipped pair ({i}, {j}) was written"
+
+
 def test_moe_mlp_skips_out_of_range_ids(q3):
     moe = synth.make_moe(num_experts=6, k_gu=64, n_gu=64, k_dn=32, n_dn=40, tokens=3, topk=2, seed=13)
     ids = oracle.topk_route(moe.logits, 2)
