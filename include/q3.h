@@ -55,8 +55,11 @@
  *   * Numerics: products are formed exactly and accumulated in fp32, so every
  *     output satisfies |y - y_exact| <= 1e-3 * sum_k |x_k w_k| for k <= 8192.
  *     Preconditions (not checked on the device): scale bytes in [16, 240],
- *     codebook bytes not NaN (0x7F/0xFF), x finite.  Code bits above bit 2 of
- *     q3_pack's input are ignored.
+ *     codebook bytes not NaN (0x7F/0xFF), x finite (bf16 subnormals are kept,
+ *     not flushed).  The bound also takes the fp32 products and partial sums
+ *     to stay inside fp32's range: no overflow, and none below its normal
+ *     range (2^-126), where fp32 cannot keep the relative precision.  Code bits
+ *     above bit 2 of q3_pack's input are ignored.
  */
 #ifndef Q3_H
 #define Q3_H

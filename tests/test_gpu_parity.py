@@ -136,6 +136,30 @@ def test_edge_values(q3):
         assert np.all(y[:, :2] == 0)
 
 
+@pytest.mark.parametrize("n,k,m", [(64, 256, 1), (64, 256, 4), (9000, 512, 1), (9000, 512, 16), (9000, 512, 64)])
+def test_subnormal_activations(q3, n, k, m):
+    """bf16 activations in the subnormal range (exponent field 0, random sign
+    and mantissa), mixed with zeros and one normal token row when m > 1,
+    against weights scaled by 2^13: every exact product stays in fp32's normal
+    range, so the bound holds only if the conversions and products keep the
+    subnormal inputs rather than flush them.  The shapes reach the split-K
+    kernel (vector ALUs and matrix cores), the tall and full-K kernels past 512
+    row tiles, and the wide kernel at 64 tokens."""
+    layer, _ = synth.make_linear(n, k, 1, seed=31)
+    layer.scales[:] = 140
+    rng = np.random.default_rng(31)
+    x = (rng.integers(1, 128, size=(m, k)) | (rng.integers(0, 2, size=(m, k)) << 15)).astype(np.uint16)
+    x[0, ::7] = 0
+    if m > 1:
+        x[1] = synth.make_linear(1, k, 1, seed=32)[1][0]     # a normal row next to the subnormal ones
+    w = pack_layer(q3, layer)
+    y_ref, bound = oracle_linear(layer, x)
+    assert np.all(bound[0] > 2.0 ** -126)
+    for fn in ("q3_gemv", "q3_gemm_small_m") if m <= 8 else ("q3_gemm_small_m",):
+        y = getattr(q3, fn)(w, dev(x)).cpu().numpy()
+        assert_close(y, y_ref, bound, f"{fn} n={n} k={k} m={m}")
+
+
 def test_empty_matrix(q3):
     layer, x = synth.make_linear(0, 64, 1, seed=1)
     w = q3.empty_packed(0, 64, "cuda")
