@@ -39,8 +39,8 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ lo
 // Expert-budget routing, one block per token, one thread per expert.  Every
 // block first computes the round's routing mass per expert (sum over tokens
 // of the token's softmax probability of that expert): each wave takes tokens
-// and reduces their max and exp-sum over the experts with a fixed lane
-// butterfly, then each thread sums its expert's probabilities over the tokens
+// and reduces their max and exp-sum over the experts in a fixed order (the
+// wave reductions below), then each thread sums its expert's probabilities over the tokens
 // in token order, so every block gets the same masses bit for bit.  The kept
 // set is the `budget` experts of largest mass (equal mass: lower index), each
 // found by counting the experts that rank before it; the block's token then
@@ -51,15 +51,31 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ lo
 // before the first use, so the per-token passes cost one memory latency in all
 // instead of one per token; the arithmetic and its order are the same either
 // way.
+// Wave-wide maximum and sum, the same value in every lane: DPP exchanges inside
+// rows of 16 lanes (xor 1, xor 2, then the half-row and row mirrors), which
+// leave each row's result in all its lanes, then the four rows' values read
+// out and combined in row order (a fixed order: run-to-run identical).  Lane
+// butterflies through LDS permutes cost a memory-pipe round trip per step.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off /= 2) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off /= 2) v += __shfl_xor(v, off, 64);
-  return v;
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
 constexpr int kStageFloats = 8192;
@@ -172,10 +188,9 @@ __global__ __launch_bounds__(1024) void budget_topk_kernel(const float* __restri
 // wave's registers, all loaded at once (no block barrier).  Measured with clock
 // stamps at one wave per SIMD, what costs is the length of dependent
 // instruction chains, so:
-//   * each token's maximum and exp-sum over the experts are DPP exchanges
-//     inside rows of 16 lanes (xor 1, xor 2, half-row and row mirrors), then
-//     the four row values read out and combined in row order; the reductions
-//     of different tokens are independent and interleave;
+//   * each token's maximum and exp-sum over the experts are the DPP
+//     reductions above; the reductions of different tokens are independent
+//     and interleave;
 //   * ranks are counted on 64-bit keys (the value's order-preserving bits
 //     above 63 - index, -0 taken as +0), so "ranks before" is one unsigned
 //     comparison; every lane compares its key with all 64 from LDS, into four
@@ -186,13 +201,6 @@ __global__ __launch_bounds__(1024) void budget_topk_kernel(const float* __restri
 // tokens and 64 experts, clock stamps: 5.5 us with readlane loops and lane
 // butterflies, 2.9 us with the keys and DPP, 2.2 us with the reciprocal and
 // the keys read before counting.)
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float lane_f(float v, int l) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-}
 __device__ __forceinline__ uint64_t rank_key(float v, int idx) {
   uint32_t b = __builtin_bit_cast(uint32_t, v + 0.0f);
   b ^= (b >> 31) ? 0xFFFFFFFFu : 0x80000000u;
@@ -228,31 +236,11 @@ __global__ __launch_bounds__(64) void budget_topk_wave_kernel(const float* __res
   const float tk = logits[(int64_t)t * E + le];
   float mx[kT], ex[kT], sm[kT];
 #pragma unroll
-  for (int u = 0; u < kT; ++u) mx[u] = live ? l[u] : -__builtin_inff();
-#pragma unroll
-  for (int u = 0; u < kT; ++u) mx[u] = fmaxf(mx[u], dpp_f<0xB1>(mx[u]));    // quad_perm [1,0,3,2]
-#pragma unroll
-  for (int u = 0; u < kT; ++u) mx[u] = fmaxf(mx[u], dpp_f<0x4E>(mx[u]));    // quad_perm [2,3,0,1]
-#pragma unroll
-  for (int u = 0; u < kT; ++u) mx[u] = fmaxf(mx[u], dpp_f<0x141>(mx[u]));   // row_half_mirror
-#pragma unroll
-  for (int u = 0; u < kT; ++u) mx[u] = fmaxf(mx[u], dpp_f<0x140>(mx[u]));   // row_mirror
-#pragma unroll
-  for (int u = 0; u < kT; ++u)
-    mx[u] = fmaxf(fmaxf(lane_f(mx[u], 0), lane_f(mx[u], 16)), fmaxf(lane_f(mx[u], 32), lane_f(mx[u], 48)));
+  for (int u = 0; u < kT; ++u) mx[u] = wave_max(live ? l[u] : -__builtin_inff());
 #pragma unroll
   for (int u = 0; u < kT; ++u) sm[u] = ex[u] = live ? expf(l[u] - mx[u]) : 0.f;
 #pragma unroll
-  for (int u = 0; u < kT; ++u) sm[u] += dpp_f<0xB1>(sm[u]);
-#pragma unroll
-  for (int u = 0; u < kT; ++u) sm[u] += dpp_f<0x4E>(sm[u]);
-#pragma unroll
-  for (int u = 0; u < kT; ++u) sm[u] += dpp_f<0x141>(sm[u]);
-#pragma unroll
-  for (int u = 0; u < kT; ++u) sm[u] += dpp_f<0x140>(sm[u]);
-#pragma unroll
-  for (int u = 0; u < kT; ++u)
-    sm[u] = (lane_f(sm[u], 0) + lane_f(sm[u], 16)) + (lane_f(sm[u], 32) + lane_f(sm[u], 48));
+  for (int u = 0; u < kT; ++u) sm[u] = wave_sum(sm[u]);
   float m = 0.f;
 #pragma unroll
   for (int u = 0; u < kT; ++u)
