@@ -53,6 +53,25 @@ __device__ __forceinline__ int clamp_q(int64_t m) {
   return (int)(m < -kHalf - 1 ? -kHalf - 1 : (m > kHalf ? kHalf : m));
 }
 
+// Lane l's value in every lane (two readlanes: lane l of the wave's first group,
+// which holds what every group holds).
+__device__ __forceinline__ double from_lane(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// The next lower lane's value (DPP row_shr:1 on both halves; the first lane of
+// each 16-lane row reads 0, the first lane of the second group of a row reads
+// the last lane of the first: lane a = 0 of a group never uses the result).
+__device__ __forceinline__ double from_lower_lane(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, 0x111, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), 0x111, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // The value of this lane lands in lane `dst` (ds_permute: each lane pushes).
 __device__ __forceinline__ double permute_to(int dst, double v) {
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
@@ -218,8 +237,8 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(const float* __restric
     // run takes the q between the midpoints to the neighbouring distinct values
     // (a q on a midpoint goes to the lower run); the others get none and keep
     // their value.
-    const double ps = __shfl(cs, g0 + (a > 0 ? a - 1 : 0), 64);
-    const double pc = __shfl(cc, g0 + (a > 0 ? a - 1 : 0), 64);
+    const double ps = from_lower_lane(cs);
+    const double pc = from_lower_lane(cc);
     const bool start = a == 0 || ps * cc != cs * pc;
     const uint32_t starts = (uint32_t)__ballot(start) & 0xFFu;    // group 0's lanes
     const uint32_t above = starts >> (a + 1);
@@ -239,7 +258,7 @@ __global__ __launch_bounds__(kFitThreads) void fit_kernel(const float* __restric
     int rank = 0;
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const double bs = __shfl(ts, g0 + b, 64), bc = __shfl(tc, g0 + b, 64);
+      const double bs = from_lane(ts, b), bc = from_lane(tc, b);
       const double l = bs * tc, r = ts * bc;
       rank += (l < r || (l == r && b < a)) ? 1 : 0;
     }
