@@ -200,9 +200,8 @@ __global__ __launch_bounds__(64 * kW) void splitk_kernel(SplitArgs a) {
   float* const red = reinterpret_cast<float*>(lds + kRed);
   if constexpr (!kDot && NT == 1 && kHS == 1) {
     // One token, one half-step: the activations go to registers right away
-    // (every lane reads its quad's 128 bytes), the token's 16 row sums are
-    // gathered into lanes 0..15 (lane 16*(r/4) holds rows 4*(r/4)..+3), and
-    // the waves' sums meet as 16 floats each.
+    // (every lane reads its quad's 128 bytes), and the waves' sums meet as the
+    // 16 row sums of each, stored straight from the four lanes that hold them.
     u32x4 xv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) xv[e] = *reinterpret_cast<const u32x4*>(xw + 128u * kb + 16u * e);
@@ -219,13 +218,9 @@ __global__ __launch_bounds__(64 * kW) void splitk_kernel(SplitArgs a) {
                                                     d, 0, 0, 0);
       }
     }
-    float r = 0.f;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float dv = __shfl(d[v], 16 * (i >> 2), 64);
-      if ((i & 3) == v) r = dv;
-    }
-    if (lane < 16) red[wave * 16 + lane] = r;
+    // Column 0 of D: lane 16 q holds rows 4 q .. 4 q + 3, stored as they are
+    // (no lane exchange: each permute is a round trip through the LDS pipe).
+    if (i == 0) *reinterpret_cast<f32x4*>(red + wave * 16 + 4 * kb) = d;
     __syncthreads();
     if (wave == 0 && lane < 16) {
       float v = red[lane];
@@ -423,16 +418,10 @@ __global__ __launch_bounds__(64 * kW) void splitk_full_kernel(SplitArgs a) {
                                                     d, 0, 0, 0);
       }
     }
-  // Row sums of column 0 into lanes 0..15 (lane 16*(r/4) holds rows 4*(r/4)..+3),
-  // then the waves' sums in wave order.
-  float r = 0.f;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const float dv = __shfl(d[v], 16 * (i >> 2), 64);
-    if ((i & 3) == v) r = dv;
-  }
+  // Column 0 of D (lane 16 q holds rows 4 q .. 4 q + 3) goes to LDS as it is,
+  // then the waves' sums are added in wave order.
   float* const red = reinterpret_cast<float*>(lds + kW * kSPW * 1024u);
-  if (lane < 16) red[wave * 16 + lane] = r;
+  if (i == 0) *reinterpret_cast<f32x4*>(red + wave * 16 + 4 * kb) = d;
   __syncthreads();
   if (wave == 0 && lane < 16) {
     float v = red[lane];
