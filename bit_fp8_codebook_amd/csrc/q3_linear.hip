@@ -249,7 +249,13 @@ __device__ __forceinline__ void pipe_unit(const StepData<R>& d, const RowTile (&
     constexpr int t = U / R, r = U % R, cur = U & 1;
     constexpr int kMfma = 4 * MT;                     // MFMAs per unit
     constexpr int kValu = (48 + kMfma - 1) / kMfma;   // ALU instructions after each of them
-    constexpr int q0 = U * kLoads / kUnits, q1 = (U + 1) * kLoads / kUnits;
+#ifdef Q3_WIDE_ISSUE8
+    constexpr int kIssueUnits = (kUnits * Q3_WIDE_ISSUE8 + 7) / 8;
+#else
+    constexpr int kIssueUnits = kUnits;
+#endif
+    constexpr int q0 = U < kIssueUnits ? U * kLoads / kIssueUnits : kLoads;
+    constexpr int q1 = U + 1 < kIssueUnits ? (U + 1) * kLoads / kIssueUnits : kLoads;
     issue_range<q0, q1>(issue);
     if constexpr (U + 1 < kUnits) {
       constexpr int t1 = (U + 1) / R, r1 = (U + 1) % R;
@@ -898,6 +904,238 @@ void wide_kernel(KArgs a) {
   }
 }
 
+// Wide products at two waves per SIMD, in half-steps.  A launch of the wide
+// kernel above is bound by its weight stream, not by its arithmetic (measured
+// on a 64-token vocabulary projection: the same launch with no dequantisation
+// and no MFMA takes as long), because its one block per CU drains all of its
+// loads at every step's barrier.  Here a block's activations are staged half
+// a step at a time (the first two groups of every quad, then the last two), so
+// the double buffer takes 64 KB and two blocks share a CU: the two blocks'
+// barriers fall at unrelated times, and while one waits for its loads the
+// other computes.  Each wave keeps R row tiles for all of K.
+//
+// LDS layout of a half-step buffer: token t's 512 bytes (four 64-k runs, one
+// per quad kb) are 32 chunks of 8 activations, chunk c = 8 kb + 4 tt + e
+// (group 2h + tt of quad kb, k 8e..8e+7) stored at position c ^ (t & 15): the
+// 16 tokens of a column tile then read one chunk from 16 different bank
+// groups.  One direct-to-LDS load moves 1 KB, tokens 2q and 2q+1.
+template <int R>
+struct HalfStep {
+  u32x2 w[R][3];     // w[r][j][tt] = word j of the lane's group 2h+tt of row tile r
+  uint32_t sc[R];    // bytes 0, 1: the scales of those two groups
+};
+
+// Selectors, codebook lookup and exact bf16 widening of weights 8e..8e+7 of
+// one group (one MFMA's A operand); the same selector rule as the whole-group
+// unpacking.
+template <int E>
+__device__ __forceinline__ bf16x8 dequant_chunk(uint32_t d0, uint32_t d1, uint32_t d2, float sc, uint32_t cbl,
+                                                uint32_t cbh) {
+  constexpr uint32_t m3 = 0x07070707u;
+  uint32_t src;
+  if constexpr (E == 0) src = d0;
+  else if constexpr (E == 1) src = d1;
+  else if constexpr (E == 2) src = d2;
+  else src = ((d0 >> 6) & 0x03030303u) | ((d1 >> 4) & 0x0C0C0C0Cu) | ((d2 >> 2) & 0x30303030u);
+  const uint32_t qa = lookup4(cbl, cbh, src & m3), qb = lookup4(cbl, cbh, (src >> 3) & m3);
+  return pack_bf16x8(fp8x2_to_bf16x2(qa, sc, false), fp8x2_to_bf16x2(qa, sc, true), fp8x2_to_bf16x2(qb, sc, false),
+                     fp8x2_to_bf16x2(qb, sc, true));
+}
+
+// The lane's row codebook of each of the wave's row tiles.
+struct RowCb {
+  uint32_t lo, hi;
+};
+
+constexpr uint32_t kHalfTokenBytes = 512;   // one token's activations of one half-step
+constexpr int kKeepPolicy = 1;               // work-group scope (sc0), no non-temporal hint
+
+// Chunk CH = 4 tt + e of a half-step: B operands of the NT column tiles, then
+// the chunk's dequantisation and 4 MFMAs for each row tile.  xrow: the lane's
+// token row in the buffer plus 16 * ((8 kb) ^ (i & 8)); i7 = i & 7.
+template <int NT, int R, int kLoads, int CH, typename Issue>
+__device__ __forceinline__ void wide_hs_chunk(const HalfStep<R>& d, const RowCb (&cb)[R], uint32_t xrow, uint32_t i7,
+                                            const uint8_t* lds, f32x4 (&acc)[R][NT], Issue& issue) {
+  if constexpr (CH < 8) {
+    constexpr int tt = CH / 4, e = CH % 4;
+    // The next half-step's loads go out an eighth per chunk (issued all at
+    // once, or in the first half of the chunks, the wave stalls on them: 5-10%
+    // slower), and stay in their chunk: left alone, the scheduler sinks them
+    // to the end, where the closing wait exposes their whole latency.
+    constexpr int q0 = CH * kLoads / 8, q1 = (CH + 1) * kLoads / 8;
+    issue_range<q0, q1>(issue);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t xa = xrow + 16u * ((uint32_t)CH ^ i7);
+    bf16x8 b[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+      b[c] = *reinterpret_cast<const bf16x8*>(lds + xa + (uint32_t)c * 16u * kHalfTokenBytes);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float sc = e8m0_to_f32((d.sc[r] >> (8 * tt)) & 0xFFu);
+      const bf16x8 a = dequant_chunk<e>(d.w[r][0][tt], d.w[r][1][tt], d.w[r][2][tt], sc, cb[r].lo, cb[r].hi);
+#pragma unroll
+      for (int c = 0; c < NT; ++c) acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[c], acc[r][c], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wide_hs_chunk<NT, R, kLoads, CH + 1>(d, cb, xrow, i7, lds, acc, issue);
+  }
+}
+
+template <int NT, int R, int kLoads, typename Issue>
+__device__ __forceinline__ void wide_hs_half(const HalfStep<R>& d, const RowCb (&cb)[R], uint32_t xrow, uint32_t i7,
+                                           const uint8_t* lds, f32x4 (&acc)[R][NT], Issue&& issue) {
+  wide_hs_chunk<NT, R, kLoads, 0>(d, cb, xrow, i7, lds, acc, issue);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < NT; ++c) asm volatile("" : "+v"(acc[r][c]));
+}
+
+constexpr int kWideHsWaves = 4;
+
+size_t wide_hs_bytes(int slice) { return 2u * (size_t)slice * kHalfTokenBytes; }
+
+template <int NT, int R>
+__global__ __launch_bounds__(64 * kWideHsWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void wide_hs_kernel(KArgs a) {
+  constexpr int kW = kWideHsWaves, kSlice = 16 * NT;
+  constexpr uint32_t buf_bytes = (uint32_t)kSlice * kHalfTokenBytes;
+  static_assert(kSlice % (2 * kW) == 0, "two tokens per activation load, spread evenly over the waves");
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 15, kb = lane >> 4;
+
+  const uint32_t gp = (uint32_t)a.G;   // a multiple of 16 here
+  const int64_t tiles = (a.n + 15) / 16;
+  const int64_t tile0 = ((int64_t)blockIdx.x * kW + wave) * R;
+  const rsrc_t code = make_rsrc(a.code, (uint32_t)(tiles * 192 * gp));
+  const rsrc_t scale = make_rsrc(a.scale, (uint32_t)(tiles * 16 * gp));
+  const int steps = (int)(gp / 16);
+  const int s_begin = (int)(blockIdx.z * steps / gridDim.z);
+  const int s_end = (int)((blockIdx.z + 1) * steps / gridDim.z);
+  float* const ybase = a.y + (int64_t)blockIdx.z * a.split_stride;
+  const rsrc_t cbr = make_rsrc(a.cb, (uint32_t)(a.n * 8));
+  // Row tiles past the matrix read the last tile again (their outputs are
+  // never stored), so a tile's plane offsets stay wave-uniform (the loads'
+  // scalar offsets) and the lane's part is shared by all of them.
+  uint32_t tcode[R], tscale[R];
+  RowCb cb[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t T = tile0 + r < tiles ? tile0 + r : tiles - 1;
+    tcode[r] = (uint32_t)T * (192u * gp);
+    tscale[r] = (uint32_t)T * (16u * gp);
+    const int64_t row = (tile0 + r) * 16 + i;
+    const u32x2 c2 = bload64(cbr, row < a.n ? (uint32_t)row * 8u : kOob);
+    cb[r].lo = c2.x;
+    cb[r].hi = c2.y;
+  }
+  const uint32_t vcode = 16u * lane, vscale = 4u * lane;
+  const rsrc_t xr = make_rsrc(a.x, (uint32_t)((a.x_rows - 1) * a.ldx * 2 + (int64_t)a.G * 64));
+  const uint32_t ldx_bytes = (uint32_t)(a.ldx * 2);
+  // Activation loads: this wave moves tokens 2q, 2q+1 for q = wave + kW*j;
+  // lane l takes token 2q + l/32 and the chunk stored at position l%32.  The
+  // position-to-chunk map depends on the token's low four bits, which for
+  // this wave's loads take two values (j even, j odd).
+  uint32_t xsrc[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const uint32_t t = 2u * (uint32_t)(wave + kW * par) + (uint32_t)(lane >> 5);
+    const uint32_t c = ((uint32_t)lane & 31u) ^ (t & 15u);
+    xsrc[par] = (uint32_t)(lane >> 5) * ldx_bytes + 256u * (c >> 3) + 16u * (c & 7u);
+  }
+  const uint32_t i7 = (uint32_t)i & 7u;
+
+  for (int slice = 0; slice < a.m; slice += kSlice) {
+    const int cnt = a.m - slice < kSlice ? a.m - slice : kSlice;
+    const uint32_t xrow0 = (uint32_t)i * kHalfTokenBytes + 16u * ((8u * (uint32_t)kb) ^ ((uint32_t)i & 8u));
+    const uint32_t xrow1 = xrow0 + buf_bytes;
+    f32x4 acc[R][NT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < NT; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // The loads of half-step (sn, H): this wave's code words and scales into
+    // dst, and its share of the activation rows into the LDS buffer at buf.
+    // A half-step past the last reads out of range (zeros, no traffic); rows
+    // of absent tokens hold zeros and only reach output columns never stored.
+    constexpr int kLoads = 4 * R + kSlice / (2 * kW);
+    auto loads_of = [&](HalfStep<R>& dst, uint32_t buf, int sn, auto hc) {
+      constexpr uint32_t H = decltype(hc)::value;
+      // The first half-step reads the first 8 bytes of every 16-byte piece and
+      // the second the rest, half a step later.  Non-temporal loads in the
+      // first half let the lines go before the second half reads them (twice
+      // the algorithmic bytes fetched, measured): only the second half of a
+      // piece is read with the streaming policy.
+      constexpr int kPol = H == 0 ? kKeepPolicy : Q3_STREAM_POLICY;
+      const bool live = sn < s_end;
+      const uint32_t sc = (uint32_t)(live ? sn : s_end - 1);
+      const uint32_t vc = live ? vcode + 8u * H : kOob, vs = live ? vscale + 2u * H : kOob;
+      return [&, buf, live, sc, vc, vs](auto q) {
+        constexpr int Q = decltype(q)::value;
+        if constexpr (Q < 3 * R) {
+          constexpr int r = Q / 3, j = Q % 3;
+          dst.w[r][j] = __builtin_amdgcn_raw_buffer_load_b64(code, vc + 1024u * j, tcode[r] + 3072u * sc, kPol);
+        } else if constexpr (Q < 4 * R) {
+          constexpr int r = Q - 3 * R;
+          dst.sc[r] = __builtin_amdgcn_raw_buffer_load_b16(scale, vs, tscale[r] + 256u * sc, kPol);
+        } else {
+          constexpr int jq = Q - 4 * R;
+          const int qi = wave + kW * jq;                 // this load moves tokens 2qi, 2qi+1
+          const int t = 2 * qi + (lane >> 5);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              xr, (__attribute__((address_space(3))) void*)(lds + buf + (uint32_t)qi * 1024u), 16,
+              live && t < cnt ? xsrc[jq & 1] + 128u * H : kOob,
+              (uint32_t)(slice + (2 * qi < cnt ? 2 * qi : 0)) * ldx_bytes + 1024u * sc, 0, 0);
+        }
+      };
+    };
+    HalfStep<R> A, B;
+    {
+      auto first = loads_of(A, 0u, s_begin, std::integral_constant<uint32_t, 0>{});
+      issue_range<0, kLoads>(first);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int s = s_begin; s < s_end; ++s) {
+      wide_hs_half<NT, R, kLoads>(A, cb, xrow0, i7, lds, acc,
+                                loads_of(B, buf_bytes, s, std::integral_constant<uint32_t, 1>{}));
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      wide_hs_half<NT, R, kLoads>(B, cb, xrow1, i7, lds, acc,
+                                loads_of(A, 0u, s + 1, std::integral_constant<uint32_t, 0>{}));
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+
+    // D layout: lane l holds rows 4*(l/16)+v (v = 0..3) of the tile for token l%16.
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      const int j = 16 * c + i;
+      if (j < cnt) {
+        float* yr = ybase + (int64_t)(slice + j) * a.ldy;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int64_t row0 = (tile0 + r) * 16 + 4 * kb;
+          if (a.vec_y && row0 + 3 < a.n) {
+            *reinterpret_cast<f32x4*>(yr + row0) = acc[r][c];
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (row0 + v < a.n) yr[row0 + v] = acc[r][c][v];
+          }
+        }
+      }
+    }
+  }
+}
+
 // ---- host side ------------------------------------------------------------------
 
 size_t full_k_bytes(int tokens, int groups) {
@@ -939,6 +1177,19 @@ hipError_t launch_wide(const KArgs& a, unsigned splits, hipStream_t s) {
   const int64_t tiles = (a.n + 15) / 16;
   const dim3 grid((unsigned)((tiles + kRowsPerBlock - 1) / kRowsPerBlock), 1, splits);
   hipLaunchKernelGGL((wide_kernel<NT, R>), grid, dim3(64 * kWideWaves), shm, s, a);
+  return hipGetLastError();
+}
+
+template <int NT, int R>
+hipError_t launch_wide_hs(const KArgs& a, unsigned splits, hipStream_t s) {
+  constexpr int kRowsPerBlock = R * kWideHsWaves;
+  const size_t shm = wide_hs_bytes(16 * NT);
+  static LdsAllowance seen;
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(wide_hs_kernel<NT, R>), shm, seen);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = (a.n + 15) / 16;
+  const dim3 grid((unsigned)((tiles + kRowsPerBlock - 1) / kRowsPerBlock), 1, splits);
+  hipLaunchKernelGGL((wide_hs_kernel<NT, R>), grid, dim3(64 * kWideHsWaves), shm, s, a);
   return hipGetLastError();
 }
 
@@ -1052,13 +1303,14 @@ hipError_t launch_r(KArgs a, int w, int mode, size_t shm, unsigned grid_y, unsig
 }
 
 
-// tokens_in_slice: tokens the LDS staging holds at once.  wide_rows and
-// splits (dense matrix-core products of streamed activations only): row tiles
-// per wave of the wide kernel (5 or 2) and K splits over blocks, each writing
-// the partial plane a.y + z * a.split_stride.
+// tokens_in_slice: tokens the LDS staging holds at once.  wide_rows, splits
+// and halfstep (dense matrix-core products of streamed activations only): row
+// tiles per wave of the wide kernel (5, 2 or 1), K splits over blocks, each
+// writing the partial plane a.y + z * a.split_stride, and the half-step
+// variant of the five-tile kernel (three or four column tiles).
 template <int NT, int kGrouped, bool kDot, int kBits = 3>
 hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t s, int wide_rows = 5,
-                      unsigned splits = 1) {
+                      unsigned splits = 1, bool halfstep = false) {
   constexpr int kSlice = kDot ? NT : 16 * NT;
   const size_t fk = full_k_bytes(tokens_in_slice, a.G);
   const bool full_k = fk <= (size_t)kFullKBudget && !(kGrouped && kExpertStream);
@@ -1082,6 +1334,9 @@ hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t
   if constexpr (!kGrouped && !kDot && kBits == 3 && NT >= kWideMinNT) {
     if (mode == kStream && a.G % 16 == 0) {
       if (wide_rows == 1) return launch_wide<NT, 1>(a, splits, s);
+      if constexpr (NT >= 3) {
+        if (halfstep && wide_rows == 5) return launch_wide_hs<NT, 5>(a, splits, s);
+      }
       return wide_rows == 2 ? launch_wide<NT, 2>(a, splits, s) : launch_wide<NT, 5>(a, splits, s);
     }
   }
@@ -1149,10 +1404,19 @@ KArgs base_args(const PlaneView& w) {
 struct SmallMPlan {
   int wide_rows;   // row tiles per wave of the wide kernel (1, 2 or 5)
   int splits;      // K splits over blocks
+  bool halfstep;   // five row tiles in half-steps, two blocks per CU
 };
 
+// Blocks of the five-tile wide kernel from which its half-step variant (two
+// blocks per CU) is the faster one, at three or four column tiles.  Measured
+// at 64 tokens and K = 4096: 151,936 rows (475 blocks) 94.2 -> 89.8 us,
+// 131,072 rows (410) 90.4 -> 82.6 us; 65,536 rows (205) 43.7 -> 50.8 us, where
+// most CUs run a single block and the half-step kernel's extra barriers and
+// 8-byte loads are not repaid.
+constexpr int64_t kHalfStepMinBlocks = 400;
+
 SmallMPlan plan_small_m(int64_t n, int groups, int64_t m) {
-  SmallMPlan pl{5, 1};
+  SmallMPlan pl{5, 1, false};
   if (n <= 0) return pl;
   const int nt = (int)((m + 15) / 16);
   if (full_k_bytes((int)m, groups) <= (size_t)kFullKBudget) return pl;   // staged whole: no split
@@ -1165,8 +1429,12 @@ SmallMPlan plan_small_m(int64_t n, int groups, int64_t m) {
     // 1.8x a two-tile one (measured at 64 tokens: 9 and 12.5 us per round
     // and row tile), so five row tiles win only where they do not add a
     // nearly empty round (N = 65536: 46 vs 50 us; N = 98304: 89 vs 74 us).
-    const int64_t rounds5 = ((tiles + 19) / 20 + 255) / 256, rounds2 = ((tiles + 7) / 8 + 255) / 256;
+    const int64_t blocks5 = (tiles + 19) / 20;
+    const bool hs = nt >= 3 && blocks5 >= kHalfStepMinBlocks;
+    const int64_t slots5 = hs ? 512 : 256;
+    const int64_t rounds5 = (blocks5 + slots5 - 1) / slots5, rounds2 = ((tiles + 7) / 8 + 255) / 256;
     if (rounds2 * 50 < rounds5 * 90) pl.wide_rows = 2;
+    else pl.halfstep = hs;
     // 512..1535 row tiles at K <= 4096: one row tile per wave (a grid of 128
     // blocks and more) in one pass beats two tiles per wave split over blocks
     // (8192 x 4096 at 64 tokens: 17.7 -> 16.0 us; 12288 x 4096: 19.2 -> 16.4 us).
@@ -1227,8 +1495,8 @@ hipError_t launch_gemm_small_m(const PlaneView& w, const uint16_t* x, int64_t m,
   hipError_t e;
   if (m <= 16) e = launch_cfg<1, kDense, false>(a, (int)m, 1, s, pl.wide_rows, pl.splits);
   else if (m <= 32) e = launch_cfg<2, kDense, false>(a, (int)m, 1, s, pl.wide_rows, pl.splits);
-  else if (m <= 48) e = launch_cfg<3, kDense, false>(a, (int)m, 1, s, pl.wide_rows, pl.splits);
-  else e = launch_cfg<4, kDense, false>(a, (int)m, 1, s, pl.wide_rows, pl.splits);
+  else if (m <= 48) e = launch_cfg<3, kDense, false>(a, (int)m, 1, s, pl.wide_rows, pl.splits, pl.halfstep);
+  else e = launch_cfg<4, kDense, false>(a, (int)m, 1, s, pl.wide_rows, pl.splits, pl.halfstep);
   if (e != hipSuccess || pl.splits == 1) return e;
   const int64_t threads = m * ((w.n + 3) / 4);
   const int vec = ((uintptr_t)ws % 16 == 0) && (w.n % 4 == 0) && ((uintptr_t)y % 16 == 0) && (ldy % 4 == 0);

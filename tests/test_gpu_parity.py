@@ -214,6 +214,20 @@ def test_many_row_groups_all_rows(q3, n, k, m):
     assert_close(y, y_ref, bound, f"n={n} k={k} m={m}")
 
 
+@pytest.mark.parametrize("n,k,m", [(128005, 2560, 64), (128005, 2048, 40), (151936, 2560, 33)])
+def test_halfstep_wide_all_rows(q3, n, k, m):
+    # Vocabulary-sized matrices with three or four column tiles take the wide
+    # kernel's half-step variant (two blocks per CU): a ragged last row tile
+    # (its tiles past n re-read the last one), an odd step count, and column
+    # tiles only partly filled with tokens.
+    layer, x = synth.make_linear(n, k, m, seed=n + k + m)
+    w = pack_layer(q3, layer)
+    y = q3.q3_gemm_small_m(w, dev(x)).cpu().numpy()
+    del w
+    y_ref, bound = oracle_linear(layer, x)
+    assert_close(y, y_ref, bound, f"half-step wide n={n} k={k} m={m}")
+
+
 @pytest.mark.parametrize("m", [1, 4, 8])
 def test_config1_full_gemv_and_mfma(q3, m):
     layer, x = synth.make_linear(4096, 4096, m, seed=0)
