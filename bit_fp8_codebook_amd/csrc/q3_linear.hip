@@ -249,13 +249,7 @@ __device__ __forceinline__ void pipe_unit(const StepData<R>& d, const RowTile (&
     constexpr int t = U / R, r = U % R, cur = U & 1;
     constexpr int kMfma = 4 * MT;                     // MFMAs per unit
     constexpr int kValu = (48 + kMfma - 1) / kMfma;   // ALU instructions after each of them
-#ifdef Q3_WIDE_ISSUE8
-    constexpr int kIssueUnits = (kUnits * Q3_WIDE_ISSUE8 + 7) / 8;
-#else
-    constexpr int kIssueUnits = kUnits;
-#endif
-    constexpr int q0 = U < kIssueUnits ? U * kLoads / kIssueUnits : kLoads;
-    constexpr int q1 = U + 1 < kIssueUnits ? (U + 1) * kLoads / kIssueUnits : kLoads;
+    constexpr int q0 = U * kLoads / kUnits, q1 = (U + 1) * kLoads / kUnits;
     issue_range<q0, q1>(issue);
     if constexpr (U + 1 < kUnits) {
       constexpr int t1 = (U + 1) / R, r1 = (U + 1) % R;
