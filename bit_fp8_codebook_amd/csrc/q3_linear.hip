@@ -36,9 +36,11 @@
 // mode the waves of a block may split K (few rows); partial sums are then
 // added through LDS in a fixed order, so results are run-to-run identical.
 //
-// The grouped variant runs one grid row per expert.  Its block first collects
-// the (token, slot) pairs routed to that expert; an expert nobody picked
-// returns before reading any weight byte (Hibana page, "Adaptive speculation" /
+// The grouped variant runs one grid row per expert the round picked (with up
+// to 64 experts, row y takes the y-th smallest picked id, so blocks with work
+// are dispatched first; past 64, row e is expert e).  Its block first collects
+// the (token, slot) pairs routed to that expert; a row without one returns
+// before reading any weight byte (Hibana page, "Adaptive speculation" /
 // "Expert sharing": a verify round reads every picked expert once).
 #include <atomic>
 #include <type_traits>
@@ -368,6 +370,18 @@ constexpr int min_waves_per_eu() {
   return R == 1 && NT <= 2 ? 4 : 2;
 }
 
+// OR of a value over the 64 lanes of a wave (every lane active), returned as
+// a wave-uniform value: DPP exchanges inside rows of 16 lanes, then the four
+// rows' results by readlane.
+__device__ __forceinline__ uint32_t wave_or32(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);   // row_mirror
+  return (uint32_t)(__builtin_amdgcn_readlane((int)v, 0) | __builtin_amdgcn_readlane((int)v, 16) |
+                    __builtin_amdgcn_readlane((int)v, 32) | __builtin_amdgcn_readlane((int)v, 48));
+}
+
 // NT: column tiles of 16 tokens (matrix-core mode) or tokens (vector-ALU mode).
 // kBits: 3 for the 3-bit layer, 2 for the two-bit draft head (two code words
 // per group, a 4-entry codebook per row).
@@ -395,13 +409,27 @@ void linear_kernel(KArgs a) {
   // ---- which expert / tokens -------------------------------------------------
   int expert = 0;
   if (kGrouped) {
-    expert = blockIdx.y;
-    if (tid < 64) {
-      const int id = tid < a.pairs_total ? a.ids[tid] : -1;
-      const bool match = id == expert;
+    // Every wave reads the round's ids and finds its block's expert itself,
+    // so the planes' addresses do not wait for the block barrier.
+    const int id = lane < a.pairs_total ? a.ids[lane] : -1;
+    int e = blockIdx.y;
+    if (a.num_experts <= 64) {
+      // Grid row y takes the round's y-th smallest picked expert, so the
+      // blocks with work come first in dispatch order and the rows past the
+      // round's distinct experts (at most its 64 pairs) exit at once.
+      const bool valid = id >= 0 && id < a.num_experts;
+      const uint64_t bit = valid ? 1ull << id : 0ull;
+      const uint64_t used = (uint64_t)wave_or32((uint32_t)bit) | (uint64_t)wave_or32((uint32_t)(bit >> 32)) << 32;
+      const bool sel = ((used >> lane) & 1ull) != 0 && __popcll(used & ((1ull << lane) - 1ull)) == (int)blockIdx.y;
+      const uint64_t pick = __ballot(sel);
+      e = pick != 0 ? __builtin_ctzll(pick) : -1;
+    }
+    expert = __builtin_amdgcn_readfirstlane(e);
+    if (wave == 0) {
+      const bool match = expert >= 0 && id == expert;
       const unsigned long long mask = __ballot(match);
-      if (match) pairs[__popcll(mask & ((1ull << tid) - 1ull))] = tid;
-      if (tid == 0) npairs = __popcll(mask);
+      if (match) pairs[__popcll(mask & ((1ull << lane) - 1ull))] = lane;
+      if (lane == 0) npairs = __popcll(mask);
     }
     __syncthreads();
     if (npairs == 0) return;   // not picked this round: no weight byte is read
@@ -1059,17 +1087,19 @@ void wide_hs_kernel(KArgs a) {
     // of absent tokens hold zeros and only reach output columns never stored.
     constexpr int kLoads = 4 * R + kSlice / (2 * kW);
     auto loads_of = [&](HalfStep<R>& dst, uint32_t buf, int sn, auto hc) {
-      constexpr uint32_t H = decltype(hc)::value;
-      // The first half-step reads the first 8 bytes of every 16-byte piece and
-      // the second the rest, half a step later.  Non-temporal loads in the
-      // first half let the lines go before the second half reads them (twice
-      // the algorithmic bytes fetched, measured): only the second half of a
-      // piece is read with the streaming policy.
-      constexpr int kPol = H == 0 ? kKeepPolicy : Q3_STREAM_POLICY;
       const bool live = sn < s_end;
       const uint32_t sc = (uint32_t)(live ? sn : s_end - 1);
-      const uint32_t vc = live ? vcode + 8u * H : kOob, vs = live ? vscale + 2u * H : kOob;
+      const uint32_t vc = live ? vcode + 8u * decltype(hc)::value : kOob;
+      const uint32_t vs = live ? vscale + 2u * decltype(hc)::value : kOob;
+      using Half = decltype(hc);
       return [&, buf, live, sc, vc, vs](auto q) {
+        constexpr uint32_t H = Half::value;
+        // The first half-step reads the first 8 bytes of every 16-byte piece
+        // and the second the rest, half a step later.  Non-temporal loads in
+        // the first half let the lines go before the second half reads them
+        // (twice the algorithmic bytes fetched, measured): only the second
+        // half of a piece is read with the streaming policy.
+        constexpr int kPol = H == 0 ? kKeepPolicy : Q3_STREAM_POLICY;
         constexpr int Q = decltype(q)::value;
         if constexpr (Q < 3 * R) {
           constexpr int r = Q / 3, j = Q % 3;
@@ -1358,6 +1388,13 @@ hipError_t launch_cfg(KArgs a, int tokens_in_slice, unsigned grid_y, hipStream_t
 // (top-k routing) an expert has at most t pairs, so t rows (times the terms per
 // pair) cover it; more pairs (repeated ids) take further slices.  Even and at
 // most 16 (one matrix-core column tile).
+// Grid rows of an expert pass: with at most 64 experts, row y takes the
+// round's y-th distinct picked expert, so no more rows than pairs are needed;
+// past 64 experts, row e is expert e.
+unsigned expert_rows(int num_experts, int pairs) {
+  return (unsigned)(num_experts <= 64 && pairs < num_experts ? pairs : num_experts);
+}
+
 int expert_slice(int t, int pairs, int terms) {
   int c = (t < pairs ? t : pairs) * terms;
   c = c < 16 ? c : 16;
@@ -1566,7 +1603,8 @@ hipError_t launch_grouped(const ExpertView& w, const uint16_t* x, int64_t ldx, i
   a.vec_y = ((uintptr_t)y % 16 == 0) && (ldy % 4 == 0);
   a.x_rows = x_by_slot ? (int64_t)t * topk : t;
   a.slice_cap = expert_slice(t, a.pairs_total, 1);
-  return launch_cfg<1, kExperts, false>(a, a.slice_cap, (unsigned)w.num_experts, s);
+  a.num_experts = w.num_experts;
+  return launch_cfg<1, kExperts, false>(a, a.slice_cap, expert_rows(w.num_experts, a.pairs_total), s);
 }
 
 hipError_t launch_moe_mlp(const ExpertView& gu, const ExpertView& dn, const uint16_t* x, int64_t ldx,
@@ -1589,7 +1627,7 @@ hipError_t launch_moe_mlp(const ExpertView& gu, const ExpertView& dn, const uint
   a.h = h;
   a.ldh = inter;
   a.slice_cap = expert_slice(t, pairs, 1);
-  hipError_t e = launch_cfg<1, kSwiGLU, false>(a, a.slice_cap, (unsigned)gu.num_experts, s);
+  hipError_t e = launch_cfg<1, kSwiGLU, false>(a, a.slice_cap, expert_rows(gu.num_experts, pairs), s);
   if (e != hipSuccess) return e;
   KArgs b = base_args(dn.base);
   b.code_stride = dn.code_stride;
@@ -1605,7 +1643,7 @@ hipError_t launch_moe_mlp(const ExpertView& gu, const ExpertView& dn, const uint
   b.part = part;
   b.ldp = ldp;
   b.slice_cap = expert_slice(t, pairs, 2);
-  e = launch_cfg<1, kDownTerms, false>(b, b.slice_cap, (unsigned)dn.num_experts, s);
+  e = launch_cfg<1, kDownTerms, false>(b, b.slice_cap, expert_rows(dn.num_experts, pairs), s);
   if (e != hipSuccess) return e;
   return launch_moe_combine(part, ldp, ids, t, topk, dn.num_experts, logits, ld_logits, dn.base.n, out, ldo, s);
 }
