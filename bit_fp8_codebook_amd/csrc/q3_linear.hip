@@ -393,8 +393,10 @@ void linear_kernel(KArgs a) {
   constexpr int kThreads = 64 * kW;
   constexpr int kSlice = kDot ? NT : 16 * NT;   // tokens per slice
   extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ int pairs[64];
-  __shared__ int npairs;
+  // Expert passes: each wave keeps its own copy of the block's (token, slot)
+  // pairs, written and read by that wave alone, so no block barrier stands
+  // between the ids and the first loads.
+  __shared__ int pairs_w[kGrouped ? kW : 1][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -407,10 +409,10 @@ void linear_kernel(KArgs a) {
   const int ks = wave - rg * sk;
 
   // ---- which expert / tokens -------------------------------------------------
-  int expert = 0;
+  int expert = 0, npairs = 0;
   if (kGrouped) {
-    // Every wave reads the round's ids and finds its block's expert itself,
-    // so the planes' addresses do not wait for the block barrier.
+    // Every wave reads the round's ids and finds its block's expert and pairs
+    // itself, so the planes' addresses and the first loads need no barrier.
     const int id = lane < a.pairs_total ? a.ids[lane] : -1;
     int e = blockIdx.y;
     if (a.num_experts <= 64) {
@@ -425,18 +427,18 @@ void linear_kernel(KArgs a) {
       e = pick != 0 ? __builtin_ctzll(pick) : -1;
     }
     expert = __builtin_amdgcn_readfirstlane(e);
-    if (wave == 0) {
-      const bool match = expert >= 0 && id == expert;
-      const unsigned long long mask = __ballot(match);
-      if (match) pairs[__popcll(mask & ((1ull << lane) - 1ull))] = lane;
-      if (lane == 0) npairs = __popcll(mask);
-    }
-    __syncthreads();
+    const bool match = expert >= 0 && id == expert;
+    const unsigned long long mask = __ballot(match);
+    if (match) pairs_w[kGrouped ? wave : 0][__popcll(mask & ((1ull << lane) - 1ull))] = lane;
+    npairs = __popcll(mask);
+    // Order this wave's writes of its pairs before its reads of them.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (npairs == 0) return;   // not picked this round: no weight byte is read
   }
-  const int total_tokens =
-      kGrouped == kDownTerms ? 2 * __builtin_amdgcn_readfirstlane(npairs)
-                             : (kGrouped ? __builtin_amdgcn_readfirstlane(npairs) : a.m);
+  const int* const pairs = pairs_w[kGrouped ? wave : 0];
+  const int total_tokens = kGrouped == kDownTerms ? 2 * npairs : (kGrouped ? npairs : a.m);
 
   const int G = a.G;
   const uint32_t gp = (uint32_t)((G + 3) & ~3);
