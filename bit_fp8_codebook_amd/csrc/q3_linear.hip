@@ -422,7 +422,7 @@ void linear_kernel(KArgs a) {
       const bool valid = id >= 0 && id < a.num_experts;
       const uint64_t bit = valid ? 1ull << id : 0ull;
       const uint64_t used = (uint64_t)wave_or32((uint32_t)bit) | (uint64_t)wave_or32((uint32_t)(bit >> 32)) << 32;
-      const bool sel = ((used >> lane) & 1ull) != 0 && __popcll(used & ((1ull << lane) - 1ull)) == (int)blockIdx.y;
+      const bool sel = ((used >> lane) & 1ull) != 0 && (int)__popcll(used & ((1ull << lane) - 1ull)) == (int)blockIdx.y;
       const uint64_t pick = __ballot(sel);
       e = pick != 0 ? __builtin_ctzll(pick) : -1;
     }
