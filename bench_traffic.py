@@ -45,10 +45,10 @@ def per_kernel(path, counter):
     return vals
 
 
-KEYS = ("splitk_kernel<", "linear_kernel<", "wide_kernel<", "split_reduce_kernel<", "fit_kernel", "pack_kernel",
-        "unpack_kernel",
-        "budget_topk_kernel", "topk_kernel", "combine_kernel", "quantize_kernel", "shortlist_chunks",
-        "rescore_kernel", "read_kernel<", "copyBuffer")
+KEYS = ("splitk_full_kernel<", "splitk_kernel<", "linear_kernel<", "wide_hs_kernel<", "wide_kernel<",
+        "split_reduce_kernel<", "fit_kernel", "pack_kernel", "unpack_kernel",
+        "budget_topk_wave_kernel<", "topk_wave_kernel", "budget_topk_kernel", "topk_kernel", "combine_kernel",
+        "quantize_kernel", "shortlist_chunks", "rescore_kernel", "read_kernel<", "copyBuffer")
 
 
 def short(name: str) -> str:
