@@ -81,6 +81,47 @@ def test_grouped_one_token_many_experts(q3):
     run_round(q3, moe, 12)
 
 
+def test_grouped_more_than_64_experts(q3):
+    # Past 64 experts grid row e is expert e (rows of unpicked experts exit
+    # after reading the ids); up to 64, row y takes the round's y-th picked id.
+    moe = synth.make_moe(num_experts=80, k_gu=256, n_gu=64, k_dn=32, n_dn=72, tokens=8, topk=4, seed=31)
+    run_round(q3, moe, 4)
+    ids = q3.q3_moe_topk(dev(moe.logits), 4).cpu().numpy()
+    out, ref, bound = _run_mlp(q3, moe, ids)
+    assert_close(out, ref, bound, "fused MLP, 80 experts")
+
+
+def test_grouped_every_pair_a_different_expert(q3):
+    # 64 pairs on 64 distinct experts: every grid row has work, one pair each,
+    # and the rows map to the experts in increasing id order.
+    moe = synth.make_moe(num_experts=64, k_gu=256, n_gu=64, k_dn=32, n_dn=72, tokens=8, topk=8, seed=32)
+    ids = np.random.default_rng(32).permutation(64).astype(np.int32).reshape(8, 8)
+    st_gu = stack_experts(q3, moe.experts_gu)
+    st_dn = stack_experts(q3, moe.experts_dn)
+    y_gu = q3.q3_grouped_expert_gemv(st_gu, dev(moe.x), dev(ids), False).cpu().numpy()
+    x_dn = np.ascontiguousarray(moe.x_dn[:, :8]).reshape(64, -1)
+    y_dn = q3.q3_grouped_expert_gemv(st_dn, dev(x_dn), dev(ids), True).cpu().numpy()
+    ref_gu, b_gu = oracle.grouped_linear(planes(moe.experts_gu), ids, moe.x, False)
+    ref_dn, b_dn = oracle.grouped_linear(planes(moe.experts_dn), ids, moe.x_dn[:, :8], True)
+    assert_close(y_gu, ref_gu.reshape(64, -1), b_gu.reshape(64, -1), "gate/up, 64 distinct experts")
+    assert_close(y_dn, ref_dn.reshape(64, -1), b_dn.reshape(64, -1), "down, 64 distinct experts")
+    out, ref, bound = _run_mlp(q3, moe, ids)
+    assert_close(out, ref, bound, "fused MLP, 64 distinct experts")
+
+
+def test_grouped_only_the_highest_experts(q3):
+    # Every pair on the last few experts of the stack: the round's picked ids
+    # are the top of the range, served by the first grid rows.
+    moe = synth.make_moe(num_experts=64, k_gu=256, n_gu=64, k_dn=32, n_dn=72, tokens=4, topk=2, seed=33)
+    ids = np.array([[63, 61], [62, 63], [61, 60], [63, 60]], dtype=np.int32)
+    st_gu = stack_experts(q3, moe.experts_gu)
+    y_gu = q3.q3_grouped_expert_gemv(st_gu, dev(moe.x), dev(ids), False).cpu().numpy()
+    ref_gu, b_gu = oracle.grouped_linear(planes(moe.experts_gu), ids, moe.x, False)
+    assert_close(y_gu, ref_gu.reshape(8, -1), b_gu.reshape(8, -1), "gate/up, highest experts")
+    out, ref, bound = _run_mlp(q3, moe, ids)
+    assert_close(out, ref, bound, "fused MLP, highest experts")
+
+
 def test_grouped_repeated_ids_take_several_slices(q3):
     # An id repeated inside a token's list gives an expert more (token, slot)
     # pairs than there are tokens, beyond the rows its block stages at once:
