@@ -188,9 +188,9 @@ __global__ __launch_bounds__(1024) void budget_topk_kernel(const float* __restri
 // wave's registers, all loaded at once (no block barrier).  Measured with clock
 // stamps at one wave per SIMD, what costs is the length of dependent
 // instruction chains, so:
-//   * each token's maximum and exp-sum over the experts are the DPP
-//     reductions above; the reductions of different tokens are independent
-//     and interleave;
+//   * each token's maximum and exp-sum over the experts are reduced by a
+//     group of 64/T lanes (T experts per lane, then DPP steps inside the
+//     group) on the logits transposed through LDS, all tokens at once;
 //   * ranks are counted on 64-bit keys (the value's order-preserving bits
 //     above 63 - index, -0 taken as +0), so "ranks before" is one unsigned
 //     comparison; every lane compares its key with all 64 from LDS, into four
@@ -221,11 +221,38 @@ __device__ __forceinline__ int count_above(const uint64_t* keys, uint64_t mine) 
   return ((c[0] + c[1]) + (c[2] + c[3])) + ((c[4] + c[5]) + (c[6] + c[7]));
 }
 
+// Maximum and sum over an aligned group of G = 4, 8 or 16 lanes (the same
+// DPP steps as the wave reductions, stopped at the group's width), the result
+// in every lane of the group.
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  if constexpr (G >= 8) v = fmaxf(v, dpp_f<0x141>(v));
+  if constexpr (G >= 16) v = fmaxf(v, dpp_f<0x140>(v));
+  return v;
+}
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  if constexpr (G >= 8) v += dpp_f<0x141>(v);
+  if constexpr (G >= 16) v += dpp_f<0x140>(v);
+  return v;
+}
+
 template <int kT>
 __global__ __launch_bounds__(64) void budget_topk_wave_kernel(const float* __restrict__ logits, int T, int E, int topk,
                                                               int budget, int32_t* __restrict__ ids,
                                                               int32_t* __restrict__ experts) {
+  // The softmax statistics are taken transposed: the round's logits go to LDS
+  // token by token, and each group of G = 64/kT lanes reduces one token over
+  // its kT experts per lane (instead of a whole-wave reduction per token); the
+  // normalised probabilities come back expert by expert.
+  constexpr int G = 64 / kT, C = kT;
   __shared__ __align__(16) uint64_t keys[64];
+  __shared__ __align__(16) float lg[kT * 64];   // lg[u][e], absent experts -inf
+  __shared__ __align__(16) float pr[64 * kT];   // pr[e][u] = exp(l - max) / sum, 0 for u >= T
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
   const bool live = lane < E;
@@ -234,17 +261,50 @@ __global__ __launch_bounds__(64) void budget_topk_wave_kernel(const float* __res
 #pragma unroll
   for (int u = 0; u < kT; ++u) l[u] = logits[(int64_t)(u < T ? u : T - 1) * E + le];   // rows past T repeat the last
   const float tk = logits[(int64_t)t * E + le];
-  float mx[kT], ex[kT], sm[kT];
 #pragma unroll
-  for (int u = 0; u < kT; ++u) mx[u] = wave_max(live ? l[u] : -__builtin_inff());
+  for (int u = 0; u < kT; ++u) lg[u * 64 + lane] = live ? l[u] : -__builtin_inff();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  {
+    const int u = lane / G, p = lane % G;   // token u, experts p*C .. p*C + C - 1
+    float v[C];
 #pragma unroll
-  for (int u = 0; u < kT; ++u) sm[u] = ex[u] = live ? expf(l[u] - mx[u]) : 0.f;
+    for (int q = 0; q < C / 4; ++q) {
+      const float4 f = *reinterpret_cast<const float4*>(lg + u * 64 + p * C + 4 * q);
+      v[4 * q] = f.x;
+      v[4 * q + 1] = f.y;
+      v[4 * q + 2] = f.z;
+      v[4 * q + 3] = f.w;
+    }
+    float mx = v[0];
 #pragma unroll
-  for (int u = 0; u < kT; ++u) sm[u] = wave_sum(sm[u]);
+    for (int j = 1; j < C; ++j) mx = fmaxf(mx, v[j]);
+    mx = group_max<G>(mx);
+    float ex[C], sm = 0.f;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      ex[j] = p * C + j < E ? expf(v[j] - mx) : 0.f;
+      sm += ex[j];
+    }
+    sm = group_sum<G>(sm);
+    const float r = __builtin_amdgcn_rcpf(sm);   // v_rcp_f32 (1 ulp) in place of a division
+#pragma unroll
+    for (int j = 0; j < C; ++j) pr[(p * C + j) * kT + u] = u < T ? ex[j] * r : 0.f;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // The expert's mass: its probabilities summed in token order.
   float m = 0.f;
 #pragma unroll
-  for (int u = 0; u < kT; ++u)
-    if (u < T) m += ex[u] * __builtin_amdgcn_rcpf(sm[u]);   // v_rcp_f32 (1 ulp) in place of a division
+  for (int q = 0; q < kT / 4; ++q) {
+    const float4 f = *reinterpret_cast<const float4*>(pr + lane * kT + 4 * q);
+    m += f.x;
+    m += f.y;
+    m += f.z;
+    m += f.w;
+  }
   // Kept set: the budget experts whose mass ranks first (absent lanes key 0, ranked last).
   const uint64_t mkey = live ? rank_key(m, lane) : 0ull;
   keys[lane] = mkey;
