@@ -183,42 +183,28 @@ __global__ __launch_bounds__(1024) void budget_topk_kernel(const float* __restri
   }
 }
 
-// The same routing for rounds of at most 16 tokens over at most 64 experts: one
-// wave per token, expert e in lane e, and the whole round's logits in that
-// wave's registers, all loaded at once (no block barrier).  Measured with clock
-// stamps at one wave per SIMD, what costs is the length of dependent
-// instruction chains, so:
+// The same routing for rounds of at most 16 tokens over at most 64 experts:
+// one block per token, expert e in lane e of each of its waves, and the whole
+// round's logits in the first wave's registers, all loaded at once.  Measured
+// with clock stamps, what costs is the length of dependent instruction chains
+// (a lone wave issues at a fraction of its SIMD's rate), so:
 //   * each token's maximum and exp-sum over the experts are reduced by a
 //     group of 64/T lanes (T experts per lane, then DPP steps inside the
 //     group) on the logits transposed through LDS, all tokens at once;
 //   * ranks are counted on 64-bit keys (the value's order-preserving bits
 //     above 63 - index, -0 taken as +0), so "ranks before" is one unsigned
-//     comparison; every lane compares its key with all 64 from LDS, into four
-//     independent counters.
+//     comparison; the 64 comparisons of each expert are split over four
+//     waves (one per SIMD) and their counts added in wave order.
 // The mass is the sum over tokens, in token order, of exp(l - max) times the
 // hardware reciprocal of the exp-sum.  Every block runs the same code on the
-// same logits, so all of them find the same kept set.  (In-kernel time for 8
-// tokens and 64 experts, clock stamps: 5.5 us with readlane loops and lane
-// butterflies, 2.9 us with the keys and DPP, 2.2 us with the reciprocal and
-// the keys read before counting.)
+// same logits, so all of them find the same kept set.  (Per dependent launch
+// of the budget router for 8 tokens and 64 experts: 6.8 us with readlane loops
+// and lane butterflies in one wave, 3.3 us with the keys and DPP reductions,
+// 2.8 us with the transposed statistics.)
 __device__ __forceinline__ uint64_t rank_key(float v, int idx) {
   uint32_t b = __builtin_bit_cast(uint32_t, v + 0.0f);
   b ^= (b >> 31) ? 0xFFFFFFFFu : 0x80000000u;
   return ((uint64_t)b << 6) | (uint64_t)(63 - idx);
-}
-// Number of the 64 keys in LDS larger than `mine`: all of them read first
-// (16-byte reads), then counted into eight independent counters.
-__device__ __forceinline__ int count_above(const uint64_t* keys, uint64_t mine) {
-  ulonglong2 k[32];
-#pragma unroll
-  for (int q = 0; q < 32; ++q) k[q] = reinterpret_cast<const ulonglong2*>(keys)[q];
-  int c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-  for (int q = 0; q < 32; ++q) {
-    c[(2 * q) & 7] += k[q].x > mine ? 1 : 0;
-    c[(2 * q + 1) & 7] += k[q].y > mine ? 1 : 0;
-  }
-  return ((c[0] + c[1]) + (c[2] + c[3])) + ((c[4] + c[5]) + (c[6] + c[7]));
 }
 
 // Maximum and sum over an aligned group of G = 4, 8 or 16 lanes (the same
@@ -241,83 +227,117 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Ranking split over kRankWaves waves of a block: wave w counts, for every
+// expert (lane), the keys kKeysPerWave*w .. +kKeysPerWave-1 above its own, and
+// the partial counts are added in wave order.  A lone wave issues its
+// comparisons at a fraction of the SIMD's rate, so four waves on four SIMDs
+// cut the counting chain to a quarter.
+constexpr int kRankWaves = 4, kKeysPerWave = 64 / kRankWaves;
+__device__ __forceinline__ int count_above_part(const uint64_t* keys, int wave, uint64_t mine) {
+  ulonglong2 k[kKeysPerWave / 2];
+#pragma unroll
+  for (int q = 0; q < kKeysPerWave / 2; ++q)
+    k[q] = reinterpret_cast<const ulonglong2*>(keys + kKeysPerWave * wave)[q];
+  int c[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int q = 0; q < kKeysPerWave / 2; ++q) {
+    c[(2 * q) & 3] += k[q].x > mine ? 1 : 0;
+    c[(2 * q + 1) & 3] += k[q].y > mine ? 1 : 0;
+  }
+  return (c[0] + c[1]) + (c[2] + c[3]);
+}
+__device__ __forceinline__ int sum_parts(const int (&part)[kRankWaves][64], int lane) {
+  int r = 0;
+#pragma unroll
+  for (int w = 0; w < kRankWaves; ++w) r += part[w][lane];
+  return r;
+}
+
 template <int kT>
-__global__ __launch_bounds__(64) void budget_topk_wave_kernel(const float* __restrict__ logits, int T, int E, int topk,
-                                                              int budget, int32_t* __restrict__ ids,
-                                                              int32_t* __restrict__ experts) {
-  // The softmax statistics are taken transposed: the round's logits go to LDS
-  // token by token, and each group of G = 64/kT lanes reduces one token over
-  // its kT experts per lane (instead of a whole-wave reduction per token); the
-  // normalised probabilities come back expert by expert.
+__global__ __launch_bounds__(64 * kRankWaves) void budget_topk_wave_kernel(const float* __restrict__ logits, int T,
+                                                                           int E, int topk, int budget,
+                                                                           int32_t* __restrict__ ids,
+                                                                           int32_t* __restrict__ experts) {
+  // The softmax statistics are taken transposed by wave 0: the round's logits
+  // go to LDS token by token, and each group of G = 64/kT lanes reduces one
+  // token over its kT experts per lane (instead of a whole-wave reduction per
+  // token); the normalised probabilities come back expert by expert.  The two
+  // rankings are then counted by all the block's waves (lane = expert in each).
   constexpr int G = 64 / kT, C = kT;
-  __shared__ __align__(16) uint64_t keys[64];
+  __shared__ __align__(16) uint64_t mkeys[64], tkeys[64];
   __shared__ __align__(16) float lg[kT * 64];   // lg[u][e], absent experts -inf
   __shared__ __align__(16) float pr[64 * kT];   // pr[e][u] = exp(l - max) / sum, 0 for u >= T
+  __shared__ int part[kRankWaves][64];
   const int t = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool live = lane < E;
   const int le = live ? lane : E - 1;
-  float l[kT];
-#pragma unroll
-  for (int u = 0; u < kT; ++u) l[u] = logits[(int64_t)(u < T ? u : T - 1) * E + le];   // rows past T repeat the last
   const float tk = logits[(int64_t)t * E + le];
+  if (wave == 0) {
+    float l[kT];
 #pragma unroll
-  for (int u = 0; u < kT; ++u) lg[u * 64 + lane] = live ? l[u] : -__builtin_inff();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  {
-    const int u = lane / G, p = lane % G;   // token u, experts p*C .. p*C + C - 1
-    float v[C];
+    for (int u = 0; u < kT; ++u) l[u] = logits[(int64_t)(u < T ? u : T - 1) * E + le];   // rows past T repeat the last
 #pragma unroll
-    for (int q = 0; q < C / 4; ++q) {
-      const float4 f = *reinterpret_cast<const float4*>(lg + u * 64 + p * C + 4 * q);
-      v[4 * q] = f.x;
-      v[4 * q + 1] = f.y;
-      v[4 * q + 2] = f.z;
-      v[4 * q + 3] = f.w;
+    for (int u = 0; u < kT; ++u) lg[u * 64 + lane] = live ? l[u] : -__builtin_inff();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    {
+      const int u = lane / G, p = lane % G;   // token u, experts p*C .. p*C + C - 1
+      float v[C];
+#pragma unroll
+      for (int q = 0; q < C / 4; ++q) {
+        const float4 f = *reinterpret_cast<const float4*>(lg + u * 64 + p * C + 4 * q);
+        v[4 * q] = f.x;
+        v[4 * q + 1] = f.y;
+        v[4 * q + 2] = f.z;
+        v[4 * q + 3] = f.w;
+      }
+      float mx = v[0];
+#pragma unroll
+      for (int j = 1; j < C; ++j) mx = fmaxf(mx, v[j]);
+      mx = group_max<G>(mx);
+      float ex[C], sm = 0.f;
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        ex[j] = p * C + j < E ? expf(v[j] - mx) : 0.f;
+        sm += ex[j];
+      }
+      sm = group_sum<G>(sm);
+      const float r = __builtin_amdgcn_rcpf(sm);   // v_rcp_f32 (1 ulp) in place of a division
+#pragma unroll
+      for (int j = 0; j < C; ++j) pr[(p * C + j) * kT + u] = u < T ? ex[j] * r : 0.f;
     }
-    float mx = v[0];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // The expert's mass: its probabilities summed in token order.
+    float m = 0.f;
 #pragma unroll
-    for (int j = 1; j < C; ++j) mx = fmaxf(mx, v[j]);
-    mx = group_max<G>(mx);
-    float ex[C], sm = 0.f;
-#pragma unroll
-    for (int j = 0; j < C; ++j) {
-      ex[j] = p * C + j < E ? expf(v[j] - mx) : 0.f;
-      sm += ex[j];
+    for (int q = 0; q < kT / 4; ++q) {
+      const float4 f = *reinterpret_cast<const float4*>(pr + lane * kT + 4 * q);
+      m += f.x;
+      m += f.y;
+      m += f.z;
+      m += f.w;
     }
-    sm = group_sum<G>(sm);
-    const float r = __builtin_amdgcn_rcpf(sm);   // v_rcp_f32 (1 ulp) in place of a division
-#pragma unroll
-    for (int j = 0; j < C; ++j) pr[(p * C + j) * kT + u] = u < T ? ex[j] * r : 0.f;
+    mkeys[lane] = live ? rank_key(m, lane) : 0ull;   // absent lanes key 0, ranked last
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // The expert's mass: its probabilities summed in token order.
-  float m = 0.f;
-#pragma unroll
-  for (int q = 0; q < kT / 4; ++q) {
-    const float4 f = *reinterpret_cast<const float4*>(pr + lane * kT + 4 * q);
-    m += f.x;
-    m += f.y;
-    m += f.z;
-    m += f.w;
-  }
-  // Kept set: the budget experts whose mass ranks first (absent lanes key 0, ranked last).
-  const uint64_t mkey = live ? rank_key(m, lane) : 0ull;
-  keys[lane] = mkey;
-  __builtin_amdgcn_wave_barrier();
-  const bool in = live && count_above(keys, mkey) < budget;
+  __syncthreads();
+  // Kept set: the budget experts whose mass ranks first.
+  const uint64_t mkey = mkeys[lane];
+  part[wave][lane] = count_above_part(mkeys, wave, mkey);
+  __syncthreads();
+  const bool in = live && sum_parts(part, lane) < budget;
   const uint64_t keep = __ballot(in);
-  __builtin_amdgcn_wave_barrier();
   // The token's ranking inside the kept set (experts outside it key 0, below every kept key).
   const uint64_t tkey = in ? rank_key(tk, lane) + 1ull : 0ull;
-  keys[lane] = tkey;
-  __builtin_amdgcn_wave_barrier();
-  const int r = count_above(keys, tkey);
-  if (in) {
+  if (wave == 0) tkeys[lane] = tkey;
+  __syncthreads();
+  part[wave][lane] = count_above_part(tkeys, wave, tkey);
+  __syncthreads();
+  if (wave == 0 && in) {
+    const int r = sum_parts(part, lane);
     if (r < topk) ids[(int64_t)t * topk + r] = lane;
     if (t == 0 && experts) experts[__popcll(keep & ((1ull << lane) - 1ull))] = lane;
   }
@@ -326,18 +346,23 @@ __global__ __launch_bounds__(64) void budget_topk_wave_kernel(const float* __res
 // Plain top-k for at most 64 experts: one wave per token, expert e in lane e,
 // ranks counted on the same 64-bit keys as above (absent lanes key 0, below
 // every expert's key + 1).
-__global__ __launch_bounds__(64) void topk_wave_kernel(const float* __restrict__ logits, int E, int topk,
-                                                       int32_t* __restrict__ ids) {
+__global__ __launch_bounds__(64 * kRankWaves) void topk_wave_kernel(const float* __restrict__ logits, int E, int topk,
+                                                                    int32_t* __restrict__ ids) {
   __shared__ __align__(16) uint64_t keys[64];
+  __shared__ int part[kRankWaves][64];
   const int t = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool live = lane < E;
   const float v = logits[(int64_t)t * E + (live ? lane : E - 1)];
   const uint64_t k = live ? rank_key(v, lane) + 1ull : 0ull;
-  keys[lane] = k;
-  __builtin_amdgcn_wave_barrier();
-  const int r = count_above(keys, k);
-  if (live && r < topk) ids[(int64_t)t * topk + r] = lane;
+  if (wave == 0) keys[lane] = k;
+  __syncthreads();
+  part[wave][lane] = count_above_part(keys, wave, k);
+  __syncthreads();
+  if (wave == 0) {
+    const int r = sum_parts(part, lane);
+    if (live && r < topk) ids[(int64_t)t * topk + r] = lane;
+  }
 }
 
 }  // namespace
@@ -346,11 +371,11 @@ hipError_t launch_moe_budget_topk(const float* logits, int32_t t, int32_t e, int
                                   int32_t* ids, int32_t* experts, hipStream_t s) {
 #ifndef Q3_NO_WAVE_ROUTER
   if (e <= 64 && t <= 16) {
-    if (t <= 4) hipLaunchKernelGGL(budget_topk_wave_kernel<4>, dim3((unsigned)t), dim3(64), 0, s, logits, (int)t,
+    if (t <= 4) hipLaunchKernelGGL(budget_topk_wave_kernel<4>, dim3((unsigned)t), dim3(64 * kRankWaves), 0, s, logits, (int)t,
                                    (int)e, (int)topk, (int)budget, ids, experts);
-    else if (t <= 8) hipLaunchKernelGGL(budget_topk_wave_kernel<8>, dim3((unsigned)t), dim3(64), 0, s, logits,
+    else if (t <= 8) hipLaunchKernelGGL(budget_topk_wave_kernel<8>, dim3((unsigned)t), dim3(64 * kRankWaves), 0, s, logits,
                                         (int)t, (int)e, (int)topk, (int)budget, ids, experts);
-    else hipLaunchKernelGGL(budget_topk_wave_kernel<16>, dim3((unsigned)t), dim3(64), 0, s, logits, (int)t, (int)e,
+    else hipLaunchKernelGGL(budget_topk_wave_kernel<16>, dim3((unsigned)t), dim3(64 * kRankWaves), 0, s, logits, (int)t, (int)e,
                             (int)topk, (int)budget, ids, experts);
     return hipGetLastError();
   }
@@ -368,7 +393,8 @@ hipError_t launch_moe_budget_topk(const float* logits, int32_t t, int32_t e, int
 hipError_t launch_moe_topk(const float* logits, int32_t t, int32_t e, int32_t topk, int32_t* ids, hipStream_t s) {
 #ifndef Q3_NO_WAVE_ROUTER
   if (e <= 64) {
-    hipLaunchKernelGGL(topk_wave_kernel, dim3((unsigned)t), dim3(64), 0, s, logits, (int)e, (int)topk, ids);
+    hipLaunchKernelGGL(topk_wave_kernel, dim3((unsigned)t), dim3(64 * kRankWaves), 0, s, logits, (int)e, (int)topk,
+                       ids);
     return hipGetLastError();
   }
 #endif
