@@ -407,6 +407,8 @@ namespace {
 
 // One block per (token, 256 output rows): the token's routing weights go to
 // LDS, then each thread sums its row over the token's slots in slot order.
+// The first eight slots' rows do not depend on the weights: their loads go out
+// before the ids and logits are read, so the two latencies overlap.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, int64_t ldp,
                                                       const int32_t* __restrict__ ids, int topk, int E,
                                                       const float* __restrict__ logits, int64_t ld_logits,
@@ -414,6 +416,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   __shared__ float pw[64];
   const int tk = blockIdx.y;
   const int tid = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * 256 + tid;
+  const bool row_ok = row < n;
+  float v0[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v0[j] = row_ok && j < topk ? part[(int64_t)(tk * topk + j) * ldp + row] : 0.f;
   if (tid < 64) {
     const int lane = tid;
     const int e = lane < topk ? ids[tk * topk + lane] : -1;
@@ -425,13 +432,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     pw[lane] = in ? z / den : 0.f;
   }
   __syncthreads();
-  const int64_t row = (int64_t)blockIdx.x * 256 + tid;
-  if (row >= n) return;
+  if (!row_ok) return;
   // The slots' rows are loaded eight at a time before any of them is added
   // (rows of slots without a routed expert lie in the same buffer and are
   // read but never added), then summed in slot order.
   float sum = 0.f;
-  for (int q0 = 0; q0 < topk; q0 += 8) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < topk && pw[j] != 0.f) sum += pw[j] * v0[j];
+  for (int q0 = 8; q0 < topk; q0 += 8) {
     float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
