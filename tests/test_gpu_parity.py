@@ -228,6 +228,24 @@ def test_halfstep_wide_all_rows(q3, n, k, m):
     assert_close(y, y_ref, bound, f"half-step wide n={n} k={k} m={m}")
 
 
+def test_halfstep_wide_strided_x_and_y(q3):
+    # The half-step kernel with activation rows 64 elements apart beyond K and
+    # output rows whose stride keeps them from 16-byte alignment (one store per
+    # output), the pad around both left untouched.
+    n, k, m = 128005, 2048, 40
+    layer, x = synth.make_linear(n, k, m, seed=77)
+    w = pack_layer(q3, layer)
+    xbig = torch.zeros((m, k + 64), dtype=torch.int16, device="cuda")
+    xbig[:, :k] = dev(x)
+    ybig = torch.full((m, n + 3), 7.0, dtype=torch.float32, device="cuda")
+    q3.q3_gemm_small_m(w, xbig[:, :k], ybig[:, :n])
+    del w
+    yb = ybig.cpu().numpy()
+    assert np.all(yb[:, n:] == 7.0)
+    y_ref, bound = oracle_linear(layer, x)
+    assert_close(yb[:, :n], y_ref, bound, "half-step wide, strided x and y")
+
+
 @pytest.mark.parametrize("m", [1, 4, 8])
 def test_config1_full_gemv_and_mfma(q3, m):
     layer, x = synth.make_linear(4096, 4096, m, seed=0)
