@@ -928,11 +928,11 @@ void wide_kernel(KArgs a) {
   }
 }
 
-// Wide products at two waves per SIMD, in half-steps.  A launch of the wide
-// kernel above is bound by its weight stream, not by its arithmetic (measured
-// on a 64-token vocabulary projection: the same launch with no dequantisation
-// and no MFMA takes as long), because its one block per CU drains all of its
-// loads at every step's barrier.  Here a block's activations are staged half
+// Wide products at two waves per SIMD, in half-steps.  With one block per CU
+// a wide launch is bound by its weight stream more than by its arithmetic
+// (measured on a 64-token vocabulary projection with one 8-wave block per CU:
+// its loads alone, with no dequantisation and no MFMA, took 95 of its 98 us),
+// because the block drains all of its loads at every step's barrier.  Here a block's activations are staged half
 // a step at a time (the first two groups of every quad, then the last two), so
 // the double buffer takes 64 KB and two blocks share a CU: the two blocks'
 // barriers fall at unrelated times, and while one waits for its loads the
