@@ -213,7 +213,10 @@ def test_budget_toy_figure(q3):
 
 @pytest.mark.parametrize("t,E,topk,budget", [(8, 64, 8, 16), (8, 64, 8, 8), (8, 64, 8, 24), (8, 64, 2, 63),
                                              (1, 10, 3, 5), (64, 128, 1, 4), (5, 1024, 16, 100),
-                                             (300, 256, 8, 32), (1024, 8, 2, 3), (2, 1000, 7, 999)])
+                                             (300, 256, 8, 32), (1024, 8, 2, 3), (2, 1000, 7, 999),
+                                             # the one-block-per-token router at 4, 8 and 16 token rows,
+                                             # with fewer tokens than rows and absent expert lanes
+                                             (3, 40, 4, 12), (5, 64, 8, 20), (12, 64, 4, 16), (16, 48, 2, 10)])
 def test_budget_matches_oracle(q3, t, E, topk, budget):
     clear = 0
     for seed in range(3):
