@@ -946,7 +946,7 @@ void wide_kernel(KArgs a) {
 template <int R>
 struct HalfStep {
   u32x2 w[R][3];     // w[r][j][tt] = word j of the lane's group 2h+tt of row tile r
-  uint32_t sc[R];    // bytes 0, 1: the scales of those two groups
+  uint32_t sc[R];    // bytes 0, 1: the scales of those two groups (bytes 2, 3 of a first half-step: the second's)
 };
 
 // Selectors, codebook lookup and exact bf16 widening of weights 8e..8e+7 of
@@ -1088,11 +1088,12 @@ void wide_hs_kernel(KArgs a) {
     // A half-step past the last reads out of range (zeros, no traffic); rows
     // of absent tokens hold zeros and only reach output columns never stored.
     constexpr int kLoads = 4 * R + kSlice / (2 * kW);
+    HalfStep<R> A, B;   // A: first half-steps, B: second half-steps
     auto loads_of = [&](HalfStep<R>& dst, uint32_t buf, int sn, auto hc) {
       const bool live = sn < s_end;
       const uint32_t sc = (uint32_t)(live ? sn : s_end - 1);
       const uint32_t vc = live ? vcode + 8u * decltype(hc)::value : kOob;
-      const uint32_t vs = live ? vscale + 2u * decltype(hc)::value : kOob;
+      const uint32_t vs = live ? vscale : kOob;
       using Half = decltype(hc);
       return [&, buf, live, sc, vc, vs](auto q) {
         constexpr uint32_t H = Half::value;
@@ -1108,7 +1109,13 @@ void wide_hs_kernel(KArgs a) {
           dst.w[r][j] = __builtin_amdgcn_raw_buffer_load_b64(code, vc + 1024u * j, tcode[r] + 3072u * sc, kPol);
         } else if constexpr (Q < 4 * R) {
           constexpr int r = Q - 3 * R;
-          dst.sc[r] = __builtin_amdgcn_raw_buffer_load_b16(scale, vs, tscale[r] + 256u * sc, kPol);
+          // The four scale bytes of the lane's quad come in with the first
+          // half-step; the second takes bytes 2 and 3 of the same word.
+          if constexpr (H == 0) dst.sc[r] = __builtin_amdgcn_raw_buffer_load_b32(scale, vs, tscale[r] + 256u * sc, kPol);
+          else {
+            (void)vs;
+            dst.sc[r] = A.sc[r] >> 16;
+          }
         } else {
           constexpr int jq = Q - 4 * R;
           const int qi = wave + kW * jq;                 // this load moves tokens 2qi, 2qi+1
@@ -1120,7 +1127,6 @@ void wide_hs_kernel(KArgs a) {
         }
       };
     };
-    HalfStep<R> A, B;
     {
       auto first = loads_of(A, 0u, s_begin, std::integral_constant<uint32_t, 0>{});
       issue_range<0, kLoads>(first);
